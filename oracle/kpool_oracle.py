@@ -1,0 +1,335 @@
+"""Plain, slow CPU oracle of the KPool DSA indexer -- test infrastructure only.
+
+Only tests/, `__graft_entry__.smoke()` and the CPU-baseline leg of bench.py may
+use this module. It shares no code with the HIP library: no kernels, headers,
+helpers, tables or constants. Everything is NumPy in FP32 (the pages fix FP32
+accumulation for the pooling), evaluated in the order the pages describe, with
+no blocking or fusion. BF16 and E4M3 rounding are written out from their
+definitions.
+
+Sources (three web pages; cited by title and section):
+  [MLM]  Megatron-LM PR #7054, "GLM5.3 Flash (KDA + mHC + KPool DSA) support +
+         FP8", section "3. KPool DSA indexer + NoPE" and section "Testing".
+  [SKY]  SkyRL PR #2179, "GLM-5.3-Flash (glm5_next) support", the commit that
+         points megatron-core at the k-pool indexer, and "Limitations /
+         follow-ups".
+  [XT]   xtuner PR #2108, "Add GLM-5.3-Flash F5: NoPE DSA + KPool indexer +
+         clamped SwiGLU", "Summary" and the F5 commit message.
+
+Readings of points the pages leave open (each one is also listed in the design
+notes of the repository):
+  * A pool is causal for query t when every one of its tokens is at or before
+    t: doc-local pools p < n_c = floor((i + 1) / kpool), i = t - cu[b]. The
+    "incomplete causal pool" is the partial pool holding tokens
+    n_c*kpool .. i (0 to kpool-1 tokens).
+  * An incomplete pool at the end of a document is not compressed.
+  * The position bias is indexed by the slot within the pool: ape[s, d].
+  * Softmax is max-subtracted and normalised by division, in FP32.
+  * The score scale D^-1/2 sits inside the ReLU.
+  * Top-k ties go to the lower pool index; NaN scores rank as -inf.
+  * Selected count is min(index_topk // kpool, n_c).
+  * Output rows: the chosen pools' tokens in ascending pool order, then the
+    tail tokens, then -1 up to width index_topk + kpool. Token and pool ids
+    are global in the packed (THD) layout.
+  * FP8 input path: 128-point Sylvester Hadamard (stages h = 1, 2, ..., 64,
+    butterfly (a, b) -> (a + b, a - b)) in FP32, times FP32(128^-1/2), rounded
+    to BF16; row exponent e = min{e : amax <= 448 * 2^e} (0 for an all-zero
+    row); codes = OCP E4M3 (e4m3fn, max 448, subnormals kept) of y * 2^-e,
+    round to nearest even. The keys are quantised after pooling.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+F32 = np.float32
+
+
+# ---------------------------------------------------------------------------
+# Number formats
+# ---------------------------------------------------------------------------
+
+def bf16_round(x) -> np.ndarray:
+    """Round FP32 values to BF16 (round to nearest, ties to even); the result
+    is returned as FP32 holding the BF16 value. BF16 keeps the top 16 bits of
+    the FP32 encoding, so rounding adds half an ulp of the dropped 16 bits,
+    plus one when the kept part is odd, and truncates."""
+    x = np.ascontiguousarray(x, dtype=F32)
+    u = x.view(np.uint32).astype(np.uint64)
+    keep_lsb = (u >> np.uint64(16)) & np.uint64(1)
+    r = (u + np.uint64(0x7FFF) + keep_lsb) & np.uint64(0xFFFF0000)
+    out = r.astype(np.uint32).view(F32)
+    return np.where(np.isnan(x), F32(np.nan), out).astype(F32)
+
+
+def e4m3_decode_table() -> np.ndarray:
+    """Values of the 127 non-negative finite OCP E4M3 (e4m3fn) codes 0..126:
+    exponent field e = code >> 3 (bias 7), mantissa m = code & 7; e == 0 is
+    subnormal m * 2^-9, otherwise (1 + m/8) * 2^(e - 7). Code 127 is NaN."""
+    codes = np.arange(127)
+    e = codes >> 3
+    m = codes & 7
+    return np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * 2.0 ** (e - 7.0))
+
+
+_E4M3 = e4m3_decode_table()
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """Encode finite values with |x| <= 448 as E4M3 codes (uint8), rounding to
+    the nearest representable value with ties to the even mantissa.
+
+    The spacing of representable values is 2^(E - 3) inside binade
+    [2^E, 2^(E + 1)) for E >= -6 and 2^-9 below 2^-6 (subnormals). Dividing by
+    that spacing is exact in FP64 and np.rint rounds halves to even, which is
+    the even mantissa because the mantissa field and the quotient share parity.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    if np.any(~np.isfinite(x)) or np.any(np.abs(x) > 448.0):
+        raise ValueError("e4m3_encode expects finite |x| <= 448")
+    a = np.abs(x)
+    _, ex = np.frexp(a)                      # a = f * 2^ex, f in [0.5, 1)
+    E = ex - 1                               # floor(log2(a)) for a > 0
+    spacing = np.where(a >= 2.0 ** -6, np.ldexp(1.0, E - 3), 2.0 ** -9)
+    val = np.rint(a / spacing) * spacing
+    code = np.searchsorted(_E4M3, val)
+    assert np.all(_E4M3[code] == val)
+    sign = np.signbit(x).astype(np.uint8) << 7       # the sign is kept, also on zero
+    return (code.astype(np.uint8) | sign).astype(np.uint8)
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    c = np.asarray(codes, dtype=np.uint8)
+    mag = _E4M3[np.minimum(c & 0x7F, 126)]
+    return np.where(c & 0x80, -mag, mag)
+
+
+def pow2_row_exponent(amax: float) -> int:
+    """Smallest integer e with amax <= 448 * 2^e; 0 when amax == 0."""
+    amax = float(amax)
+    if amax == 0.0:
+        return 0
+    e = int(np.ceil(np.log2(amax / 448.0)))
+    while amax > np.ldexp(448.0, e):
+        e += 1
+    while amax <= np.ldexp(448.0, e - 1):
+        e -= 1
+    return e
+
+
+def fwht128(x) -> np.ndarray:
+    """Unnormalised 128-point Walsh-Hadamard transform of each row, in FP32,
+    Sylvester (natural) order: stages h = 1, 2, 4, ..., 64; in every block of
+    2h entries, entry j < h and entry j + h become (a + b, a - b)."""
+    y = np.array(x, dtype=F32, copy=True)
+    R, n = y.shape
+    assert n == 128
+    h = 1
+    while h < n:
+        blocks = y.reshape(R, n // (2 * h), 2, h)
+        a = blocks[:, :, 0, :]
+        b = blocks[:, :, 1, :]
+        y = np.stack([a + b, a - b], axis=2).reshape(R, n)
+        h *= 2
+    return y
+
+
+def fp8_quantize_rows(x):
+    """FP8 input path of [MLM] section 3 (a Hadamard rotation in FP32, a BF16
+    rounding, then E4M3 codes under a power-of-two scale per row), applied to
+    rows of 128 BF16 values.
+
+    Returns (codes uint8 [R, 128], exponents int [R], dequantised FP32 [R, 128]
+    = decode(code) * 2^e). The row scale is 2^e."""
+    x = np.asarray(x, dtype=F32)
+    R = x.shape[0]
+    y = bf16_round(fwht128(x) * F32(1.0 / np.sqrt(128.0)))
+    amax = np.abs(y).max(axis=1) if R else np.zeros(0, F32)
+    exps = np.array([pow2_row_exponent(a) for a in amax], dtype=np.int64)
+    scaled = y.astype(np.float64) * np.ldexp(1.0, -exps)[:, None]
+    codes = e4m3_encode(scaled)
+    deq = (e4m3_decode(codes) * np.ldexp(1.0, exps)[:, None]).astype(F32)
+    return codes, exps, deq
+
+
+# ---------------------------------------------------------------------------
+# Packed-THD bookkeeping
+# ---------------------------------------------------------------------------
+
+def cu_pools_of(cu_seqlens, kpool: int) -> np.ndarray:
+    """Pool offsets per document: complete pools floor(L_b / kpool), summed.
+    In a packed batch the pooling starts afresh at every document start
+    ([MLM] section 3)."""
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    counts = (cu[1:] - cu[:-1]) // kpool
+    return np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+
+
+def doc_of(t: int, cu_seqlens) -> int:
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    return int(np.searchsorted(cu, t, side="right") - 1)
+
+
+def causal_pools(i: int, kpool: int) -> int:
+    """Number of complete pools whose tokens all lie at or before doc-local
+    position i."""
+    return (i + 1) // kpool
+
+
+def tail_len(i: int, kpool: int, tail_on: bool) -> int:
+    """Tokens of the query's incomplete causal pool (0 .. kpool - 1)."""
+    return (i + 1) % kpool if tail_on else 0
+
+
+# ---------------------------------------------------------------------------
+# Step 1: key compression ([MLM] section 3; [SKY] k-pool commit)
+# ---------------------------------------------------------------------------
+
+def compress(k, gate, ape, cu_seqlens, kpool: int):
+    """Pooled keys: for each document, each complete pool and each dimension
+    d, a per-dimension softmax over the pool's slots of (gate logit + slot
+    bias) weights the slot keys; FP32 arithmetic, BF16 result.
+
+    k, gate: [T, D] (BF16 values held as FP32); ape: [kpool, D] FP32.
+    Returns (pooled FP32 [P, D] holding BF16 values, cu_pools int64 [B + 1])."""
+    k = np.asarray(k, dtype=F32)
+    gate = np.asarray(gate, dtype=F32)
+    ape = np.asarray(ape, dtype=F32)
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    cuP = cu_pools_of(cu, kpool)
+    D = k.shape[1]
+    pooled = np.zeros((int(cuP[-1]), D), dtype=F32)
+    for b in range(len(cu) - 1):
+        n = int(cuP[b + 1] - cuP[b])
+        if n == 0:
+            continue
+        start = int(cu[b])
+        ks = k[start:start + n * kpool].reshape(n, kpool, D)
+        gs = gate[start:start + n * kpool].reshape(n, kpool, D)
+        a = gs + ape[None, :, :]                       # [n, kpool, D]
+        m = a[:, 0, :]
+        for s in range(1, kpool):
+            m = np.maximum(m, a[:, s, :])
+        e = np.exp(a - m[:, None, :]).astype(F32)
+        Z = e[:, 0, :]
+        for s in range(1, kpool):
+            Z = Z + e[:, s, :]
+        pi = e / Z[:, None, :]
+        acc = pi[:, 0, :] * ks[:, 0, :]
+        for s in range(1, kpool):
+            acc = acc + pi[:, s, :] * ks[:, s, :]
+        pooled[int(cuP[b]):int(cuP[b]) + n] = bf16_round(acc)
+    return pooled, cuP
+
+
+# ---------------------------------------------------------------------------
+# Step 2: pool scores ([MLM] section 3: the top-k is taken over pools; [XT] F5
+# commit: the indexer score, with head_dim^-1/2 inside the ReLU)
+# ---------------------------------------------------------------------------
+
+def row_scores(q_t, w_t, keys, scale: float) -> np.ndarray:
+    """score[p] = sum_h w[h] * ReLU(scale * q[h] . key[p]) for the given keys
+    (the query's causal pools). q_t: [H, D]; w_t: [H]; keys: [n, D]."""
+    q_t = np.asarray(q_t, dtype=F32)
+    w_t = np.asarray(w_t, dtype=F32)
+    keys = np.asarray(keys, dtype=F32)
+    n = keys.shape[0]
+    out = np.zeros(n, dtype=F32)
+    if n == 0:
+        return out
+    dots = (q_t @ keys.T).astype(F32)                  # [H, n], FP32
+    sc = F32(scale)
+    for h in range(q_t.shape[0]):
+        out = out + w_t[h] * np.maximum(F32(0.0), sc * dots[h])
+    return out.astype(F32)
+
+
+# ---------------------------------------------------------------------------
+# Step 3: pool top-k ([MLM] section 3: top index_topk // kpool pools)
+# ---------------------------------------------------------------------------
+
+def select_pools(scores, k_sel: int) -> np.ndarray:
+    """Doc-local indices of the min(k_sel, n) highest-scoring pools, in
+    ascending order. Larger score first, equal scores to the lower index; NaN
+    ranks as -inf."""
+    s = np.asarray(scores, dtype=F32)
+    n = s.shape[0]
+    n_sel = min(k_sel, n)
+    s = np.where(np.isnan(s), F32(-np.inf), s)
+    order = np.lexsort((np.arange(n), -s))              # score desc, index asc
+    return np.sort(order[:n_sel]).astype(np.int64)
+
+
+# ---------------------------------------------------------------------------
+# Step 4: expansion + tail ([MLM] section 3; [SKY] "Limitations / follow-ups":
+# score pools, expand the chosen ones to tokens, then add the query's tail)
+# ---------------------------------------------------------------------------
+
+def expand_row(t: int, cu_seqlens, cu_pools, pool_ids_global, kpool: int,
+               index_topk: int, tail_on: bool) -> np.ndarray:
+    """Token row of query t: each chosen pool's kpool consecutive tokens in
+    ascending pool order, then the tail tokens n_c*kpool .. i of the query's
+    document, then -1 up to width index_topk + kpool."""
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    cuP = np.asarray(cu_pools, dtype=np.int64)
+    b = doc_of(t, cu)
+    i = t - int(cu[b])
+    row = []
+    for gid in pool_ids_global:
+        p = int(gid) - int(cuP[b])
+        row.extend(int(cu[b]) + p * kpool + s for s in range(kpool))
+    if tail_on:
+        n_c = causal_pools(i, kpool)
+        row.extend(range(int(cu[b]) + n_c * kpool, t + 1))
+    W = index_topk + kpool
+    assert len(row) <= W
+    return np.array(row + [-1] * (W - len(row)), dtype=np.int32)
+
+
+# ---------------------------------------------------------------------------
+# The whole path
+# ---------------------------------------------------------------------------
+
+def indexer_topk(q, w, pooled, cu_seqlens, kpool: int, index_topk: int,
+                 tail_on: bool, scale: float = 0.0, rows=None, fp8: bool = False,
+                 return_scores: bool = False):
+    """Token indices [R, index_topk + kpool] and global pool ids
+    [R, index_topk // kpool] (-1 padded) for the query rows `rows` (default:
+    all). q: [T, H, D]; w: [T, H] FP32; pooled: [P, D] (BF16 values).
+
+    With fp8, q rows (t, h) and pooled rows are replaced by their dequantised
+    FP8 values before scoring."""
+    q = np.asarray(q, dtype=F32)
+    w = np.asarray(w, dtype=F32)
+    pooled = np.asarray(pooled, dtype=F32)
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    cuP = cu_pools_of(cu, kpool)
+    T, H, D = q.shape
+    if scale == 0.0:
+        scale = float(F32(1.0 / np.sqrt(D)))
+    rows = list(range(T)) if rows is None else [int(r) for r in rows]
+    k_sel = index_topk // kpool
+    W = index_topk + kpool
+    if fp8:
+        _, _, keys_all = fp8_quantize_rows(pooled)
+    else:
+        keys_all = pooled
+    tok = np.full((len(rows), W), -1, dtype=np.int32)
+    pid = np.full((len(rows), k_sel), -1, dtype=np.int32)
+    all_scores = []
+    for r, t in enumerate(rows):
+        b = doc_of(t, cu)
+        i = t - int(cu[b])
+        n_c = causal_pools(i, kpool)
+        keys = keys_all[int(cuP[b]):int(cuP[b]) + n_c]
+        q_t = q[t]
+        if fp8:
+            _, _, q_t = fp8_quantize_rows(q_t)
+        sc = row_scores(q_t, w[t], keys, scale)
+        if return_scores:
+            all_scores.append(sc)
+        chosen = select_pools(sc, k_sel) + int(cuP[b])
+        pid[r, :len(chosen)] = chosen
+        tok[r] = expand_row(t, cu, cuP, chosen, kpool, index_topk, tail_on)
+    if return_scores:
+        return tok, pid, all_scores
+    return tok, pid

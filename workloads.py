@@ -1,0 +1,145 @@
+"""Seeded synthetic inputs for the KPool indexer (shared by the oracle tests, the
+GPU tests and the benchmark).
+
+This module only draws random numbers and casts them to the storage dtypes the
+indexer consumes; it holds none of the method's arithmetic. Both the CPU oracle
+and the HIP library are fed from here, and neither is imported by this file.
+
+Workloads follow the shapes of the GLM-5.3-Flash indexer described on the
+Megatron-LM PR #7054 page ("GLM-5.3-Flash at a glance": index_kpool = 4,
+index_kpool_always_select_tail = true, index_topk = 2048), with synthetic
+values: q, k and the gate logits ~ N(0, 1) stored as BF16, w ~ N(0, 1)/sqrt(H)
+in FP32, the per-slot position bias ~ N(0, 0.1) (standard deviation 0.1) in
+FP32. The long-context workloads scale the keys of 5 % of the tokens by 4 to
+give heavy-tailed scores.
+
+Draw order for one workload, from one CPU torch.Generator seeded with `seed`:
+  1. document lengths (packed workloads only): randint(lo, hi + 1, (B,))
+  2. q = randn(T, H, D)
+  3. k = randn(T, D)
+  4. w = randn(T, H) / sqrt(H)
+  5. gate = randn(T, D)
+  6. ape = 0.1 * randn(kpool, D)
+  7. heavy-tailed workloads only: rows randperm(T)[:round(frac * T)] of k *= 4
+  8. q, k and gate are cast to BF16 (round to nearest even)
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field, replace
+from typing import Optional, Sequence
+
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    T: int = 0                      # total tokens (single-document workloads)
+    H: int = 32                     # indexer heads
+    D: int = 128                    # indexer head dim
+    kpool: int = 4
+    index_topk: int = 2048
+    tail: bool = True               # always_select_tail
+    fp8: bool = False               # FP8 input path
+    query_chunk: int = 0            # 0 = library default
+    doc_lengths: Optional[Sequence[int]] = None   # explicit document lengths
+    num_docs: int = 0               # > 0: draw this many lengths uniformly
+    doc_len_range: tuple = (512, 4096)
+    heavy_frac: float = 0.0         # fraction of key rows scaled by 4
+    seed: int = 0
+
+    @property
+    def k_sel(self) -> int:
+        return self.index_topk // self.kpool
+
+    @property
+    def width(self) -> int:
+        return self.index_topk + self.kpool
+
+
+# The five workloads: tiny single sequence, 4K single sequence, packed batch
+# of 8 documents, 64K long context, 32K FP8 input path.
+WORKLOADS = [
+    Workload("tiny_T256_H4_D64", T=256, H=4, D=64, kpool=4, index_topk=64),
+    Workload("single_T4096_H32_D128", T=4096),
+    Workload("packed8_H32_D128", num_docs=8, doc_len_range=(512, 4096)),
+    Workload("long_T65536_H32_D128", T=65536, query_chunk=4096, heavy_frac=0.05),
+    Workload("fp8_T32768_H32_D128", T=32768, fp8=True, query_chunk=4096,
+             heavy_frac=0.05),
+]
+
+
+def workload(index_or_name) -> Workload:
+    if isinstance(index_or_name, int):
+        return WORKLOADS[index_or_name]
+    for w in WORKLOADS:
+        if w.name == index_or_name:
+            return w
+    raise KeyError(index_or_name)
+
+
+@dataclass
+class Inputs:
+    """CPU tensors of one workload. BF16 tensors are torch.bfloat16."""
+    wl: Workload
+    q: torch.Tensor          # bf16 [T, H, D]
+    k: torch.Tensor          # bf16 [T, D]
+    w: torch.Tensor          # f32  [T, H]
+    gate: torch.Tensor       # bf16 [T, D]
+    ape: torch.Tensor        # f32  [kpool, D]
+    cu_seqlens: torch.Tensor  # int32 [B + 1]
+    doc_lengths: list = field(default_factory=list)
+
+    @property
+    def T(self) -> int:
+        return int(self.q.shape[0])
+
+    @property
+    def max_seqlen(self) -> int:
+        return max(self.doc_lengths) if self.doc_lengths else 0
+
+
+def make_inputs(wl: Workload, seed: Optional[int] = None) -> Inputs:
+    g = torch.Generator().manual_seed(wl.seed if seed is None else seed)
+    if wl.doc_lengths is not None:
+        lengths = [int(x) for x in wl.doc_lengths]
+    elif wl.num_docs > 0:
+        lo, hi = wl.doc_len_range
+        lengths = torch.randint(lo, hi + 1, (wl.num_docs,), generator=g).tolist()
+    else:
+        lengths = [wl.T]
+    T = sum(lengths)
+    H, D, kp = wl.H, wl.D, wl.kpool
+    q = torch.randn(T, H, D, generator=g)
+    k = torch.randn(T, D, generator=g)
+    w = torch.randn(T, H, generator=g) / math.sqrt(H)
+    gate = torch.randn(T, D, generator=g)
+    ape = 0.1 * torch.randn(kp, D, generator=g)
+    if wl.heavy_frac > 0 and T > 0:
+        heavy = torch.randperm(T, generator=g)[: int(round(wl.heavy_frac * T))]
+        k[heavy] *= 4.0
+    cu = torch.zeros(len(lengths) + 1, dtype=torch.int32)
+    if lengths:
+        cu[1:] = torch.cumsum(torch.tensor(lengths, dtype=torch.int64), 0).to(torch.int32)
+    return Inputs(wl=wl, q=q.to(torch.bfloat16), k=k.to(torch.bfloat16),
+                  w=w.to(torch.float32).contiguous(), gate=gate.to(torch.bfloat16),
+                  ape=ape.to(torch.float32).contiguous(), cu_seqlens=cu,
+                  doc_lengths=lengths)
+
+
+def custom(name="custom", **kw) -> Workload:
+    """A workload with explicit fields (tests use this for small cases)."""
+    return replace(Workload(name), **kw)
+
+
+def strided_rows(T: int, n: int) -> list:
+    """n query rows strided uniformly over [0, T), the last row always included."""
+    if T <= 0:
+        return []
+    if n >= T:
+        return list(range(T))
+    rows = sorted(set(int(round(x)) for x in torch.linspace(0, T - 1, n).tolist()))
+    if rows[-1] != T - 1:
+        rows.append(T - 1)
+    return rows
