@@ -1,0 +1,248 @@
+"""Benchmark of the KPool indexer hot path on one MI355X.
+
+One step = the whole path over one batch: kpool_compress + kpool_indexer_topk
+(logits, pool top-k and tail + expansion for every query chunk). Inputs are
+seeded synthetic tensors already resident in HBM when timing starts.
+
+Prints ONE JSON line: throughput in queries/s (tokens of the batch / step
+time), the roofline of the dominant kernel (the MFMA logits kernel, timed live
+with HIP events on the launch stream, priced against the BF16 or FP8 dense
+MFMA peak), per-phase achieved rates, and the CPU oracle timed on this host on
+a bounded sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME|IDX]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+import torch  # noqa: E402
+
+import workloads as wlm  # noqa: E402
+
+METRIC = "KPool indexer queries/s at 64K ctx; logits TFLOP/s as % of MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_FP8_TFLOPS = 5000.0
+PEAK_HBM_GBS = 8000.0
+
+
+def log(msg):
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def causal_counts(doc_lengths, kpool, k_sel):
+    """(sum of n_c over all queries, sum of n_c over queries that need
+    selection, number of such queries)."""
+    tot = need = rows = 0
+    for L in doc_lengths:
+        i = np.arange(L, dtype=np.int64)
+        nc = (i + 1) // kpool
+        tot += int(nc.sum())
+        m = nc > k_sel
+        need += int(nc[m].sum())
+        rows += int(m.sum())
+    return tot, need, rows
+
+
+class Path:
+    def __init__(self, inp: wlm.Inputs, dev="cuda:0"):
+        import sparse_attention_indexer_kpool_amd as kp
+        self.kp = kp
+        wl = inp.wl
+        self.inp = inp
+        self.p = kp.Params(num_docs=len(inp.doc_lengths), total_tokens=inp.T,
+                           max_seqlen=inp.max_seqlen, num_heads=wl.H, head_dim=wl.D,
+                           kpool=wl.kpool, index_topk=wl.index_topk,
+                           always_select_tail=int(wl.tail), use_fp8=int(wl.fp8),
+                           query_chunk=wl.query_chunk)
+        T = inp.T
+        self.q = inp.q.to(dev)
+        self.k = inp.k.to(dev)
+        self.gate = inp.gate.to(dev)
+        self.w = inp.w.to(dev)
+        self.ape = inp.ape.to(dev)
+        self.cu = inp.cu_seqlens.to(dev)
+        self.cu_pools = torch.zeros(len(inp.doc_lengths) + 1, dtype=torch.int32, device=dev)
+        self.pooled = torch.zeros(max(T // wl.kpool, 1), wl.D, dtype=torch.bfloat16, device=dev)
+        self.ws = torch.empty(max(kp.kpool_workspace_bytes(self.p), 256), dtype=torch.uint8,
+                              device=dev)
+        self.tok = torch.empty(T, self.p.width, dtype=torch.int32, device=dev)
+        self.qc = self.p.query_chunk if self.p.query_chunk > 0 else 4096
+        self.ld = kp.kpool_logits_ld(self.p)
+
+    def step(self):
+        kp = self.kp
+        kp.kpool_compress(self.p, self.k, self.gate, self.ape, self.cu, self.cu_pools, self.pooled)
+        kp.kpool_indexer_topk(self.p, self.q, self.w, self.pooled, self.cu, self.cu_pools,
+                              self.ws, self.tok, None)
+
+    # --- phases timed on their own (same launches as inside a step) --------
+    def phase_compress(self):
+        self.kp.kpool_compress(self.p, self.k, self.gate, self.ape, self.cu, self.cu_pools,
+                               self.pooled)
+
+    def phase_logits(self, logits):
+        kp = self.kp
+        for c0 in range(0, self.inp.T, self.qc):
+            c1 = min(self.inp.T, c0 + self.qc)
+            kp.kpool_logits(self.p, self.q, self.w, self.pooled, self.cu, self.cu_pools, c0, c1,
+                            self.ws, logits[:c1 - c0], flags=kp.KPOOL_LOGITS_SKIP_ALL_SELECTED)
+
+    def phase_select(self, logits, ids):
+        kp = self.kp
+        for c0 in range(0, self.inp.T, self.qc):
+            c1 = min(self.inp.T, c0 + self.qc)
+            kp.kpool_select(self.p, logits[:c1 - c0], c0, c1, self.cu, self.cu_pools, ids[c0:c1])
+
+    def phase_expand(self, ids):
+        self.kp.kpool_expand(self.p, ids, self.cu, self.cu_pools, self.tok)
+
+
+def time_region(fn, reps):
+    """Average ms of fn over reps, HIP events on torch's current stream (the
+    stream every launch of the library goes to)."""
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    s.record()
+    for _ in range(reps):
+        fn()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / reps
+
+
+def cpu_baseline(inp: wlm.Inputs, n_rows: int):
+    """The oracle as it stands on this host's cores: compress in full, then
+    scoring, selection and expansion of n_rows strided query rows."""
+    import oracle
+    wl = inp.wl
+    q = inp.q.float().numpy()
+    k = inp.k.float().numpy()
+    gate = inp.gate.float().numpy()
+    w = inp.w.numpy()
+    ape = inp.ape.numpy()
+    cu = inp.cu_seqlens.numpy().astype(np.int64)
+    t0 = time.perf_counter()
+    pooled, _ = oracle.compress(k, gate, ape, cu, wl.kpool)
+    t1 = time.perf_counter()
+    rows = wlm.strided_rows(inp.T, n_rows)
+    oracle.indexer_topk(q, w, pooled, cu, wl.kpool, wl.index_topk, wl.tail, rows=rows, fp8=wl.fp8)
+    t2 = time.perf_counter()
+    # per-query cost: the sampled rows plus their share of the compression
+    per_query = (t2 - t1) / len(rows) + (t1 - t0) / inp.T
+    threads = torch.get_num_threads()
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        pass
+    return {"value": round(1.0 / per_query, 2), "unit": "queries/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{wl.name}: compress of all {inp.T} tokens ({t1 - t0:.2f} s) + scoring, "
+                      f"top-k and expansion of {len(rows)} strided query rows ({t2 - t1:.2f} s); "
+                      f"NumPy FP32 on {os.cpu_count()} host CPUs"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="long_T65536_H32_D128")
+    ap.add_argument("--cpu-rows", type=int, default=512)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the indexer here runs "
+              "on a single device and has no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+    rank = int(os.environ.get("RANK", "0"))
+
+    wl = wlm.workload(int(args.workload)) if args.workload.isdigit() else wlm.workload(args.workload)
+    log(f"inputs {wl.name}")
+    inp = wlm.make_inputs(wl)
+    path = Path(inp)
+    T = inp.T
+    tot_nc, need_nc, need_rows = causal_counts(inp.doc_lengths, wl.kpool, wl.k_sel)
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        path.step()
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    ms = time_region(path.step, args.steps)
+    log(f"{ms:.3f} ms/step")
+
+    # phases, each timed live on the launch stream with the same launches
+    logits = torch.empty(path.qc, path.ld, dtype=torch.float32, device="cuda:0")
+    ids = torch.empty(T, wl.k_sel, dtype=torch.int32, device="cuda:0")
+    reps = max(3, min(args.steps, 10))
+    path.phase_logits(logits)      # also leaves the pooled keys / fp8 buffers in place
+    ms_compress = time_region(path.phase_compress, reps)
+    ms_logits = time_region(lambda: path.phase_logits(logits), reps)
+    ms_select = time_region(lambda: path.phase_select(logits, ids), reps)
+    ms_expand = time_region(lambda: path.phase_expand(ids), reps)
+    n_chunks = (T + path.qc - 1) // path.qc
+
+    flops = 2.0 * wl.H * wl.D * need_nc
+    peak = PEAK_FP8_TFLOPS if wl.fp8 else PEAK_BF16_TFLOPS
+    achieved = flops / (ms_logits * 1e-3) / 1e12
+    P = sum(L // wl.kpool for L in inp.doc_lengths)
+    by_compress = 4 * T * wl.D + 4 * wl.kpool * wl.D + 2 * P * wl.D
+    by_select = 4 * need_nc + 4 * T * wl.k_sel
+    by_expand = 4 * T * (wl.k_sel + wl.width)
+
+    def gbs(b, m):
+        return round(b / (m * 1e-3) / 1e9, 1)
+
+    out = {
+        "metric": METRIC,
+        "value": round(T / (ms * 1e-3), 1),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8" if wl.fp8 else "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "T": T, "H": wl.H, "D": wl.D, "kpool": wl.kpool,
+                   "index_topk": wl.index_topk, "always_select_tail": wl.tail,
+                   "query_chunk": path.qc, "docs": len(inp.doc_lengths), "fp8": wl.fp8},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                     "kernel": "logits_kernel", "launches_per_step": n_chunks,
+                     "algorithmic_flops_per_step": flops},
+        "phases_ms": {"compress": round(ms_compress, 4), "logits": round(ms_logits, 4),
+                      "select": round(ms_select, 4), "expand": round(ms_expand, 4)},
+        "phases_hbm": {
+            "compress": {"bytes": by_compress, "GB/s": gbs(by_compress, ms_compress),
+                         "frac": round(by_compress / (ms_compress * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+            "select": {"bytes": by_select, "GB/s": gbs(by_select, ms_select),
+                       "frac": round(by_select / (ms_select * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+            "expand": {"bytes": by_expand, "GB/s": gbs(by_expand, ms_expand),
+                       "frac": round(by_expand / (ms_expand * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+        },
+    }
+    if rank == 0 and not args.no_cpu_baseline:
+        log(f"cpu baseline on {args.cpu_rows} rows")
+        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_rows)
+    else:
+        out["cpu_baseline"] = None
+    if rank == 0:
+        print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

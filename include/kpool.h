@@ -1,0 +1,188 @@
+/*
+ * kpool.h -- C ABI of the KPool DSA indexer on AMD MI355X (gfx950).
+ *
+ * The indexer picks, for every query of a packed (THD) batch, the earlier
+ * tokens its sparse attention will read. The method is the KPool indexer of
+ * GLM-5.3-Flash as described on three pull-request pages, cited here by title
+ * and section:
+ *   [MLM] Megatron-LM PR #7054 "GLM5.3 Flash (KDA + mHC + KPool DSA) support +
+ *         FP8", section "3. KPool DSA indexer + NoPE";
+ *   [SKY] SkyRL PR #2179 "GLM-5.3-Flash (glm5_next) support", the commit
+ *         that adopts the k-pool indexer and "Limitations / follow-ups";
+ *   [XT]  xtuner PR #2108 "Add GLM-5.3-Flash F5: NoPE DSA + KPool indexer +
+ *         clamped SwiGLU", "Summary" and the F5 commit message.
+ *
+ * Notation. B documents, cu_seqlens cu[0..B] (int32, cu[0] = 0, cu[B] = T,
+ * non-decreasing). Document b holds tokens cu[b] .. cu[b+1]-1, length L_b.
+ * P_b = floor(L_b / kpool) complete pools; cu_pools cuP[b] = sum_{b'<b} P_b';
+ * P = cuP[B]. For token t of document b, i = t - cu[b] is its position,
+ * n_c(t) = floor((i + 1) / kpool) its causal pools (pools whose tokens are all
+ * at or before t), K_sel = index_topk / kpool (integer division), W =
+ * index_topk + kpool the output row width, and tail(t) = (i + 1) mod kpool
+ * when always_select_tail is set, else 0. max_pools = floor(max_seqlen / kpool).
+ *
+ * Memory. Every pointer is device memory owned by the caller unless stated
+ * otherwise. The library never allocates, frees or synchronises: work is
+ * enqueued on `stream` (a hipStream_t passed as void*; NULL = the null
+ * stream) and the caller synchronises. BF16 tensors are passed as raw 16-bit
+ * words. Outputs are overwritten in full, padding included.
+ *
+ * Errors. Every entry point checks its arguments before enqueuing anything;
+ * on failure it enqueues nothing, leaves the outputs untouched and returns a
+ * status, with a description in kpool_last_error() (per calling thread). A
+ * launch failure reported by the HIP runtime returns KPOOL_E_LAUNCH.
+ * Pointers must be 16-byte aligned (cu_seqlens, cu_pools, w, ape and
+ * row_scale: 4-byte aligned). The contents of cu_seqlens are a precondition
+ * that the host cannot see: for contents that break it, outputs are
+ * unspecified, but every kernel keeps its reads and writes inside the
+ * documented extents of the buffers.
+ */
+#ifndef KPOOL_H_
+#define KPOOL_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KPOOL_ABI_VERSION 1
+
+typedef enum {
+  KPOOL_OK = 0,
+  KPOOL_E_INVALID = 1,      /* null / misaligned pointer, inconsistent sizes   */
+  KPOOL_E_UNSUPPORTED = 2,  /* a valid shape this library has no kernel for    */
+  KPOOL_E_WORKSPACE = 3,    /* workspace smaller than kpool_workspace_bytes()  */
+  KPOOL_E_LAUNCH = 4        /* the HIP runtime reported an error               */
+} kpool_status;
+
+typedef struct {
+  int32_t num_docs;           /* B >= 1                                            */
+  int32_t total_tokens;       /* T >= 0, equals cu_seqlens[B]                      */
+  int32_t max_seqlen;         /* >= every L_b; sets max_pools and the tile width   */
+  int32_t num_heads;          /* H in {4, 8, 16, 32, 64}                           */
+  int32_t head_dim;           /* D in {64, 128}; the FP8 path needs D == 128       */
+  int32_t kpool;              /* 1 .. 64                                           */
+  int32_t index_topk;         /* >= kpool                                          */
+  int32_t always_select_tail; /* 0 / 1                                             */
+  int32_t use_fp8;            /* 0 / 1: FP8 input path                             */
+  int32_t query_chunk;        /* query rows per logits tile; 0 = default 4096      */
+  float   scale;              /* score scale inside the ReLU; 0 = head_dim^-1/2    */
+} kpool_params;
+
+/* KPOOL_ABI_VERSION of the built library. */
+int kpool_abi_version(void);
+
+/* Bytes of device workspace kpool_indexer_topk and kpool_logits need for
+ * these parameters (0 when T == 0). The workspace holds the FP32 logits tile
+ * (query_chunk x kpool_logits_ld floats), the pool ids of one chunk and, with
+ * use_fp8, the E4M3 codes and row scales of q and of the pooled keys. */
+size_t kpool_workspace_bytes(const kpool_params* p);
+
+/* Row stride, in floats, of the logits tiles of kpool_logits / kpool_select:
+ * max_pools rounded up to a multiple of 64. */
+int64_t kpool_logits_ld(const kpool_params* p);
+
+/* Step 1, key compression ([MLM] section 3; [SKY] k-pool commit). For each
+ * document b, pool p < P_b and dimension d, with slot tokens
+ * t_s = cu[b] + p*kpool + s:
+ *   a_s = gate[t_s, d] + ape[s, d]                (FP32)
+ *   pooled[cuP[b] + p, d] = BF16( sum_s softmax_s(a)[s] * k[t_s, d] )
+ * with FP32 accumulation and round-to-nearest-even to BF16. Pools restart at
+ * every document; a document's last L_b mod kpool tokens form no pool.
+ *   k, gate     BF16 [T, D] row-major
+ *   ape         FP32 [kpool, D]
+ *   cu_seqlens  int32 [B + 1]
+ *   cu_pools    out int32 [B + 1] (cuP)
+ *   pooled      out BF16 [floor(T / kpool), D]; rows P.. are not written
+ * Uses params: num_docs, total_tokens, head_dim, kpool. */
+kpool_status kpool_compress(const kpool_params* p, const void* k, const void* gate,
+                            const float* ape, const int32_t* cu_seqlens,
+                            int32_t* cu_pools, void* pooled, void* stream);
+
+/* Steps 2-4 for every query of the batch ([MLM] section 3; [SKY] limitations;
+ * [XT] summary and F5 commit):
+ *   score[t, p] = sum_h w[t, h] * ReLU(scale * q[t, h, :] . pooled[p, :])
+ * over the causal pools p = cuP[b] .. cuP[b] + n_c(t) - 1 of t's document;
+ * the min(K_sel, n_c(t)) best pools (ties to the lower pool id) are expanded,
+ * in ascending pool order, to their kpool tokens, followed by the tail(t)
+ * tokens cu[b] + n_c(t)*kpool .. t, then -1 up to width W. Query rows are
+ * processed query_chunk at a time through a logits tile in the workspace.
+ * With use_fp8 the q rows (t, h) and the pooled rows first go through the FP8
+ * input path of kpool_fp8_quantize and are scored from their E4M3 codes and
+ * power-of-two scales.
+ *   q          BF16 [T, H, D]
+ *   w          FP32 [T, H]
+ *   pooled     BF16 [floor(T / kpool), D] as written by kpool_compress
+ *   cu_pools   int32 [B + 1] as written by kpool_compress
+ *   workspace  at least kpool_workspace_bytes(p) bytes, 256-byte aligned
+ *   out_token_idx  out int32 [T, W]: global token indices, ascending, -1 pad
+ *   out_pool_idx   out int32 [T, K_sel] (may be NULL): global pool ids,
+ *                  ascending, -1 pad */
+kpool_status kpool_indexer_topk(const kpool_params* p, const void* q, const float* w,
+                                const void* pooled, const int32_t* cu_seqlens,
+                                const int32_t* cu_pools, void* workspace,
+                                size_t workspace_bytes, int32_t* out_token_idx,
+                                int32_t* out_pool_idx, void* stream);
+
+/* Step 2 alone, for query rows q_begin .. q_end-1 (0 <= q_begin <= q_end <= T):
+ *   out[r, j] = score of row t = q_begin + r against doc-local pool j of t's
+ *               document, for j < n_c(t)
+ * (row stride ld = kpool_logits_ld(p) floats). Same scoring as
+ * kpool_indexer_topk, including the FP8 path (whose quantised q rows and keys
+ * are written to the workspace first). flags:
+ *   KPOOL_LOGITS_FILL_MASKED  also write -inf in columns n_c(t) .. ld-1
+ *   KPOOL_LOGITS_SKIP_ALL_SELECTED  rows whose n_c(t) <= K_sel may be left
+ *       unwritten (their selection takes every pool); this is the launch
+ *       kpool_indexer_topk makes for each query chunk.
+ * Columns and rows not covered by the flags are left untouched. */
+#define KPOOL_LOGITS_FILL_MASKED 1
+#define KPOOL_LOGITS_SKIP_ALL_SELECTED 2
+kpool_status kpool_logits(const kpool_params* p, const void* q, const float* w,
+                          const void* pooled, const int32_t* cu_seqlens,
+                          const int32_t* cu_pools, int32_t q_begin, int32_t q_end,
+                          void* workspace, size_t workspace_bytes, float* out,
+                          int32_t flags, void* stream);
+
+/* Step 3 alone: for rows r of a logits tile laid out as kpool_logits writes it
+ * (row stride kpool_logits_ld(p)), the min(K_sel, n_c(t)) largest scores of
+ * columns 0 .. n_c(t)-1, t = q_begin + r; larger score first, equal scores to
+ * the lower column, NaN ranks as -inf. Writes global pool ids cuP[b] + j in
+ * ascending order, -1 padded, to out_pool_idx [q_end - q_begin, K_sel]. */
+kpool_status kpool_select(const kpool_params* p, const float* logits, int32_t q_begin,
+                          int32_t q_end, const int32_t* cu_seqlens,
+                          const int32_t* cu_pools, int32_t* out_pool_idx, void* stream);
+
+/* Step 4 alone, for every query t: expands the pool ids of row t of pool_idx
+ * [T, K_sel] (global ids, ascending, -1 padded, min(K_sel, n_c(t)) valid) to
+ * kpool consecutive tokens each and appends the tail:
+ *   out[t, j] = cu[b] + (id - cuP[b])*kpool + (j mod kpool),
+ *               id = pool_idx[t, j / kpool],           j < kpool*n_sel
+ *   then the tail(t) tokens cu[b] + n_c(t)*kpool .. t, then -1 to width W. */
+kpool_status kpool_expand(const kpool_params* p, const int32_t* pool_idx,
+                          const int32_t* cu_seqlens, const int32_t* cu_pools,
+                          int32_t* out_token_idx, void* stream);
+
+/* FP8 input path ([MLM] section 3) for `rows` rows of 128 BF16 values:
+ *   y = BF16( FWHT_128(x) * FP32(128^-1/2) )   FP32 butterflies, stages
+ *        h = 1, 2, ..., 64, (a, b) -> (a + b, a - b), Sylvester order
+ *   e = min{ e integer : max|y| <= 448 * 2^e } (0 for an all-zero row)
+ *   codes = E4M3 (OCP e4m3fn, round to nearest even, subnormals kept) of
+ *           y * 2^-e;  row_scale = 2^e
+ *   x      BF16 [rows, 128];  codes out uint8 [rows, 128];
+ *   row_scale out FP32 [rows]. */
+kpool_status kpool_fp8_quantize(const void* x, int32_t rows, uint8_t* codes,
+                                float* row_scale, void* stream);
+
+/* Static description of a status code. */
+const char* kpool_status_string(kpool_status s);
+
+/* Detail of the last failure of the calling thread ("" if none). */
+const char* kpool_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KPOOL_H_ */

@@ -1,0 +1,203 @@
+"""Python binding of libkpool.so, the KPool DSA indexer for AMD MI355X (gfx950).
+
+The functions below carry the names of the C entry points in include/kpool.h
+and only marshal arguments: torch tensors supply device pointers and the
+current HIP stream, every step of the indexer runs in the library's HIP
+kernels. There is no fallback: when libkpool.so is missing, or a tensor is not
+on the GPU, a call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libkpool.so")
+
+KPOOL_OK, KPOOL_E_INVALID, KPOOL_E_UNSUPPORTED, KPOOL_E_WORKSPACE, KPOOL_E_LAUNCH = range(5)
+
+
+class KPoolError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"kpool status {status}: {detail}")
+        self.status = status
+        self.detail = detail
+
+
+class _Params(ctypes.Structure):
+    _fields_ = [
+        ("num_docs", ctypes.c_int32),
+        ("total_tokens", ctypes.c_int32),
+        ("max_seqlen", ctypes.c_int32),
+        ("num_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("kpool", ctypes.c_int32),
+        ("index_topk", ctypes.c_int32),
+        ("always_select_tail", ctypes.c_int32),
+        ("use_fp8", ctypes.c_int32),
+        ("query_chunk", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+    ]
+
+
+@dataclass
+class Params:
+    """Mirror of kpool_params (include/kpool.h)."""
+    num_docs: int
+    total_tokens: int
+    max_seqlen: int
+    num_heads: int
+    head_dim: int
+    kpool: int = 4
+    index_topk: int = 2048
+    always_select_tail: int = 1
+    use_fp8: int = 0
+    query_chunk: int = 0
+    scale: float = 0.0
+
+    def c(self) -> _Params:
+        return _Params(int(self.num_docs), int(self.total_tokens), int(self.max_seqlen),
+                       int(self.num_heads), int(self.head_dim), int(self.kpool),
+                       int(self.index_topk), int(self.always_select_tail), int(self.use_fp8),
+                       int(self.query_chunk), float(self.scale))
+
+    @property
+    def k_sel(self) -> int:
+        return self.index_topk // self.kpool
+
+    @property
+    def width(self) -> int:
+        return self.index_topk + self.kpool
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libkpool.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m sparse_attention_indexer_kpool_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.POINTER(_Params)
+        vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        L.kpool_abi_version.restype = ctypes.c_int
+        L.kpool_abi_version.argtypes = []
+        L.kpool_workspace_bytes.restype = sz
+        L.kpool_workspace_bytes.argtypes = [P]
+        L.kpool_logits_ld.restype = ctypes.c_int64
+        L.kpool_logits_ld.argtypes = [P]
+        L.kpool_compress.restype = ctypes.c_int
+        L.kpool_compress.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
+        L.kpool_indexer_topk.restype = ctypes.c_int
+        L.kpool_indexer_topk.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp]
+        L.kpool_logits.restype = ctypes.c_int
+        L.kpool_logits.argtypes = [P, vp, vp, vp, vp, vp, i32, i32, vp, sz, vp, i32, vp]
+        L.kpool_select.restype = ctypes.c_int
+        L.kpool_select.argtypes = [P, vp, i32, i32, vp, vp, vp, vp]
+        L.kpool_expand.restype = ctypes.c_int
+        L.kpool_expand.argtypes = [P, vp, vp, vp, vp, vp]
+        L.kpool_fp8_quantize.restype = ctypes.c_int
+        L.kpool_fp8_quantize.argtypes = [vp, i32, vp, vp, vp]
+        L.kpool_status_string.restype = ctypes.c_char_p
+        L.kpool_status_string.argtypes = [ctypes.c_int]
+        L.kpool_last_error.restype = ctypes.c_char_p
+        L.kpool_last_error.argtypes = []
+        _lib = L
+    return _lib
+
+
+EXPORTS = ["kpool_abi_version", "kpool_workspace_bytes", "kpool_logits_ld", "kpool_compress",
+           "kpool_indexer_topk", "kpool_logits", "kpool_select", "kpool_expand",
+           "kpool_fp8_quantize", "kpool_status_string", "kpool_last_error"]
+
+
+def _check(status: int) -> None:
+    if status != KPOOL_OK:
+        raise KPoolError(status, lib().kpool_last_error().decode())
+
+
+def _ptr(t) -> int:
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def kpool_abi_version() -> int:
+    return lib().kpool_abi_version()
+
+
+def kpool_workspace_bytes(p: Params) -> int:
+    return int(lib().kpool_workspace_bytes(ctypes.byref(p.c())))
+
+
+def kpool_logits_ld(p: Params) -> int:
+    return int(lib().kpool_logits_ld(ctypes.byref(p.c())))
+
+
+def kpool_compress(p: Params, k, gate, ape, cu_seqlens, cu_pools, pooled, stream=None) -> None:
+    _check(lib().kpool_compress(ctypes.byref(p.c()), _ptr(k), _ptr(gate), _ptr(ape),
+                                _ptr(cu_seqlens), _ptr(cu_pools), _ptr(pooled), _stream(stream)))
+
+
+def kpool_indexer_topk(p: Params, q, w, pooled, cu_seqlens, cu_pools, workspace,
+                       out_token_idx, out_pool_idx=None, stream=None) -> None:
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().kpool_indexer_topk(ctypes.byref(p.c()), _ptr(q), _ptr(w), _ptr(pooled),
+                                    _ptr(cu_seqlens), _ptr(cu_pools), _ptr(workspace), ws_bytes,
+                                    _ptr(out_token_idx), _ptr(out_pool_idx), _stream(stream)))
+
+
+KPOOL_LOGITS_FILL_MASKED = 1
+KPOOL_LOGITS_SKIP_ALL_SELECTED = 2
+
+
+def kpool_logits(p: Params, q, w, pooled, cu_seqlens, cu_pools, q_begin, q_end, workspace,
+                 out, flags=KPOOL_LOGITS_FILL_MASKED, stream=None) -> None:
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().kpool_logits(ctypes.byref(p.c()), _ptr(q), _ptr(w), _ptr(pooled),
+                              _ptr(cu_seqlens), _ptr(cu_pools), int(q_begin), int(q_end),
+                              _ptr(workspace), ws_bytes, _ptr(out), int(flags),
+                              _stream(stream)))
+
+
+def kpool_select(p: Params, logits, q_begin, q_end, cu_seqlens, cu_pools, out_pool_idx,
+                 stream=None) -> None:
+    _check(lib().kpool_select(ctypes.byref(p.c()), _ptr(logits), int(q_begin), int(q_end),
+                              _ptr(cu_seqlens), _ptr(cu_pools), _ptr(out_pool_idx),
+                              _stream(stream)))
+
+
+def kpool_expand(p: Params, pool_idx, cu_seqlens, cu_pools, out_token_idx, stream=None) -> None:
+    _check(lib().kpool_expand(ctypes.byref(p.c()), _ptr(pool_idx), _ptr(cu_seqlens),
+                              _ptr(cu_pools), _ptr(out_token_idx), _stream(stream)))
+
+
+def kpool_fp8_quantize(x, rows, codes, row_scale, stream=None) -> None:
+    _check(lib().kpool_fp8_quantize(_ptr(x), int(rows), _ptr(codes), _ptr(row_scale),
+                                    _stream(stream)))
+
+
+def kpool_status_string(status: int) -> str:
+    return lib().kpool_status_string(int(status)).decode()
+
+
+def kpool_last_error() -> str:
+    return lib().kpool_last_error().decode()

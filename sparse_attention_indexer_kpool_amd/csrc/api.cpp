@@ -1,0 +1,339 @@
+// C ABI of libkpool.so: argument checks, workspace layout and the query-chunk
+// loop of the KPool indexer. The operations themselves are documented in
+// include/kpool.h; this file only validates and enqueues kernels.
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "kpool.h"
+#include "kpool_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+kpool_status fail(kpool_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+kpool_status ok() {
+  g_last_error.clear();
+  return KPOOL_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+constexpr int kDefaultQueryChunk = 4096;
+
+struct Derived {
+  int B, T, H, D, kpool, topk, k_sel, width, max_pools, qc, tail, fp8;
+  int64_t ld;
+  float scale;
+  size_t off_logits, off_ids, off_qc, off_qs, off_kc, off_ks, total;
+};
+
+kpool_status derive(const kpool_params* p, Derived* d, bool need_heads) {
+  if (!p) return fail(KPOOL_E_INVALID, "params is null");
+  d->B = p->num_docs;
+  d->T = p->total_tokens;
+  d->H = p->num_heads;
+  d->D = p->head_dim;
+  d->kpool = p->kpool;
+  d->topk = p->index_topk;
+  d->tail = p->always_select_tail;
+  d->fp8 = p->use_fp8;
+  if (d->B < 1) return fail(KPOOL_E_INVALID, "num_docs must be >= 1 (got %d)", d->B);
+  if (d->T < 0) return fail(KPOOL_E_INVALID, "total_tokens must be >= 0 (got %d)", d->T);
+  if (p->max_seqlen < 0 || p->max_seqlen > d->T)
+    return fail(KPOOL_E_INVALID, "max_seqlen must be in [0, total_tokens] (got %d, T = %d)",
+                p->max_seqlen, d->T);
+  if (d->kpool < 1 || d->kpool > 64)
+    return fail(KPOOL_E_UNSUPPORTED, "kpool must be in [1, 64] (got %d)", d->kpool);
+  if (d->D != 64 && d->D != 128)
+    return fail(KPOOL_E_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", d->D);
+  if (d->tail != 0 && d->tail != 1)
+    return fail(KPOOL_E_INVALID, "always_select_tail must be 0 or 1");
+  if (d->fp8 != 0 && d->fp8 != 1) return fail(KPOOL_E_INVALID, "use_fp8 must be 0 or 1");
+  if (need_heads) {
+    if (d->H != 4 && d->H != 8 && d->H != 16 && d->H != 32 && d->H != 64)
+      return fail(KPOOL_E_UNSUPPORTED, "num_heads must be 4, 8, 16, 32 or 64 (got %d)", d->H);
+    if (d->topk < d->kpool)
+      return fail(KPOOL_E_INVALID, "index_topk (%d) must be >= kpool (%d)", d->topk, d->kpool);
+    if (d->topk > (1 << 24)) return fail(KPOOL_E_UNSUPPORTED, "index_topk too large");
+    if (d->fp8 && d->D != 128)
+      return fail(KPOOL_E_UNSUPPORTED, "the FP8 path needs head_dim == 128 (got %d)", d->D);
+    if (p->query_chunk < 0) return fail(KPOOL_E_INVALID, "query_chunk must be >= 0");
+    if (!(p->scale >= 0.f) || p->scale > 1e30f)
+      return fail(KPOOL_E_INVALID, "scale must be finite and >= 0 (0 = head_dim^-1/2)");
+  }
+  d->k_sel = d->topk / d->kpool;
+  d->width = d->topk + d->kpool;
+  d->max_pools = p->max_seqlen / d->kpool;
+  if (need_heads && d->max_pools > kpool::kMaxSelectPools)
+    return fail(KPOOL_E_UNSUPPORTED, "max_seqlen / kpool = %d exceeds %d pools per document",
+                d->max_pools, kpool::kMaxSelectPools);
+  d->ld = (int64_t)round_up((size_t)std::max(d->max_pools, 1), 64);
+  d->scale = p->scale > 0.f ? p->scale : 1.0f / sqrtf((float)d->D);
+  int qc = p->query_chunk > 0 ? p->query_chunk : kDefaultQueryChunk;
+  d->qc = std::max(1, std::min(qc, std::max(d->T, 1)));
+  // workspace layout (256-byte aligned pieces)
+  size_t off = 0;
+  d->off_logits = off;
+  off = round_up(off + (size_t)d->qc * d->ld * 4, 256);
+  d->off_ids = off;
+  off = round_up(off + (size_t)d->qc * std::max(d->k_sel, 1) * 4, 256);
+  d->off_qc = d->off_qs = d->off_kc = d->off_ks = off;
+  if (d->fp8) {
+    const size_t qrows = (size_t)d->T * d->H, krows = (size_t)(d->T / d->kpool);
+    d->off_qc = off;
+    off = round_up(off + qrows * 128, 256);
+    d->off_qs = off;
+    off = round_up(off + qrows * 4, 256);
+    d->off_kc = off;
+    off = round_up(off + krows * 128, 256);
+    d->off_ks = off;
+    off = round_up(off + krows * 4, 256);
+  }
+  d->total = d->T > 0 ? off : 0;
+  return KPOOL_OK;
+}
+
+kpool_status check_ptr(const void* ptr, size_t align, const char* name) {
+  if (!ptr) return fail(KPOOL_E_INVALID, "%s is null", name);
+  if (!aligned(ptr, align)) return fail(KPOOL_E_INVALID, "%s is not %zu-byte aligned", name, align);
+  return KPOOL_OK;
+}
+
+#define CHECK(expr)                       \
+  do {                                    \
+    kpool_status s_ = (expr);             \
+    if (s_ != KPOOL_OK) return s_;        \
+  } while (0)
+
+kpool_status after_launch() {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(KPOOL_E_LAUNCH, "HIP launch error: %s", hipGetErrorString(e));
+  return ok();
+}
+
+kpool::LogitsArgs logits_args(const Derived& d, const void* q, const float* w, const void* pooled,
+                              const int32_t* cu, const int32_t* cuP, uint8_t* ws) {
+  kpool::LogitsArgs a{};
+  a.q = d.fp8 ? (const void*)(ws + d.off_qc) : q;
+  a.q_scale = d.fp8 ? reinterpret_cast<const float*>(ws + d.off_qs) : nullptr;
+  a.w = w;
+  a.keys = d.fp8 ? (const void*)(ws + d.off_kc) : pooled;
+  a.k_scale = d.fp8 ? reinterpret_cast<const float*>(ws + d.off_ks) : nullptr;
+  a.cu = cu;
+  a.cu_pools = cuP;
+  a.B = d.B; a.T = d.T; a.H = d.H; a.D = d.D; a.kpool = d.kpool;
+  a.max_pools = d.max_pools; a.k_sel = d.k_sel; a.scale = d.scale;
+  a.ld = d.ld;
+  a.fp8 = d.fp8;
+  return a;
+}
+
+void quantize_inputs(const Derived& d, const void* q, const void* pooled, const int32_t* cuP,
+                     int q_begin, int q_end, uint8_t* ws, hipStream_t st) {
+  const size_t qrow0 = (size_t)q_begin * d.H;
+  const int qrows = (q_end - q_begin) * d.H;
+  kpool::launch_fp8_quantize(reinterpret_cast<const uint16_t*>(q) + qrow0 * 128, qrows, nullptr,
+                             ws + d.off_qc + qrow0 * 128,
+                             reinterpret_cast<float*>(ws + d.off_qs) + qrow0, st);
+  kpool::launch_fp8_quantize(reinterpret_cast<const uint16_t*>(pooled), d.T / d.kpool,
+                             cuP + d.B, ws + d.off_kc, reinterpret_cast<float*>(ws + d.off_ks), st);
+}
+
+}  // namespace
+
+extern "C" {
+
+int kpool_abi_version(void) { return KPOOL_ABI_VERSION; }
+
+size_t kpool_workspace_bytes(const kpool_params* p) {
+  Derived d;
+  if (derive(p, &d, true) != KPOOL_OK) return 0;
+  return d.total;
+}
+
+int64_t kpool_logits_ld(const kpool_params* p) {
+  Derived d;
+  if (derive(p, &d, true) != KPOOL_OK) return 0;
+  return d.ld;
+}
+
+kpool_status kpool_compress(const kpool_params* p, const void* k, const void* gate,
+                            const float* ape, const int32_t* cu_seqlens, int32_t* cu_pools,
+                            void* pooled, void* stream) {
+  Derived d;
+  CHECK(derive(p, &d, false));
+  CHECK(check_ptr(cu_seqlens, 4, "cu_seqlens"));
+  CHECK(check_ptr(cu_pools, 4, "cu_pools"));
+  if (d.T / d.kpool > 0) {
+    CHECK(check_ptr(k, 16, "k"));
+    CHECK(check_ptr(gate, 16, "gate"));
+    CHECK(check_ptr(ape, 16, "ape"));
+    CHECK(check_ptr(pooled, 16, "pooled"));
+  }
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  kpool::launch_cu_pools(cu_seqlens, d.B, d.kpool, cu_pools, st);
+  kpool::launch_compress(reinterpret_cast<const uint16_t*>(k),
+                         reinterpret_cast<const uint16_t*>(gate), ape, cu_seqlens, cu_pools, d.B,
+                         d.T, d.D, d.kpool, reinterpret_cast<uint16_t*>(pooled), st);
+  return after_launch();
+}
+
+kpool_status kpool_indexer_topk(const kpool_params* p, const void* q, const float* w,
+                                const void* pooled, const int32_t* cu_seqlens,
+                                const int32_t* cu_pools, void* workspace,
+                                size_t workspace_bytes, int32_t* out_token_idx,
+                                int32_t* out_pool_idx, void* stream) {
+  Derived d;
+  CHECK(derive(p, &d, true));
+  if (d.T == 0) return ok();
+  CHECK(check_ptr(q, 16, "q"));
+  CHECK(check_ptr(w, 4, "w"));
+  CHECK(check_ptr(cu_seqlens, 4, "cu_seqlens"));
+  CHECK(check_ptr(cu_pools, 4, "cu_pools"));
+  CHECK(check_ptr(out_token_idx, 16, "out_token_idx"));
+  if (out_pool_idx) CHECK(check_ptr(out_pool_idx, 4, "out_pool_idx"));
+  if (d.T / d.kpool > 0) CHECK(check_ptr(pooled, 16, "pooled"));
+  CHECK(check_ptr(workspace, 256, "workspace"));
+  if (workspace_bytes < d.total)
+    return fail(KPOOL_E_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, d.total);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
+  (void)hipGetLastError();
+  if (d.fp8) quantize_inputs(d, q, pooled, cu_pools, 0, d.T, ws, st);
+  kpool::LogitsArgs a = logits_args(d, q, w, pooled, cu_seqlens, cu_pools, ws);
+  a.out = reinterpret_cast<float*>(ws + d.off_logits);
+  a.skip_select_all = 1;
+  for (int c0 = 0; c0 < d.T; c0 += d.qc) {
+    const int c1 = std::min(d.T, c0 + d.qc);
+    a.q_begin = c0;
+    a.q_end = c1;
+    kpool::launch_logits(a, st);
+    int32_t* ids = out_pool_idx ? out_pool_idx + (size_t)c0 * d.k_sel
+                                : reinterpret_cast<int32_t*>(ws + d.off_ids);
+    kpool::launch_select(a.out, d.ld, c0, c1, cu_seqlens, cu_pools, d.B, d.T, d.kpool, d.k_sel,
+                         d.max_pools, ids, st);
+    kpool::launch_expand(ids, c0, c1, cu_seqlens, cu_pools, d.B, d.T, d.kpool, d.k_sel, d.width,
+                         d.tail, d.max_pools, out_token_idx + (size_t)c0 * d.width, st);
+  }
+  return after_launch();
+}
+
+kpool_status kpool_logits(const kpool_params* p, const void* q, const float* w,
+                          const void* pooled, const int32_t* cu_seqlens,
+                          const int32_t* cu_pools, int32_t q_begin, int32_t q_end,
+                          void* workspace, size_t workspace_bytes, float* out, int32_t flags,
+                          void* stream) {
+  Derived d;
+  CHECK(derive(p, &d, true));
+  if (flags & ~(KPOOL_LOGITS_FILL_MASKED | KPOOL_LOGITS_SKIP_ALL_SELECTED))
+    return fail(KPOOL_E_INVALID, "unknown logits flags 0x%x", flags);
+  if (q_begin < 0 || q_end < q_begin || q_end > d.T)
+    return fail(KPOOL_E_INVALID, "query rows [%d, %d) outside [0, %d]", q_begin, q_end, d.T);
+  if (q_end == q_begin) return ok();
+  CHECK(check_ptr(q, 16, "q"));
+  CHECK(check_ptr(w, 4, "w"));
+  CHECK(check_ptr(cu_seqlens, 4, "cu_seqlens"));
+  CHECK(check_ptr(cu_pools, 4, "cu_pools"));
+  CHECK(check_ptr(out, 16, "out"));
+  if (d.T / d.kpool > 0) CHECK(check_ptr(pooled, 16, "pooled"));
+  if (d.fp8) {
+    CHECK(check_ptr(workspace, 256, "workspace"));
+    if (workspace_bytes < d.total)
+      return fail(KPOOL_E_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, d.total);
+  }
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
+  (void)hipGetLastError();
+  if (d.fp8) quantize_inputs(d, q, pooled, cu_pools, q_begin, q_end, ws, st);
+  kpool::LogitsArgs a = logits_args(d, q, w, pooled, cu_seqlens, cu_pools, ws);
+  a.out = out;
+  a.q_begin = q_begin;
+  a.q_end = q_end;
+  a.fill_masked = (flags & KPOOL_LOGITS_FILL_MASKED) ? 1 : 0;
+  a.skip_select_all = (flags & KPOOL_LOGITS_SKIP_ALL_SELECTED) ? 1 : 0;
+  kpool::launch_logits(a, st);
+  return after_launch();
+}
+
+kpool_status kpool_select(const kpool_params* p, const float* logits, int32_t q_begin,
+                          int32_t q_end, const int32_t* cu_seqlens, const int32_t* cu_pools,
+                          int32_t* out_pool_idx, void* stream) {
+  Derived d;
+  CHECK(derive(p, &d, true));
+  if (q_begin < 0 || q_end < q_begin || q_end > d.T)
+    return fail(KPOOL_E_INVALID, "query rows [%d, %d) outside [0, %d]", q_begin, q_end, d.T);
+  if (q_end == q_begin) return ok();
+  CHECK(check_ptr(logits, 16, "logits"));
+  CHECK(check_ptr(cu_seqlens, 4, "cu_seqlens"));
+  CHECK(check_ptr(cu_pools, 4, "cu_pools"));
+  CHECK(check_ptr(out_pool_idx, 4, "out_pool_idx"));
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  kpool::launch_select(logits, d.ld, q_begin, q_end, cu_seqlens, cu_pools, d.B, d.T, d.kpool,
+                       d.k_sel, d.max_pools, out_pool_idx, st);
+  return after_launch();
+}
+
+kpool_status kpool_expand(const kpool_params* p, const int32_t* pool_idx,
+                          const int32_t* cu_seqlens, const int32_t* cu_pools,
+                          int32_t* out_token_idx, void* stream) {
+  Derived d;
+  CHECK(derive(p, &d, true));
+  if (d.T == 0) return ok();
+  CHECK(check_ptr(pool_idx, 4, "pool_idx"));
+  CHECK(check_ptr(cu_seqlens, 4, "cu_seqlens"));
+  CHECK(check_ptr(cu_pools, 4, "cu_pools"));
+  CHECK(check_ptr(out_token_idx, 16, "out_token_idx"));
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  kpool::launch_expand(pool_idx, 0, d.T, cu_seqlens, cu_pools, d.B, d.T, d.kpool, d.k_sel,
+                       d.width, d.tail, d.max_pools, out_token_idx, st);
+  return after_launch();
+}
+
+kpool_status kpool_fp8_quantize(const void* x, int32_t rows, uint8_t* codes, float* row_scale,
+                                void* stream) {
+  if (rows < 0) return fail(KPOOL_E_INVALID, "rows must be >= 0 (got %d)", rows);
+  if (rows == 0) return ok();
+  CHECK(check_ptr(x, 16, "x"));
+  CHECK(check_ptr(codes, 16, "codes"));
+  CHECK(check_ptr(row_scale, 4, "row_scale"));
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  kpool::launch_fp8_quantize(reinterpret_cast<const uint16_t*>(x), rows, nullptr, codes, row_scale,
+                             st);
+  return after_launch();
+}
+
+const char* kpool_status_string(kpool_status s) {
+  switch (s) {
+    case KPOOL_OK: return "ok";
+    case KPOOL_E_INVALID: return "invalid argument";
+    case KPOOL_E_UNSUPPORTED: return "unsupported shape";
+    case KPOOL_E_WORKSPACE: return "workspace too small";
+    case KPOOL_E_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+const char* kpool_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

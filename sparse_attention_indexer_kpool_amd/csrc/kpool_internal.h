@@ -1,0 +1,52 @@
+// Host-side launchers of the KPool kernels (internal to libkpool.so). Every
+// launcher assumes its arguments were validated by the C-ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kpool {
+
+void launch_cu_pools(const int32_t* cu, int B, int kpool, int32_t* cu_pools, hipStream_t st);
+
+void launch_compress(const uint16_t* k, const uint16_t* gate, const float* ape,
+                     const int32_t* cu, const int32_t* cu_pools, int B, int T, int D,
+                     int kpool, uint16_t* pooled, hipStream_t st);
+
+// FP8 input path over `rows` rows of 128 BF16 values. When rows_dev is not
+// null, rows at or beyond *rows_dev are skipped (the count lives on the
+// device, e.g. cu_pools[B]).
+void launch_fp8_quantize(const uint16_t* x, int rows, const int32_t* rows_dev,
+                         uint8_t* codes, float* row_scale, hipStream_t st);
+
+struct LogitsArgs {
+  const void* q;            // BF16 [T, H, D] or E4M3 codes [T, H, 128]
+  const float* q_scale;     // FP8 path: FP32 [T, H] row scales, else null
+  const float* w;           // FP32 [T, H]
+  const void* keys;         // BF16 [T/kpool, D] or E4M3 codes [T/kpool, 128]
+  const float* k_scale;     // FP8 path: FP32 [T/kpool] row scales, else null
+  const int32_t* cu;
+  const int32_t* cu_pools;
+  int B, T, H, D, kpool, max_pools, k_sel;
+  float scale;
+  int q_begin, q_end;       // global query rows of this launch
+  float* out;               // FP32 [q_end - q_begin, ld]
+  int64_t ld;
+  int fill_masked;          // 1: write -inf in columns n_c .. ld-1
+  int skip_select_all;      // 1: leave rows with n_c <= k_sel unwritten
+  int fp8;
+};
+void launch_logits(const LogitsArgs& a, hipStream_t st);
+
+void launch_select(const float* logits, int64_t ld, int q_begin, int q_end,
+                   const int32_t* cu, const int32_t* cu_pools, int B, int T, int kpool,
+                   int k_sel, int max_pools, int32_t* out_ids, hipStream_t st);
+
+void launch_expand(const int32_t* pool_ids, int q_begin, int q_end, const int32_t* cu,
+                   const int32_t* cu_pools, int B, int T, int kpool, int k_sel, int width,
+                   int tail, int max_pools, int32_t* out, hipStream_t st);
+
+// Largest max_pools the selection kernel handles (rows live in registers).
+constexpr int kMaxSelectPools = 65536;
+
+}  // namespace kpool

@@ -1,0 +1,411 @@
+// Step 2 of the KPool indexer: pool scores of a chunk of query rows.
+//
+//   score[t, j] = sum_h w[t, h] * ReLU(scale * q[t, h, :] . pooled[cuP[b] + j, :])
+//
+// for the causal pools j < n_c(t) of t's document. Megatron-LM PR #7054,
+// section "3. KPool DSA indexer + NoPE" (top-k over pools, FP32 head weights);
+// xtuner PR #2108, F5 commit (the DSA indexer score with head_dim^-1/2 inside
+// the ReLU, which ReLU's positive homogeneity lets us fold into w) and
+// "Summary" (the logits tile is bounded by query chunking).
+//
+// A dense contraction on MFMA: M = (query, head) rows, N = pools, K = D. A
+// wave keeps MT row tiles of 32 (query, head) rows of q in registers for the
+// whole launch (A operand) and sweeps the document's causal pools; a
+// workgroup of NW waves shares each 64-pool tile of keys through LDS (B
+// operand, rows padded by 16 bytes so the 16-byte lane reads of one pass hit
+// distinct banks). The epilogue stays in registers: each lane holds 16 rows of
+// one pool column of a 32 x 32 accumulator, multiplies by w' = w * scale,
+// clamps at 0 and sums the heads of each query, then adds the other half-wave.
+//
+// bf16: v_mfma_f32_32x32x16_bf16. fp8: v_mfma_f32_32x32x64_f8f6f4 on E4M3
+// codes; the row scales of q fold into w' and the key scales multiply the
+// head sum (both are powers of two, so this is exact up to FP32 rounding).
+//
+// The K index is permuted identically for A and B (lane half g takes a
+// contiguous slice of D), which leaves every dot product unchanged and lets a
+// lane read one contiguous run of q and of each key row.
+
+#include <algorithm>
+#include <type_traits>
+
+#include "kpool_device.h"
+#include "kpool_internal.h"
+
+namespace kpool {
+
+// FP8 MFMA K: 64 uses v_mfma_f32_32x32x64_f8f6f4, 16 uses
+// v_mfma_f32_32x32x16_fp8_fp8.
+#ifndef KPOOL_FP8_MFMA_K
+#define KPOOL_FP8_MFMA_K 64
+#endif
+constexpr int kFp8K = KPOOL_FP8_MFMA_K;
+static_assert(kFp8K == 64 || kFp8K == 16, "FP8 MFMA K");
+
+constexpr int kLogitsWaves = 8;
+constexpr int kPoolTile = 64;      // pools per LDS stage (two 32-wide MFMA tiles)
+
+template <int H, int D, bool FP8>
+struct LogitsCfg {
+  static constexpr int MT = 2;                       // 32-row tiles per wave
+  static constexpr int QPW = 32 * MT / H;            // queries per wave (H <= 32)
+  static constexpr int QPB = kLogitsWaves * (QPW > 0 ? QPW : 1);   // queries per workgroup
+  static constexpr int ROWB = FP8 ? D : 2 * D;       // bytes per key row
+  static constexpr int CPR = ROWB / 16;              // 16-byte chunks per key row
+  static constexpr int TILE_BYTES = kPoolTile * ROWB;
+  static constexpr int LPW = TILE_BYTES / (1024 * kLogitsWaves);   // 1 KB loads per wave
+  static constexpr int KSTEP = FP8 ? kFp8K : 16;     // K per MFMA
+  static constexpr int NSTEP = D / KSTEP;            // MFMAs per 32 x 32 tile
+  static_assert(LPW >= 1 && LPW * 1024 * kLogitsWaves == TILE_BYTES, "tile split");
+};
+
+// LDS tile layout: key row r (0..63) occupies ROWB contiguous bytes; its
+// 16-byte chunk c sits at chunk position c ^ f(r). A 16-byte lane read is
+// served 16 lanes (256 bytes) per pass; the lanes of a pass read 16
+// consecutive rows at one chunk, and f spreads them over 16 bank groups:
+// 256-byte rows use f(r) = r & 15; 128-byte rows pair rows (r, r + 1) in one
+// 256-byte line and use f(r) = (r >> 1) & 7.
+template <int CPR>
+__device__ __forceinline__ int swz(int r, int c) {
+  return CPR == 16 ? (c ^ (r & 15)) : (c ^ ((r >> 1) & 7));
+}
+
+// Issue this wave's share of a key tile straight into LDS (gfx950
+// global_load_lds_dwordx4: lane l of an instruction fills 16 bytes at
+// lds + 16 l). Rows past the causal range read the last causal row instead:
+// their scores are never stored.
+template <int H, int D, bool FP8>
+__device__ __forceinline__ void load_key_tile(const uint8_t* __restrict__ keys, int pool0, int j0,
+                                              int maxnc, uint8_t* lds, int wid, int lane) {
+  using C = LogitsCfg<H, D, FP8>;
+#pragma unroll
+  for (int i = 0; i < C::LPW; ++i) {
+    const int L = (wid * C::LPW + i) * 64 + lane;     // LDS chunk index
+    const int r = L / C::CPR, pos = L % C::CPR;
+    const int c = swz<C::CPR>(r, pos);
+    const int jr = j0 + r < maxnc ? j0 + r : maxnc - 1;
+    const uint8_t* src = keys + (size_t)(pool0 + jr) * C::ROWB + c * 16;
+    __builtin_amdgcn_global_load_lds(src, lds + (wid * C::LPW + i) * 1024, 16, 0, 0);
+  }
+}
+
+// ReLU as an integer max on the encoding: non-negative floats (and +0) are
+// non-negative integers, negative floats and -0 are negative integers. One
+// VALU op and no NaN canonicalisation, unlike fmaxf.
+__device__ __forceinline__ float relu(float x) {
+  return __int_as_float(max(__float_as_int(x), 0));
+}
+
+__device__ __forceinline__ void wait_vmem_all() {
+  // s_waitcnt vmcnt(0), leaving expcnt / lgkmcnt unconstrained
+  __builtin_amdgcn_s_waitcnt(0x0f70);
+}
+
+// Output slots of one lane per 32-pool unit: the queries whose score for pool
+// column n of the unit this lane stores.
+template <int H>
+struct OutSlots {
+  static constexpr int MT = 2;
+  static constexpr int N = H == 4 ? MT * 4 : (H == 64 ? 1 : MT * (32 / H) / 2);
+  // query (within the wave) of slot k for half-wave g
+  __device__ static int query(int k, int g) {
+    if constexpr (H == 4) return (k >> 2) * 8 + 2 * (k & 3) + g;   // k = mt * 4 + J
+    else if constexpr (H == 64) return 0;
+    else return 2 * k + g;
+  }
+};
+
+template <int H, int D, bool FP8>
+__global__ __launch_bounds__(64 * kLogitsWaves) void logits_kernel(LogitsArgs a) {
+  using C = LogitsCfg<H, D, FP8>;
+  using S = OutSlots<H>;
+  constexpr int MT = C::MT, QPB = C::QPB;
+  constexpr int QPW = QPB / kLogitsWaves;
+  static_assert(H >= 4 && H <= 64 && (H & (H - 1)) == 0, "H in {4, 8, 16, 32, 64}");
+
+  // two separate LDS objects, so that reads of one provably do not alias the
+  // direct-to-LDS loads filling the other
+  __shared__ __attribute__((aligned(1024))) uint8_t tile0[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t tile1[C::TILE_BYTES];
+  __shared__ int q_doc[QPB], q_nc[QPB];
+  __shared__ int seg_lo, seg_hi;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wid = tid >> 6;
+  const int g = lane >> 5, n = lane & 31;
+  const int t0 = a.q_begin + blockIdx.x * QPB;
+  const uint8_t* keys = reinterpret_cast<const uint8_t*>(a.keys);
+
+  if (tid < QPB) {
+    const int t = t0 + tid;
+    if (t < a.q_end) {
+      const QueryInfo qi = query_info(a.cu, a.cu_pools, a.B, a.T, a.kpool, a.max_pools, t);
+      q_doc[tid] = qi.doc;
+      q_nc[tid] = qi.n_c;
+    } else {
+      q_doc[tid] = -1;
+      q_nc[tid] = 0;
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int lo = 0x7fffffff, hi = -1;
+    for (int j = 0; j < QPB; ++j)
+      if (q_doc[j] >= 0) { lo = min(lo, q_doc[j]); hi = max(hi, q_doc[j]); }
+    seg_lo = lo; seg_hi = hi;
+  }
+
+  // ---- A operand: this wave's (query, head) rows, held for the whole launch.
+  // Row m of tile mt is flat row mt * 32 + m of the wave: query flat / H,
+  // head flat % H. Lane (n, g) holds row n, K slice [g D/2, (g + 1) D/2).
+  using Frag = typename std::conditional<FP8, typename std::conditional<kFp8K == 64, i32x8_t, long>::type,
+                                         bf16x8_t>::type;
+  Frag afrag[MT][C::NSTEP];
+  float wq[MT][16];          // w' of the 16 accumulator rows this lane holds
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int flat = mt * 32 + n;
+    const int qb = wid * QPW + flat / H;
+    const int h = flat % H;
+    const int t = t0 + qb;
+    const bool ok = t < a.q_end;
+    const uint8_t* src = reinterpret_cast<const uint8_t*>(a.q) +
+                         ((size_t)(ok ? t : 0) * H + h) * C::ROWB + g * (C::ROWB / 2);
+#pragma unroll
+    for (int s = 0; s < C::NSTEP; ++s) {
+      if constexpr (FP8 && kFp8K == 64) {
+        const uint4 lo4 = ok ? *reinterpret_cast<const uint4*>(src + s * 32) : make_uint4(0, 0, 0, 0);
+        const uint4 hi4 = ok ? *reinterpret_cast<const uint4*>(src + s * 32 + 16) : make_uint4(0, 0, 0, 0);
+        i32x8_t f = {(int)lo4.x, (int)lo4.y, (int)lo4.z, (int)lo4.w,
+                     (int)hi4.x, (int)hi4.y, (int)hi4.z, (int)hi4.w};
+        afrag[mt][s] = f;
+      } else if constexpr (FP8) {
+        afrag[mt][s] = ok ? *reinterpret_cast<const long*>(src + s * 8) : 0l;
+      } else {
+        const uint4 v = ok ? *reinterpret_cast<const uint4*>(src + s * 16) : make_uint4(0, 0, 0, 0);
+        afrag[mt][s] = __builtin_bit_cast(bf16x8_t, v);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int row = (j >> 2) * 8 + g * 4 + (j & 3);   // accumulator row of slot j
+      const int fr = mt * 32 + row;
+      const int qb2 = wid * QPW + fr / H;
+      const int h2 = fr % H;
+      const int t2 = t0 + qb2;
+      float wv = 0.f;
+      if (t2 < a.q_end) {
+        wv = a.w[(size_t)t2 * H + h2] * a.scale;
+        if constexpr (FP8) wv *= a.q_scale[(size_t)t2 * H + h2];
+      }
+      wq[mt][j] = wv;
+    }
+  }
+
+  // ---- scores leave through a buffer resource over this workgroup's rows;
+  // a masked lane stores at offset num_records, which the hardware drops
+  const int wg_rows = min(QPB, a.q_end - t0);
+  const uint32_t nrec = (uint32_t)((size_t)wg_rows * a.ld * 4);
+  const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
+      a.out + (size_t)(t0 - a.q_begin) * a.ld, 0, (int)nrec, 0x00020000);
+  __syncthreads();
+  const int b_lo = seg_lo, b_hi = seg_hi;
+
+  for (int b = b_lo; b <= b_hi; ++b) {
+    // widest causal range among this workgroup's queries of document b
+    int maxnc = 0;
+    for (int j = 0; j < QPB; ++j)
+      if (q_doc[j] == b) maxnc = max(maxnc, q_nc[j]);
+    if (maxnc == 0) continue;
+    if (a.skip_select_all && maxnc <= a.k_sel) continue;
+    const int pool0 = clampi(a.cu_pools[b], 0, a.T / a.kpool);
+    const int ntiles = (maxnc + kPoolTile - 1) / kPoolTile;
+
+    // per output slot: causal limit (0 for other documents) and row offset
+    uint32_t lim[S::N], roff[S::N];
+#pragma unroll
+    for (int k = 0; k < S::N; ++k) {
+      const int qb = wid * QPW + S::query(k, g);
+      const bool mine = q_doc[qb] == b && (H != 64 || g == 0);
+      lim[k] = mine ? (uint32_t)q_nc[qb] : 0u;
+      roff[k] = (uint32_t)((size_t)qb * a.ld * 4);
+    }
+
+    // epilogue of one 32-pool unit whose first column is cbase (negative:
+    // nothing to store): w' * ReLU, sum over heads, causal mask, store
+    auto epilogue = [&](const f32x16_t (&acc)[MT], int cbase) {
+      const int col = cbase + n;
+      float kscale = 1.f;
+      if constexpr (FP8) kscale = a.k_scale[pool0 + clampi(col, 0, maxnc - 1)];
+      float part[MT][4];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int J = 0; J < 4; ++J) {
+          float s4 = wq[mt][J * 4] * relu(acc[mt][J * 4]);
+#pragma unroll
+          for (int jj = 1; jj < 4; ++jj) s4 += wq[mt][J * 4 + jj] * relu(acc[mt][J * 4 + jj]);
+          part[mt][J] = s4;
+        }
+      float outv[S::N];
+      if constexpr (H == 4) {
+        // rows 8J + 4g .. + 3 are query 2J + g of the tile: already complete
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int J = 0; J < 4; ++J) outv[mt * 4 + J] = part[mt][J];
+      } else if constexpr (H == 64) {
+        // both row tiles hold the same query; add the two half-waves
+        const float s = ((part[0][0] + part[0][1]) + (part[0][2] + part[0][3])) +
+                        ((part[1][0] + part[1][1]) + (part[1][2] + part[1][3]));
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s),
+                                                         false, false);
+        outv[0] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+      } else {
+        constexpr int QPT = 32 / H;                      // queries per 32-row tile
+        constexpr int JPQ = 4 / QPT;                     // row groups per query
+        float tot[MT * QPT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int qq = 0; qq < QPT; ++qq) {
+            float s = part[mt][qq * JPQ];
+#pragma unroll
+            for (int J = qq * JPQ + 1; J < (qq + 1) * JPQ; ++J) s += part[mt][J];
+            tot[mt * QPT + qq] = s;
+          }
+        // pair queries 2i and 2i+1: after the swap the low half-wave holds
+        // the full sum of query 2i and the high half-wave that of 2i+1
+#pragma unroll
+        for (int i = 0; i < S::N; ++i) {
+          const auto sw = __builtin_amdgcn_permlane32_swap(
+              __float_as_uint(tot[2 * i]), __float_as_uint(tot[2 * i + 1]), false, false);
+          outv[i] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < S::N; ++k) {
+        const bool ok = (uint32_t)col < lim[k];
+        const uint32_t off = ok ? roff[k] + (uint32_t)col * 4u : nrec;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(outv[k] * kscale), orsrc, (int)off, 0, 0);
+      }
+    };
+
+    // MFMAs of one 32-pool unit (key rows 32 np .. 32 np + 31 of tile tb)
+    auto mma = [&](f32x16_t (&acc)[MT], const uint8_t* __restrict__ tb, int np) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) acc[mt][j] = 0.f;
+      const int r = np * 32 + n;                        // key row of this lane
+      const uint8_t* brow = tb + r * C::ROWB;
+#pragma unroll
+      for (int s = 0; s < C::NSTEP; ++s) {
+        if constexpr (FP8 && kFp8K == 16) {
+          const int c = g * (C::CPR / 2) + (s >> 1);
+          const long bf = *reinterpret_cast<const long*>(brow + swz<C::CPR>(r, c) * 16 + (s & 1) * 8);
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+            acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(afrag[mt][s], bf, acc[mt], 0, 0, 0);
+        } else if constexpr (FP8) {
+          const int c0 = g * (C::CPR / 2) + 2 * s;
+          const uint4 lo4 = *reinterpret_cast<const uint4*>(brow + swz<C::CPR>(r, c0) * 16);
+          const uint4 hi4 = *reinterpret_cast<const uint4*>(brow + swz<C::CPR>(r, c0 + 1) * 16);
+          i32x8_t bf = {(int)lo4.x, (int)lo4.y, (int)lo4.z, (int)lo4.w,
+                        (int)hi4.x, (int)hi4.y, (int)hi4.z, (int)hi4.w};
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+            acc[mt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(afrag[mt][s], bf, acc[mt], 0,
+                                                                      0, 0, 0, 0, 0);
+        } else {
+          const int c = g * (C::CPR / 2) + s;
+          const uint4 v = *reinterpret_cast<const uint4*>(brow + swz<C::CPR>(r, c) * 16);
+          const bf16x8_t bf = __builtin_bit_cast(bf16x8_t, v);
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+            acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afrag[mt][s], bf, acc[mt], 0, 0, 0);
+        }
+      }
+    };
+
+    // interleave the MFMAs of one unit with the epilogue VALU work of the
+    // previous unit so the matrix core and the vector ALU work together
+    auto interleave = [&]() {
+#pragma unroll
+      for (int i = 0; i < C::NSTEP * MT; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);   // VALU
+      }
+    };
+
+    f32x16_t accA[MT], accB[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) accB[mt][j] = 0.f;
+    int prev = -1;       // first column of the unit held in accB (-1: none)
+
+    __syncthreads();     // both LDS buffers are free
+    load_key_tile<H, D, FP8>(keys, pool0, 0, maxnc, tile0, wid, lane);
+
+    // Tiles alternate between tile0 and tile1; the body is instantiated once
+    // per buffer so each LDS read names a fixed buffer.
+    auto step = [&](const int jt, const uint8_t* __restrict__ tb, uint8_t* __restrict__ nb) {
+      wait_vmem_all();
+      __syncthreads();   // tile jt is in LDS; tile jt - 1 is no longer read
+      const int j0 = jt * kPoolTile;
+      if (jt + 1 < ntiles) load_key_tile<H, D, FP8>(keys, pool0, j0 + kPoolTile, maxnc, nb, wid, lane);
+      mma(accA, tb, 0);
+      epilogue(accB, prev);
+      interleave();
+      mma(accB, tb, 1);
+      epilogue(accA, j0);
+      interleave();
+      prev = j0 + 32;
+    };
+    for (int jt = 0; jt < ntiles; jt += 2) {
+      step(jt, tile0, tile1);
+      if (jt + 1 < ntiles) step(jt + 1, tile1, tile0);
+    }
+    epilogue(accB, prev);
+  }
+}
+
+__global__ void fill_kernel(float* __restrict__ out, size_t count, float v) {
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (; i < count; i += stride) out[i] = v;
+}
+
+template <int H, int D, bool FP8>
+static void launch_hdf(const LogitsArgs& a, hipStream_t st) {
+  constexpr int QPB = LogitsCfg<H, D, FP8>::QPB;
+  const int rows = a.q_end - a.q_begin;
+  logits_kernel<H, D, FP8><<<(rows + QPB - 1) / QPB, 64 * kLogitsWaves, 0, st>>>(a);
+}
+
+template <int D, bool FP8>
+static void launch_df(const LogitsArgs& a, hipStream_t st) {
+  switch (a.H) {
+    case 4: launch_hdf<4, D, FP8>(a, st); break;
+    case 8: launch_hdf<8, D, FP8>(a, st); break;
+    case 16: launch_hdf<16, D, FP8>(a, st); break;
+    case 32: launch_hdf<32, D, FP8>(a, st); break;
+    default: launch_hdf<64, D, FP8>(a, st); break;
+  }
+}
+
+void launch_logits(const LogitsArgs& a, hipStream_t st) {
+  const int rows = a.q_end - a.q_begin;
+  if (rows <= 0) return;
+  if (a.fill_masked) {
+    const size_t count = (size_t)rows * a.ld;
+    const int blocks = (int)std::min<size_t>((count + 255) / 256, 8192);
+    fill_kernel<<<blocks, 256, 0, st>>>(a.out, count, -INFINITY);
+  }
+  if (a.fp8) launch_df<128, true>(a, st);
+  else if (a.D == 128) launch_df<128, false>(a, st);
+  else launch_df<64, false>(a, st);
+}
+
+}  // namespace kpool

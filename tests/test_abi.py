@@ -1,0 +1,140 @@
+"""The C ABI on the CPU: the library loads, exports every entry point that
+include/kpool.h declares, sizes its workspace, and rejects bad arguments
+before touching the GPU (every call here fails validation, so no HIP call is
+made)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_attention_indexer_kpool_amd as kp
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    with open(os.path.join(ROOT, "include", "kpool.h")) as f:
+        src = f.read()
+    return sorted(set(re.findall(r"^[a-z_0-9 \*]+?\b(kpool_[a-z_0-9]+)\s*\(", src, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert "kpool_indexer_topk" in names and "kpool_compress" in names
+    lib = kp.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(kp.EXPORTS) == names
+    assert kp.kpool_abi_version() == 1
+
+
+def P(**kw):
+    base = dict(num_docs=1, total_tokens=65536, max_seqlen=65536, num_heads=32, head_dim=128,
+                kpool=4, index_topk=2048, always_select_tail=1, use_fp8=0, query_chunk=4096)
+    base.update(kw)
+    return kp.Params(**base)
+
+
+def test_workspace_and_ld():
+    p = P()
+    ld = kp.kpool_logits_ld(p)
+    assert ld == 16384
+    ws = kp.kpool_workspace_bytes(p)
+    assert ws >= 4096 * 16384 * 4 + 4096 * 512 * 4
+    p8 = P(use_fp8=1, total_tokens=32768, max_seqlen=32768)
+    ws8 = kp.kpool_workspace_bytes(p8)
+    assert ws8 >= 4096 * 8192 * 4 + 32768 * 32 * (128 + 4) + 8192 * 132
+    assert kp.kpool_logits_ld(P(max_seqlen=4097, total_tokens=5000)) == 1024
+    assert kp.kpool_logits_ld(P(max_seqlen=4100, total_tokens=5000)) == 1088
+    assert kp.kpool_workspace_bytes(P(total_tokens=0, max_seqlen=0)) == 0
+    # unsupported or invalid parameters size to 0
+    assert kp.kpool_workspace_bytes(P(num_heads=12)) == 0
+    assert kp.kpool_workspace_bytes(P(max_seqlen=70000)) == 0
+
+
+def raw(name, *args):
+    assert _no_gpu_visible()
+    L = kp.lib()
+    st = getattr(L, name)(*args)
+    assert st not in (kp.KPOOL_OK, kp.KPOOL_E_LAUNCH), f"{name} passed validation: {kp.kpool_last_error()}"
+    return st
+
+
+def pref(p):
+    return ctypes.byref(p.c())
+
+
+FAKE = 1 << 20          # a 16-byte aligned non-null value never dereferenced: validation fails first
+
+
+def _no_gpu_visible():
+    import torch
+    return torch.cuda.device_count() == 0
+
+
+# Raw calls with fake pointers must never reach a launch; they only run where
+# no GPU is visible, so a wrong expectation can never touch a device.
+raw_calls = pytest.mark.skipif(not _no_gpu_visible(), reason="fake-pointer calls run only without a GPU")
+
+
+@raw_calls
+@pytest.mark.parametrize("p,status,msg", [
+    (P(num_heads=12), kp.KPOOL_E_UNSUPPORTED, "num_heads"),
+    (P(head_dim=96), kp.KPOOL_E_UNSUPPORTED, "head_dim"),
+    (P(kpool=0), kp.KPOOL_E_UNSUPPORTED, "kpool"),
+    (P(index_topk=2), kp.KPOOL_E_INVALID, "index_topk"),
+    (P(use_fp8=1, head_dim=64), kp.KPOOL_E_UNSUPPORTED, "FP8"),
+    (P(max_seqlen=262148, total_tokens=262148), kp.KPOOL_E_UNSUPPORTED, "pools"),
+    (P(max_seqlen=10, total_tokens=5), kp.KPOOL_E_INVALID, "max_seqlen"),
+    (P(num_docs=0), kp.KPOOL_E_INVALID, "num_docs"),
+    (P(query_chunk=-1), kp.KPOOL_E_INVALID, "query_chunk"),
+    (P(always_select_tail=2), kp.KPOOL_E_INVALID, "always_select_tail"),
+])
+def test_indexer_rejects_bad_params(p, status, msg):
+    st = raw("kpool_indexer_topk", pref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, FAKE, None, None)
+    assert st == status
+    assert msg in kp.kpool_last_error()
+
+
+@raw_calls
+def test_pointer_checks():
+    p = P()
+    ws = kp.kpool_workspace_bytes(p)
+    # null q
+    assert raw("kpool_indexer_topk", pref(p), None, FAKE, FAKE, FAKE, FAKE, FAKE, ws, FAKE, None, None) == kp.KPOOL_E_INVALID
+    assert "q is null" in kp.kpool_last_error()
+    # misaligned output
+    assert raw("kpool_indexer_topk", pref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, FAKE + 4, None, None) == kp.KPOOL_E_INVALID
+    assert "out_token_idx" in kp.kpool_last_error()
+    # workspace too small
+    assert raw("kpool_indexer_topk", pref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws - 1, FAKE, None, None) == kp.KPOOL_E_WORKSPACE
+    # misaligned workspace
+    assert raw("kpool_indexer_topk", pref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 16, ws, FAKE, None, None) == kp.KPOOL_E_INVALID
+    # compress: null keys
+    assert raw("kpool_compress", pref(p), None, FAKE, FAKE, FAKE, FAKE, FAKE, None) == kp.KPOOL_E_INVALID
+    # logits: rows out of range
+    assert raw("kpool_logits", pref(p), FAKE, FAKE, FAKE, FAKE, FAKE, 5, 3, FAKE, ws, FAKE, 1, None) == kp.KPOOL_E_INVALID
+    assert raw("kpool_logits", pref(p), FAKE, FAKE, FAKE, FAKE, FAKE, 0, 65537, FAKE, ws, FAKE, 1, None) == kp.KPOOL_E_INVALID
+    assert raw("kpool_logits", pref(p), FAKE, FAKE, FAKE, FAKE, FAKE, 0, 16, FAKE, ws, FAKE, 8, None) == kp.KPOOL_E_INVALID
+    # select / expand: null outputs
+    assert raw("kpool_select", pref(p), FAKE, 0, 10, FAKE, FAKE, None, None) == kp.KPOOL_E_INVALID
+    assert raw("kpool_expand", pref(p), FAKE, FAKE, FAKE, None, None) == kp.KPOOL_E_INVALID
+    # fp8: negative rows, null codes
+    assert raw("kpool_fp8_quantize", FAKE, -1, FAKE, FAKE, None) == kp.KPOOL_E_INVALID
+    assert raw("kpool_fp8_quantize", FAKE, 4, None, FAKE, None) == kp.KPOOL_E_INVALID
+    # null params
+    assert raw("kpool_indexer_topk", None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, FAKE, None, None) == kp.KPOOL_E_INVALID
+
+
+def test_status_strings():
+    assert kp.kpool_status_string(0) == "ok"
+    assert kp.kpool_status_string(3) == "workspace too small"
+    assert kp.kpool_status_string(99) == "unknown status"
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        kp.kpool_fp8_quantize(torch.zeros(4, 128, dtype=torch.bfloat16), 4,
+                              torch.zeros(4, 128, dtype=torch.uint8), torch.zeros(4))

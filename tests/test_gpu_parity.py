@@ -1,0 +1,355 @@
+"""GPU parity: every step of the HIP path, called through the C ABI, against
+the CPU oracle on the same seeded inputs.
+
+Stages are compared in isolation so that a legitimate 1-ulp difference in a
+pooled key cannot move a near-tie downstream:
+  compress   GPU pooled vs oracle pooled            <= 1 BF16 ulp; cu_pools exact
+  fp8 codes  GPU quantiser vs oracle on the same BF16 rows     bit-exact
+  logits     GPU scores vs oracle scores from the GPU's pooled keys
+             |g - o| <= 2e-3 * max(|o|, 0.01 * max_row |o|); -inf past n_c
+  select     GPU selection of the GPU's logits vs oracle selection of the same
+             logits                                          bit-exact
+  expand     GPU expansion vs oracle expansion of the same pool ids  bit-exact
+  end to end GPU pool sets vs oracle sets from oracle scores: equal except
+             pools within 1e-3 relative of the k-th score; token rows equal the
+             oracle's expansion of the GPU's pool ids exactly.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import pins
+import workloads as wlm
+from gpu_common import DEV, Dev, log, oracle_inputs, scores_close, sets_match_up_to_ties
+
+import sparse_attention_indexer_kpool_amd as kp
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    kp.lib()   # fails loudly when the HIP library is missing
+    log(f"device {torch.cuda.get_device_name(0)}; libkpool ABI {kp.kpool_abi_version()}")
+
+
+_cache = {}
+
+
+def dev_for(idx_or_wl):
+    key = idx_or_wl if isinstance(idx_or_wl, (int, str)) else idx_or_wl.name
+    if key not in _cache:
+        wl = wlm.workload(idx_or_wl) if isinstance(idx_or_wl, (int, str)) else idx_or_wl
+        log(f"inputs {wl.name}")
+        d = Dev(wlm.make_inputs(wl))
+        d.compress()
+        _cache[key] = d
+    return _cache[key]
+
+
+SMALL = [
+    wlm.custom("ragged_docs_k4_h32", doc_lengths=[1, 3, 4, 5, 131, 0, 700, 66, 2], H=32, D=128,
+               kpool=4, index_topk=64),
+    wlm.custom("docs_k3_h8_d64", doc_lengths=[97, 300, 41], H=8, D=64, kpool=3, index_topk=30),
+    wlm.custom("docs_k1_h16", doc_lengths=[150, 90], H=16, D=128, kpool=1, index_topk=32),
+    wlm.custom("docs_k2_h64_notail", doc_lengths=[260, 77], H=64, D=128, kpool=2, index_topk=40,
+               tail=False),
+    wlm.custom("docs_k8_h4_d64", doc_lengths=[513, 64], H=4, D=64, kpool=8, index_topk=64),
+]
+
+
+# ---------------------------------------------------------------------------
+# compress
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("wl", [0, 1, 2, 3, 4] + SMALL, ids=lambda w: w if isinstance(w, int) else w.name)
+def test_compress(wl):
+    d = dev_for(wl)
+    log(f"compress {d.inp.wl.name} T={d.inp.T}")
+    pooled, cuP = d.compress()
+    q, k, gate, w, ape, cu = oracle_inputs(d.inp)
+    ref, ref_cuP = oracle.compress(k, gate, ape, cu, d.inp.wl.kpool)
+    assert np.array_equal(cuP, ref_cuP)
+    assert pooled.shape == ref.shape
+    # 1 BF16 ulp, plus the FP32 evaluation bound where the slot terms cancel
+    pins.assert_within_bf16_ulps(pooled, ref, 1,
+                                 pins.pooled_fp32_floor(k, gate, ape, cu, d.inp.wl.kpool))
+    # rows past P are left alone
+    P = int(cuP[-1])
+    rest = d.pooled[P:].view(torch.int16)
+    assert bool((rest == 0x7F7F).all())
+
+
+# ---------------------------------------------------------------------------
+# FP8 input path
+# ---------------------------------------------------------------------------
+
+def test_fp8_quantize_bitexact():
+    g = torch.Generator().manual_seed(11)
+    x = torch.randn(3000, 128, generator=g)
+    x[::7] *= 40.0
+    x[1::7] *= 1e-3
+    x[5] = 0.0
+    x[6, :] = 0.0
+    x[6, 3] = 1e-30
+    x[9] = torch.linspace(-300, 300, 128)
+    xb = x.to(torch.bfloat16)
+    codes = torch.empty(3000, 128, dtype=torch.uint8, device=DEV)
+    scale = torch.empty(3000, dtype=torch.float32, device=DEV)
+    kp.kpool_fp8_quantize(xb.to(DEV), 3000, codes, scale)
+    torch.cuda.synchronize()
+    rc, re, _ = oracle.fp8_quantize_rows(xb.float().numpy())
+    assert np.array_equal(codes.cpu().numpy(), rc)
+    assert np.array_equal(scale.cpu().numpy(), np.ldexp(1.0, re).astype(np.float32))
+
+
+def test_fp8_quantize_pooled_keys_bitexact():
+    d = dev_for(4)
+    P = int(d.cu_pools[-1].item())
+    codes = torch.empty(P, 128, dtype=torch.uint8, device=DEV)
+    scale = torch.empty(P, dtype=torch.float32, device=DEV)
+    kp.kpool_fp8_quantize(d.pooled[:P].contiguous(), P, codes, scale)
+    torch.cuda.synchronize()
+    rc, re, _ = oracle.fp8_quantize_rows(d.pooled[:P].float().cpu().numpy())
+    assert np.array_equal(codes.cpu().numpy(), rc)
+    assert np.array_equal(scale.cpu().numpy(), np.ldexp(1.0, re).astype(np.float32))
+
+
+# ---------------------------------------------------------------------------
+# logits
+# ---------------------------------------------------------------------------
+
+def _check_logits(d, q_begin, q_end, fp8=False):
+    p = d.p
+    if fp8 != bool(p.use_fp8):
+        p = kp.Params(**{**p.__dict__, "use_fp8": int(fp8)})
+    out = d.logits(q_begin, q_end, p).cpu().numpy()
+    q, k, gate, w, ape, cu = oracle_inputs(d.inp)
+    pooled = d.pooled.float().cpu().numpy()
+    kpool = d.inp.wl.kpool
+    cuP = oracle.cu_pools_of(cu, kpool)
+    if fp8:
+        P = int(cuP[-1])
+        _, _, keys_all = oracle.fp8_quantize_rows(pooled[:P])
+    else:
+        keys_all = pooled
+    worst = 0.0
+    for r, t in enumerate(range(q_begin, q_end)):
+        b = oracle.doc_of(t, cu)
+        n_c = oracle.causal_pools(t - int(cu[b]), kpool)
+        keys = keys_all[int(cuP[b]):int(cuP[b]) + n_c]
+        qt = q[t]
+        if fp8:
+            _, _, qt = oracle.fp8_quantize_rows(qt)
+        ref = oracle.row_scores(qt, w[t], keys, 1.0 / np.sqrt(d.inp.wl.D))
+        okk, err = scores_close(out[r, :n_c], ref)
+        worst = max(worst, err)
+        assert okk, f"row {t}: worst error {err} of tolerance"
+        assert np.all(np.isneginf(out[r, n_c:])), f"row {t}: masked columns not -inf"
+    return worst
+
+
+@pytest.mark.parametrize("wl", [0] + SMALL, ids=lambda w: w if isinstance(w, int) else w.name)
+def test_logits_small_all_rows(wl):
+    d = dev_for(wl)
+    T = d.inp.T
+    log(f"logits {d.inp.wl.name} rows 0..{T}")
+    worst = _check_logits(d, 0, T)
+    log(f"  worst error / tolerance = {worst:.3f}")
+
+
+@pytest.mark.parametrize("wl,ranges", [
+    (1, [(0, 37), (2040, 2100), (4000, 4096)]),
+    (2, [(2600, 2700), (5100, 5190), (19600, 19679)]),
+    (3, [(0, 16), (32700, 32790), (65500, 65536)]),
+])
+def test_logits_full_size_sampled(wl, ranges):
+    d = dev_for(wl)
+    for a, b in ranges:
+        log(f"logits {d.inp.wl.name} rows {a}..{b}")
+        _check_logits(d, a, b)
+
+
+def test_logits_fp8_sampled():
+    d = dev_for(4)
+    for a, b in [(0, 16), (16380, 16420), (32740, 32768)]:
+        log(f"logits fp8 rows {a}..{b}")
+        _check_logits(d, a, b, fp8=True)
+
+
+# ---------------------------------------------------------------------------
+# select (exact, on the GPU's own logits) and expand (exact)
+# ---------------------------------------------------------------------------
+
+def _select_exact(d, logits_dev, q_begin, q_end):
+    p = d.p
+    out = torch.full((q_end - q_begin, p.k_sel), -999, dtype=torch.int32, device=DEV)
+    kp.kpool_select(p, logits_dev, q_begin, q_end, d.cu, d.cu_pools, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    lg = logits_dev.cpu().numpy()
+    cu = d.inp.cu_seqlens.numpy().astype(np.int64)
+    cuP = oracle.cu_pools_of(cu, p.kpool)
+    for r, t in enumerate(range(q_begin, q_end)):
+        b = oracle.doc_of(t, cu)
+        n_c = oracle.causal_pools(t - int(cu[b]), p.kpool)
+        ref = oracle.select_pools(lg[r, :n_c], p.k_sel) + int(cuP[b])
+        row = np.full(p.k_sel, -1, np.int64)
+        row[:len(ref)] = ref
+        assert np.array_equal(got[r], row), f"row {t}"
+
+
+@pytest.mark.parametrize("wl", [0, 1] + SMALL[:3], ids=lambda w: w if isinstance(w, int) else w.name)
+def test_select_exact(wl):
+    d = dev_for(wl)
+    T = d.inp.T
+    log(f"select {d.inp.wl.name}")
+    lg = d.logits(0, T)
+    _select_exact(d, lg, 0, T)
+
+
+def test_select_exact_adversarial():
+    """Ties, NaN, +-inf, signed zeros, heavy tails, constant rows, tiny
+    gaps, on one long document (4096 tokens, 1024 pools, K_sel 32)."""
+    wl = wlm.custom("adv", T=4096, H=4, D=64, kpool=4, index_topk=128)
+    d = Dev(wlm.make_inputs(wl))
+    d.compress()
+    T, ld = 4096, kp.kpool_logits_ld(d.p)
+    g = torch.Generator().manual_seed(5)
+    lg = torch.randn(T, ld, generator=g)
+    lg[0::9] = torch.randint(-3, 4, (len(range(0, T, 9)), ld), generator=g).float()  # heavy ties
+    lg[1::9] = 1.0                                                             # all equal
+    lg[2::9, ::5] = float("nan")
+    lg[3::9, ::3] = float("-inf")
+    lg[4::9, ::7] = float("inf")
+    lg[5::9] = torch.where(torch.rand(len(range(5, T, 9)), ld, generator=g) < 0.5, -0.0, 0.0)
+    lg[6::9] *= 1e30
+    lg[7::9] = 1.0 + torch.randint(0, 3, (len(range(7, T, 9)), ld), generator=g).float() * 2 ** -23
+    lg[8::9] = lg[8::9] ** 3
+    _select_exact(d, lg.to(DEV).contiguous(), 0, T)
+
+
+@pytest.mark.parametrize("wl", [0, 2] + SMALL, ids=lambda w: w if isinstance(w, int) else w.name)
+def test_expand_exact(wl):
+    d = dev_for(wl)
+    p = d.p
+    T = d.inp.T
+    cu = d.inp.cu_seqlens.numpy().astype(np.int64)
+    cuP = oracle.cu_pools_of(cu, p.kpool)
+    # pool ids: a seeded random valid choice per row
+    rng = np.random.default_rng(3)
+    ids = np.full((T, p.k_sel), -1, np.int32)
+    for t in range(T):
+        b = oracle.doc_of(t, cu)
+        n_c = oracle.causal_pools(t - int(cu[b]), p.kpool)
+        n = min(p.k_sel, n_c)
+        ids[t, :n] = np.sort(rng.choice(n_c, n, replace=False)) + cuP[b]
+    out = torch.full((T, p.width), 777, dtype=torch.int32, device=DEV)
+    kp.kpool_expand(p, torch.from_numpy(ids).to(DEV), d.cu, d.cu_pools, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    for t in range(T):
+        ref = oracle.expand_row(t, cu, cuP, [x for x in ids[t] if x >= 0], p.kpool,
+                                p.index_topk, bool(p.always_select_tail))
+        assert np.array_equal(got[t], ref), f"row {t}"
+
+
+# ---------------------------------------------------------------------------
+# end to end
+# ---------------------------------------------------------------------------
+
+def _end_to_end(d, rows, fp8=False):
+    tok, pid = d.indexer()
+    q, k, gate, w, ape, cu = oracle_inputs(d.inp)
+    pooled = d.pooled.float().cpu().numpy()
+    p = d.p
+    cuP = oracle.cu_pools_of(cu, p.kpool)
+    P = int(cuP[-1])
+    otok, opid, osc = oracle.indexer_topk(q, w, pooled[:P], cu, p.kpool, p.index_topk,
+                                          bool(p.always_select_tail), rows=rows, fp8=fp8,
+                                          return_scores=True)
+    exact_rows = 0
+    for r, t in enumerate(rows):
+        b = oracle.doc_of(t, cu)
+        okk, why = sets_match_up_to_ties(pid[t], opid[r], osc[r], int(cuP[b]), p.k_sel)
+        assert okk, f"row {t}: {why}"
+        exact_rows += int(np.array_equal(pid[t], opid[r]))
+        gids = [x for x in pid[t] if x >= 0]
+        assert gids == sorted(gids)
+        assert np.array_equal(tok[t], oracle.expand_row(t, cu, cuP, gids, p.kpool, p.index_topk,
+                                                        bool(p.always_select_tail))), f"row {t}"
+    log(f"  {exact_rows}/{len(rows)} rows identical to the oracle's pool set")
+    return tok, pid
+
+
+@pytest.mark.parametrize("wl", [0] + SMALL, ids=lambda w: w if isinstance(w, int) else w.name)
+def test_end_to_end_small(wl):
+    d = dev_for(wl)
+    log(f"end to end {d.inp.wl.name}")
+    _end_to_end(d, list(range(d.inp.T)))
+
+
+@pytest.mark.parametrize("wl,n", [(1, 192), (2, 192), (3, 96), (4, 64)])
+def test_end_to_end_full_size_sampled(wl, n):
+    d = dev_for(wl)
+    rows = wlm.strided_rows(d.inp.T, n)
+    cu = d.inp.cu_seqlens.tolist()
+    rows = sorted(set(rows) | {max(c - 1, 0) for c in cu[1:]} | set(cu[:-1]))
+    rows = [r for r in rows if r < d.inp.T]
+    log(f"end to end {d.inp.wl.name}: {len(rows)} sampled rows, query_chunk {d.p.query_chunk}")
+    _end_to_end(d, rows, fp8=bool(d.inp.wl.fp8))
+
+
+def test_chunking_and_pool_idx_invariance():
+    """Any query_chunk, and asking or not for pool ids, gives identical rows."""
+    d = dev_for(2)
+    base_tok, base_pid = d.indexer()
+    for qc in (1000, 4096, 333):
+        p = kp.Params(**{**d.p.__dict__, "query_chunk": qc})
+        tok, pid = d.indexer(p)
+        assert np.array_equal(tok, base_tok) and np.array_equal(pid, base_pid), qc
+    tok, _ = d.indexer(with_pool_idx=False)
+    assert np.array_equal(tok, base_tok)
+
+
+def test_prefix_visibility_and_structure():
+    """Rows of short prefixes hold the whole prefix; every row has
+    kpool * min(K_sel, n_c) + tail ascending entries inside its document."""
+    d = dev_for(2)
+    tok, pid = d.indexer()
+    p = d.p
+    cu = d.inp.cu_seqlens.numpy().astype(np.int64)
+    for t in range(d.inp.T):
+        b = oracle.doc_of(t, cu)
+        lo = int(cu[b])
+        i = t - lo
+        n_c = (i + 1) // p.kpool
+        row = tok[t]
+        nv = p.kpool * min(p.k_sel, n_c) + (i + 1) % p.kpool
+        assert np.all(row[nv:] == -1) and np.all(row[:nv] >= lo) and np.all(row[:nv] <= t)
+        assert np.all(np.diff(row[:nv]) > 0)
+        if i + 1 <= p.index_topk:
+            assert np.array_equal(row[:nv], np.arange(lo, t + 1))
+
+
+def test_packed_equals_per_document():
+    d = dev_for(2)
+    tok, pid = d.indexer()
+    inp = d.inp
+    cu = inp.cu_seqlens.tolist()
+    cuP = d.cu_pools.cpu().tolist()
+    for b in (0, 2, 7):
+        s, e = cu[b], cu[b + 1]
+        wl = wlm.custom("one_doc", doc_lengths=[e - s], H=inp.wl.H, D=inp.wl.D,
+                        kpool=inp.wl.kpool, index_topk=inp.wl.index_topk)
+        sub = wlm.Inputs(wl=wl, q=inp.q[s:e], k=inp.k[s:e], w=inp.w[s:e].contiguous(),
+                         gate=inp.gate[s:e], ape=inp.ape,
+                         cu_seqlens=torch.tensor([0, e - s], dtype=torch.int32),
+                         doc_lengths=[e - s])
+        ds = Dev(sub)
+        ds.compress()
+        t2, p2 = ds.indexer()
+        assert np.array_equal(np.where(t2 >= 0, t2 + s, -1), tok[s:e]), b
+        assert np.array_equal(np.where(p2 >= 0, p2 + cuP[b], -1), pid[s:e]), b
