@@ -83,16 +83,29 @@ def oracle_inputs(inp: wlm.Inputs):
             inp.w.numpy(), inp.ape.numpy(), inp.cu_seqlens.numpy().astype(np.int64))
 
 
-def scores_close(got, ref):
-    """|g - o| <= 2e-3 * max(|o|, 0.01 * max_j |o[j]|) elementwise, per row."""
+def scores_close(got, ref, sabs=None, head_dim=128):
+    """|g - o| <= 2e-3 * max(|o|, 0.01 * max_j |o[j]|) + 2 * gamma_D * sabs
+    elementwise, per row. sabs[j] = sum_h |w_h| * scale * sum_d |q_hd k_jd| is
+    the magnitude scale of the score's terms; gamma_D = D * 2^-24 is the
+    textbook rounding-error bound of an FP32 dot product of length D, applied
+    to each side. It matters only where the heads cancel."""
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
     if ref.size == 0:
         return True, 0.0
     floor = 0.01 * np.abs(ref).max()
     lim = 2e-3 * np.maximum(np.abs(ref), floor) + 1e-30
+    if sabs is not None:
+        lim = lim + 2.0 * head_dim * 2.0 ** -24 * np.asarray(sabs, np.float64)
     err = np.abs(got - ref) / lim
     return bool(np.all(err <= 1.0)), float(err.max())
+
+
+def term_scale(q_t, w_t, keys, scale):
+    """sum_h |w_h| * scale * sum_d |q_hd| |k_jd| for each key row j."""
+    qa = np.abs(np.asarray(q_t, np.float64))
+    ka = np.abs(np.asarray(keys, np.float64))
+    return (np.abs(np.asarray(w_t, np.float64))[:, None] * scale * (qa @ ka.T)).sum(0)
 
 
 def sets_match_up_to_ties(got_ids, ref_ids, ref_scores, pool0, k_sel, rel=1e-3):
