@@ -3,77 +3,77 @@
 // Megatron-LM PR #7054, section "3. KPool DSA indexer + NoPE": the indexer's
 // top-k runs over pools and keeps index_topk // kpool of them. xtuner PR #2108
 // (selector fix commit) names a radix-select row selector as the production
-// alternative to a full sort; this kernel is an exact histogram selection
-// written for gfx950.
+// alternative to a full sort; this kernel is an exact selection written for
+// gfx950.
 //
-// One workgroup of 256 (or 1024) threads per query row; HBM-bound: each causal
-// score is read once with coalesced 16-byte loads and stays in registers.
+// One workgroup per query row; HBM-bound: each causal score is read once with
+// coalesced 16-byte loads and stays in registers. Selection order: larger
+// score first, equal scores to the lower pool index, NaN ranks as -inf.
 //
-//   1. min / max of the row (invalid tail slots hold NaN, which min / max skip
-//      and which ranks as -inf).
-//   2. One histogram of 1024 bins that are linear in the value,
-//      bin = trunc((x - min) * 1024 / (max - min)) clamped to [0, 1023]. FP32
-//      subtraction, multiplication and truncation are monotone, so bins
-//      follow the order of the values exactly; equal values share a bin and a
-//      larger bin means a larger value. Linear bins spread typical score
-//      distributions thinly, which keeps LDS atomic collisions rare.
-//   3. The bin b* holding the k-th largest value, found by a suffix scan of
-//      the histogram.
-//   4. The few candidates of b* are gathered to LDS and ranked against each
-//      other (larger value first, ties to the lower index), which gives the
-//      exact threshold element (tau, idx_tau).
-//   5. An element is chosen iff x > tau, or x == tau and idx <= idx_tau. The
-//      chosen pool ids are written in ascending order: per-wave ballot counts
-//      of every 1024-element group are scanned once, then each lane writes at
-//      its prefix.
+//   1. The row is loaded (slots past n_c hold NaN).
+//   2. A sample of the row (one value in eight) is histogrammed over 1024
+//      bins linear in the value between the sample's min and max; its upper
+//      tail gives a level L below which, with a wide margin, no chosen value
+//      lies.
+//   3. Every value >= L is appended to a list in LDS (one segment per wave,
+//      a ballot prefix per lane). The list size is exact, so L is verified:
+//      if fewer than K_sel values reach L, or a segment overflows, the row
+//      takes the general path below.
+//   4. On the short list: a value-linear histogram finds the bin b* holding
+//      the K_sel-th value (bins are monotone in the value: FP32 subtraction,
+//      multiplication and truncation all preserve order), the few values of
+//      b* are ranked against each other, and that gives the exact threshold
+//      element (tau, idx_tau). An element is chosen iff it ranks at or above
+//      it.
+//   5. Chosen pools set bits of an LDS bitmap over the row; one prefix sum of
+//      per-thread bit counts turns the bitmap into ascending pool ids.
 //
-// Rows whose values are not all finite, whose values are all equal or whose
-// threshold bin is crowded fall back to a general path: repeated histogram
-// rounds over order-preserving 32-bit keys (NaN -> -inf, -0 -> +0) with bins
-// that are a right shift of key - min, then over the pool index once all
-// remaining keys tie. Rows with n_c <= K_sel select every causal pool and read
-// no logits.
+// General path (non-finite or constant rows, an unlucky sample): repeated
+// histogram rounds over order-preserving 32-bit keys (NaN -> -inf, -0 -> +0),
+// bins a right shift of key - min, then over the pool index once all
+// remaining keys tie; it re-reads the row from memory. Rows with
+// n_c <= K_sel select every causal pool and read no logits.
 
 #include "kpool_device.h"
 #include "kpool_internal.h"
 
 namespace kpool {
 
+constexpr int kBins = 1024;         // value-linear bins
+constexpr int kLogKeyBins = 10;     // key-space bins of the general path
+constexpr int kKeyBins = 1 << kLogKeyBins;
+
 // Makes the compiler forget what it knows about the values, so per-element
-// results of one phase (bins, ballots) are recomputed in the next instead of
-// being held in registers across a barrier.
+// results of one phase are recomputed in the next instead of being held in
+// registers across a barrier.
 template <int E>
 __device__ __forceinline__ void forget(float (&v)[E]) {
 #pragma unroll
   for (int e = 0; e < E; ++e) asm volatile("" : "+v"(v[e]));
 }
 
-constexpr int kFastBins = 1024;     // value-linear bins of the first round
-constexpr int kLogKeyBins = 10;     // key-space bins of the general path
-constexpr int kKeyBins = 1 << kLogKeyBins;
-
-template <int NT>
+template <int NT, int G>
 struct SelectShared {
   static constexpr int NW = NT / 64;
-  uint32_t hist[kFastBins + 1];       // + one bin for non-candidates
+  static constexpr int WORDS = NT * G / 8;       // bitmap words: 4 G NT bits
+  uint32_t hist[kBins + 1];
   float red_f[2][NW];
   uint32_t red_u[2][NW];
   int wave_tot[NW];
-  int res[3];                         // b*, count above b*, count in b*
-  float cand_val[NT];
+  int res[3];                                    // b*, count above b*, count in b*
   uint32_t cand_key[NT];
   int cand_idx[NT];
   int cand_cnt;
-  float th_val;
+  int seg_cnt[NW];
   uint32_t th_key;
   int th_idx;
-  int grp[64 * NW];
+  uint32_t bitmap[WORDS];
 };
 
-// Suffix scan of the histogram: the bin b* with (count above b*) < k <=
+// Suffix scan of sh.hist[0 .. NBINS): the bin b* with (count above b*) < k <=
 // (count above b*) + hist[b*]. Results land in sh.res; ends with a barrier.
-template <int NT, int NBINS>
-__device__ __forceinline__ void find_bin(SelectShared<NT>& sh, int k) {
+template <int NT, int G, int NBINS>
+__device__ __forceinline__ void find_bin(SelectShared<NT, G>& sh, int k) {
   constexpr int NW = NT / 64;
   constexpr int BPT = (NBINS + NT - 1) / NT;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -101,15 +101,23 @@ __device__ __forceinline__ void find_bin(SelectShared<NT>& sh, int k) {
   __syncthreads();
 }
 
+// Value-linear bin over [lo, lo + kBins / inv]; NaN lands in bin 0 (fmaxf
+// returns the non-NaN operand).
+__device__ __forceinline__ int vbin(float x, float lo, float inv) {
+  return (int)fminf(fmaxf((x - lo) * inv, 0.f), (float)(kBins - 1));
+}
+
 template <int NT, int G>
 __global__ __launch_bounds__(NT) void select_kernel(
     const float* __restrict__ logits, int64_t ld, int q_begin, int q_end,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ cu_pools, int B, int T,
-    int kpool, int k_sel, int max_pools, int32_t* __restrict__ out_ids) {
+    int kpool, int k_sel, int max_pools, int list_cap, int32_t* __restrict__ out_ids) {
   constexpr int NW = NT / 64;
-  constexpr int E = 4 * G;                    // values per thread
-  static_assert(E <= 64 && G * NW <= 64 * NW, "sizes");
-  __shared__ SelectShared<NT> sh;
+  constexpr int E = 4 * G;                       // values per thread
+  using Sh = SelectShared<NT, G>;
+  __shared__ Sh sh;
+  extern __shared__ __attribute__((aligned(16))) uint8_t dyn[];
+  uint2* list = reinterpret_cast<uint2*>(dyn);      // list_cap (value bits, index) pairs
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wid = tid >> 6;
@@ -124,113 +132,205 @@ __global__ __launch_bounds__(NT) void select_kernel(
     return;
   }
   const int ng = (n_c + 4 * NT - 1) / (4 * NT);      // groups holding valid values
+  const int nwords = (n_c + 31) >> 5;
   auto idx_of = [&](int g, int c) { return (g * NT + tid) * 4 + c; };
 
-  // ---- 1. load (invalid slots = NaN) and the row's min / max
-  // Groups below ng are loaded by every lane (uniform branch); a lane whose
-  // slots lie past n_c reads an in-row address (clamped to the row's last 16
-  // bytes) and masks the values to NaN without branching.
+  // ---- 1. load the row. All loads are issued before any value is used, so a
+  // wave keeps its loads in flight together. Groups below ng - 1 are full and
+  // load through a uniform base; the last group clamps its addresses into the
+  // row and masks slots past n_c to NaN (which never reaches the level below
+  // and ranks as -inf).
+  const uint8_t* rowb = reinterpret_cast<const uint8_t*>(logits + (size_t)r * ld);
   const float* row = logits + (size_t)r * ld;
+  const int lastg = ng - 1;
+  float4 raw[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    if (g < lastg) {
+      raw[g] = *reinterpret_cast<const float4*>(rowb + g * NT * 16 + tid * 16);
+    } else if (g == lastg) {
+      const int off = min(g * NT * 16 + tid * 16, ((int)ld - 4) * 4);
+      raw[g] = *reinterpret_cast<const float4*>(rowb + off);
+    } else {
+      raw[g] = make_float4(NAN, NAN, NAN, NAN);
+    }
+  }
   float v[E];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    float4 f = make_float4(NAN, NAN, NAN, NAN);
-    if (g < ng) {
+    v[4 * g + 0] = raw[g].x; v[4 * g + 1] = raw[g].y; v[4 * g + 2] = raw[g].z; v[4 * g + 3] = raw[g].w;
+    if (g == lastg) {
       const int base = (g * NT + tid) * 4;
-      const int addr = base < (int)ld - 4 ? base : (int)ld - 4;
-      f = *reinterpret_cast<const float4*>(row + addr);
-      f.x = base + 0 < n_c ? f.x : NAN;
-      f.y = base + 1 < n_c ? f.y : NAN;
-      f.z = base + 2 < n_c ? f.z : NAN;
-      f.w = base + 3 < n_c ? f.w : NAN;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) v[4 * g + c] = base + c < n_c ? v[4 * g + c] : NAN;
     }
-    v[4 * g + 0] = f.x; v[4 * g + 1] = f.y; v[4 * g + 2] = f.z; v[4 * g + 3] = f.w;
   }
   forget(v);
-  float mn = INFINITY, mx = -INFINITY;
-#pragma unroll
-  for (int e = 0; e < E; ++e) { mn = fminf(mn, v[e]); mx = fmaxf(mx, v[e]); }
-  mn = wave_min(mn);
-  mx = wave_max(mx);
-  if (lane == 0) { sh.red_f[0][wid] = mn; sh.red_f[1][wid] = mx; }
-  for (int j = tid; j <= kFastBins; j += NT) sh.hist[j] = 0u;
-  __syncthreads();
-  mn = sh.red_f[0][0]; mx = sh.red_f[1][0];
-#pragma unroll
-  for (int w = 1; w < NW; ++w) { mn = fminf(mn, sh.red_f[0][w]); mx = fmaxf(mx, sh.red_f[1][w]); }
-  const float range = mx - mn;
-  bool fast = (range > 0.f) && (range <= 3.0e38f);    // finite, not all equal, no overflow
 
-  float tau = 0.f;
-  int idx_tau = 0;
+  // ---- 2. sample: value (g, (g / 2) mod 4) of every even group g, its
+  // min / max, and a value-linear histogram of it
+  float smn = INFINITY, smx = -INFINITY;
+  int ns = 0;
+#pragma unroll
+  for (int g = 0; g < G; g += 2) {
+    if (g < ng) {
+      const float x = v[4 * g + ((g >> 1) & 3)];
+      smn = fminf(smn, x);
+      smx = fmaxf(smx, x);
+      ns += x == x;
+    }
+  }
+  smn = wave_min(smn);
+  smx = wave_max(smx);
+  ns = wave_sum(ns);
+  if (lane == 0) { sh.red_f[0][wid] = smn; sh.red_f[1][wid] = smx; sh.wave_tot[wid] = ns; }
+  for (int j = tid; j <= kBins; j += NT) sh.hist[j] = 0u;
+  for (int j = tid; j < nwords; j += NT) sh.bitmap[j] = 0u;
+  if (tid == 0) { sh.cand_cnt = 0; sh.res[0] = sh.res[1] = sh.res[2] = 0; }
+  __syncthreads();
+  smn = sh.red_f[0][0]; smx = sh.red_f[1][0];
+  int S = sh.wave_tot[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) {
+    smn = fminf(smn, sh.red_f[0][w]);
+    smx = fmaxf(smx, sh.red_f[1][w]);
+    S += sh.wave_tot[w];
+  }
+  __syncthreads();                                   // wave_tot is reused below
+  const float srange = smx - smn;
+  bool fast = S > 0 && (srange > 0.f) && (srange <= 3.0e38f);   // finite, not constant
+
   if (fast) {
-    // ---- 2. value-linear histogram (NaN and invalid slots land in bin 0)
-    const float inv = (float)kFastBins / range;
-    auto bin_of = [&](float x) {
-      // fmaxf returns 0 for a NaN argument, so NaN lands in bin 0
-      return (int)fminf(fmaxf((x - mn) * inv, 0.f), (float)(kFastBins - 1));
-    };
+    const float inv = (float)kBins / srange;
+#pragma unroll
+    for (int g = 0; g < G; g += 2) {
+      if (g < ng) {
+        const float x = v[4 * g + ((g >> 1) & 3)];
+        if (x == x) atomicAdd(&sh.hist[vbin(x, smn, inv)], 1u);
+      }
+    }
+    __syncthreads();
+    // sample rank of the level: a 25 % margin over the expected count of
+    // chosen values in the sample plus four standard deviations
+    const float expect = (float)k_sel * (float)S / (float)n_c;
+    int m = (int)ceilf(1.25f * expect + 4.f * sqrtf(expect) + 4.f);
+    m = m < S ? m : S;
+    find_bin<NT, G, kBins>(sh, m > 0 ? m : 1);
+    const float L = smn + (float)sh.res[0] * (srange / (float)kBins);
+
+    // ---- 3. compact every value >= L into the LDS list. Each wave appends
+    // to its own segment of seg_cap entries: a ballot gives each lane its
+    // prefix, the running count stays scalar, and a (value, index) pair is one
+    // 8-byte LDS write. A wave that would overflow its segment stops writing;
+    // its count still records the overflow.
+    const int seg_cap = list_cap / NW;
+    uint2* seg = list + wid * seg_cap;
+    int running = 0;
+    forget(v);
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       if (g < ng) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) atomicAdd(&sh.hist[bin_of(v[4 * g + c])], 1u);
+        for (int c = 0; c < 4; ++c) {
+          const bool keep = v[4 * g + c] >= L;
+          const uint64_t m = __ballot(keep);
+          const int cnt = __popcll(m);
+          if (running + cnt <= seg_cap) {
+            if (keep) seg[running + popc_lt(m)] = make_uint2(__float_as_uint(v[4 * g + c]), (uint32_t)idx_of(g, c));
+          }
+          running += cnt;
+        }
       }
     }
+    if (lane == 0) sh.seg_cnt[wid] = running;
+    for (int j = tid; j <= kBins; j += NT) sh.hist[j] = 0u;
     __syncthreads();
-    forget(v);
-    if (tid == 0) sh.hist[0] -= (uint32_t)(ng * 4 * NT - n_c);   // drop the invalid slots
-    __syncthreads();
-    // ---- 3. threshold bin
-    find_bin<NT, kFastBins>(sh, k_sel);
-    const int bstar = sh.res[0];
-    const int k_in = k_sel - sh.res[1];              // still to take from b*
-    const int c_in = sh.res[2];
-    if (c_in > NT) {
-      fast = false;                                  // crowded bin: general path
+    // segment offsets of the packed list [0, total)
+    int seg_off[NW + 1];
+    bool overflow = false;
+    seg_off[0] = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const int c = sh.seg_cnt[w];
+      overflow |= c > seg_cap;
+      seg_off[w + 1] = seg_off[w] + c;
+    }
+    const int total = seg_off[NW];
+    // entry k of the packed list
+    auto entry = [&](int k) -> uint2 {
+      int w = 0;
+#pragma unroll
+      for (int u = 1; u < NW; ++u) w += k >= seg_off[u];
+      return list[w * seg_cap + (k - seg_off[w])];
+    };
+    if (overflow || total < k_sel) {
+      fast = false;                                    // the level missed: general path
     } else {
-      // ---- 4. gather b* and rank its candidates
-      if (tid == 0) sh.cand_cnt = 0;
+      // ---- 4. exact threshold on the list
+      float lmn = INFINITY, lmx = -INFINITY;
+      for (int j = tid; j < total; j += NT) {
+        const float x = __uint_as_float(entry(j).x);
+        lmn = fminf(lmn, x);
+        lmx = fmaxf(lmx, x);
+      }
+      lmn = wave_min(lmn);
+      lmx = wave_max(lmx);
+      if (lane == 0) { sh.red_f[0][wid] = lmn; sh.red_f[1][wid] = lmx; }
       __syncthreads();
+      lmn = sh.red_f[0][0]; lmx = sh.red_f[1][0];
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        if (g < ng) {
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const float x = v[4 * g + c];
-            const int ix = idx_of(g, c);
-            // invalid slots are NaN and sit in bin 0
-            if (bin_of(x) == bstar && (bstar != 0 || ix < n_c)) {
+      for (int w = 1; w < NW; ++w) { lmn = fminf(lmn, sh.red_f[0][w]); lmx = fmaxf(lmx, sh.red_f[1][w]); }
+      const float lrange = lmx - lmn;
+      if (!(lrange > 0.f) || !(lrange <= 3.0e38f)) {
+        fast = false;                                  // ties or infinities: general path
+      } else {
+        const float linv = (float)kBins / lrange;
+        for (int j = tid; j < total; j += NT)
+          atomicAdd(&sh.hist[vbin(__uint_as_float(entry(j).x), lmn, linv)], 1u);
+        __syncthreads();
+        find_bin<NT, G, kBins>(sh, k_sel);
+        const int bstar = sh.res[0];
+        const int k_in = k_sel - sh.res[1];
+        const int c_in = sh.res[2];
+        if (c_in > NT) {
+          fast = false;                                // crowded bin: general path
+        } else {
+          for (int j = tid; j < total; j += NT) {
+            const uint2 en = entry(j);
+            const float x = __uint_as_float(en.x);
+            if (vbin(x, lmn, linv) == bstar) {
               const int slot = atomicAdd(&sh.cand_cnt, 1);
               sh.cand_key[slot] = f32_order_key(x);
-              sh.cand_idx[slot] = ix;
+              sh.cand_idx[slot] = (int)en.y;
             }
+          }
+          __syncthreads();
+          if (tid < c_in) {
+            const uint32_t mk = sh.cand_key[tid];
+            const int mi = sh.cand_idx[tid];
+            int rank = 0;
+            for (int q = 0; q < c_in; ++q) {
+              const uint32_t okey = sh.cand_key[q];
+              rank += (okey > mk) || (okey == mk && sh.cand_idx[q] < mi);
+            }
+            if (rank == k_in - 1) { sh.th_key = mk; sh.th_idx = mi; }
+          }
+          __syncthreads();
+          const uint32_t tk = sh.th_key;
+          const int ti = sh.th_idx;
+          // ---- 5a. chosen list entries set their bitmap bits
+          for (int j = tid; j < total; j += NT) {
+            const uint2 en = entry(j);
+            const uint32_t kx = f32_order_key(__uint_as_float(en.x));
+            const int ix = (int)en.y;
+            if (kx > tk || (kx == tk && ix <= ti)) atomicOr(&sh.bitmap[ix >> 5], 1u << (ix & 31));
           }
         }
       }
-      __syncthreads();
-      if (tid < c_in) {
-        const uint32_t mk = sh.cand_key[tid];
-        const int mi = sh.cand_idx[tid];
-        int rank = 0;
-        for (int m = 0; m < c_in; ++m) {
-          const uint32_t okey = sh.cand_key[m];
-          rank += (okey > mk) || (okey == mk && sh.cand_idx[m] < mi);
-        }
-        if (rank == k_in - 1) { sh.th_key = mk; sh.th_idx = mi; }
-      }
-      __syncthreads();
-      const uint32_t tk = sh.th_key;
-      idx_tau = sh.th_idx;
-      // back from key to value; a NaN threshold ranks as -inf (key of -inf)
-      const uint32_t u = (tk & 0x80000000u) ? (tk & 0x7fffffffu) : ~tk;
-      tau = __uint_as_float(u);
-      if (!(fabsf(tau) <= 3.402823466e38f)) fast = false;   // +-inf threshold: general path
     }
     __syncthreads();
   }
 
-  uint64_t sel = 0;    // bit e: value e is chosen (general path only)
   if (!fast) {
     // ---- general path: histogram rounds over keys, then over the index. It
     // is rare, so it re-reads the row instead of holding keys in registers.
@@ -238,7 +338,7 @@ __global__ __launch_bounds__(NT) void select_kernel(
       const int ix = idx_of(e >> 2, e & 3);
       return ix < n_c ? row[ix] : NAN;
     };
-    uint64_t cand = 0;
+    uint64_t cand = 0, sel = 0;
 #pragma unroll 1
     for (int e = 0; e < E; ++e) cand |= (uint64_t)(idx_of(e >> 2, e & 3) < n_c) << e;
     int k = k_sel, c_cnt = n_c, mode = 0;
@@ -261,9 +361,9 @@ __global__ __launch_bounds__(NT) void select_kernel(
           const uint32_t mk = sh.cand_key[tid];
           const int mi = sh.cand_idx[tid];
           int rank = 0;
-          for (int m = 0; m < c_cnt; ++m) {
-            const uint32_t okey = sh.cand_key[m];
-            rank += (okey > mk) || (okey == mk && sh.cand_idx[m] < mi);
+          for (int q = 0; q < c_cnt; ++q) {
+            const uint32_t okey = sh.cand_key[q];
+            rank += (okey > mk) || (okey == mk && sh.cand_idx[q] < mi);
           }
           if (rank == k - 1) { sh.th_key = mk; sh.th_idx = mi; }
         }
@@ -314,7 +414,7 @@ __global__ __launch_bounds__(NT) void select_kernel(
         }
       }
       __syncthreads();
-      find_bin<NT, kKeyBins>(sh, k);
+      find_bin<NT, G, kKeyBins>(sh, k);
       const uint32_t bstar = (uint32_t)sh.res[0];
       const int n_above = sh.res[1];
       const int n_in = sh.res[2];
@@ -331,64 +431,57 @@ __global__ __launch_bounds__(NT) void select_kernel(
       c_cnt = n_in;
       __syncthreads();
     }
-  }
-
-  // ---- 5. write the chosen pools in ascending order
-  forget(v);
-  auto chosen = [&](int g, int c) -> bool {
-    if (!fast) return (sel >> (4 * g + c)) & 1ull;
-    const float x = v[4 * g + c];
-    return x > tau || (x == tau && idx_of(g, c) <= idx_tau);
-  };
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    if (g < ng) {
-      int tot = 0;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) tot += __popcll(__ballot(chosen(g, c)));
-      if (lane == 0) sh.grp[g * NW + wid] = tot;
-    }
-  }
-  __syncthreads();
-  forget(v);
-  if (wid == 0) {
-    int carry = 0;
-    for (int base = 0; base < ng * NW; base += 64) {
-      const int j = base + lane;
-      const int x = j < ng * NW ? sh.grp[j] : 0;
-      const int incl = wave_prefix_sum(x);
-      if (j < ng * NW) sh.grp[j] = carry + incl - x;
-      carry += __shfl(incl, 63, 64);
-    }
-  }
-  __syncthreads();
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    if (g < ng) {
-      int pos = sh.grp[g * NW + wid];
-      uint64_t m[4];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) m[c] = __ballot(chosen(g, c));
-      if ((m[0] | m[1] | m[2] | m[3]) == 0ull) continue;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) pos += popc_lt(m[c]);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        if ((m[c] >> lane) & 1ull) {
-          if (pos < k_sel) o[pos] = qi.pool0 + idx_of(g, c);
-          ++pos;
-        }
+#pragma unroll 1
+    for (int e = 0; e < E; ++e) {
+      if ((sel >> e) & 1ull) {
+        const int ix = idx_of(e >> 2, e & 3);
+        atomicOr(&sh.bitmap[ix >> 5], 1u << (ix & 31));
       }
     }
+    __syncthreads();
   }
+
+  // ---- 5b. bitmap -> ascending pool ids: thread tid owns words
+  // [tid * wpt, (tid + 1) * wpt); a block prefix sum of bit counts places them
+  const int wpt = (nwords + NT - 1) / NT;
+  int cnt = 0;
+  for (int i = 0; i < wpt; ++i) {
+    const int w = tid * wpt + i;
+    if (w < nwords) cnt += __popc(sh.bitmap[w]);
+  }
+  const int incl = wave_prefix_sum(cnt);
+  if (lane == 63) sh.wave_tot[wid] = incl;
+  __syncthreads();
+  int pos = incl - cnt;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) pos += w < wid ? sh.wave_tot[w] : 0;
+  for (int i = 0; i < wpt; ++i) {
+    const int w = tid * wpt + i;
+    uint32_t m = w < nwords ? sh.bitmap[w] : 0u;
+    while (m) {
+      const int bit = __ffs(m) - 1;
+      if (pos < k_sel) o[pos] = qi.pool0 + w * 32 + bit;
+      ++pos;
+      m &= m - 1;
+    }
+  }
+}
+
+// LDS list capacity: room for the survivors of the sampled level (about
+// 1.25 K_sel plus a few sample standard deviations, scaled by the sampling).
+static int list_capacity(int k_sel) {
+  int cap = 3 * k_sel + 1024;
+  cap = cap < 2048 ? 2048 : cap;
+  return cap > 8192 ? 8192 : cap;
 }
 
 template <int NT, int G>
 static void launch_sel(const float* logits, int64_t ld, int q_begin, int q_end,
                        const int32_t* cu, const int32_t* cu_pools, int B, int T, int kpool,
                        int k_sel, int max_pools, int32_t* out_ids, hipStream_t st) {
-  select_kernel<NT, G><<<q_end - q_begin, NT, 0, st>>>(
-      logits, ld, q_begin, q_end, cu, cu_pools, B, T, kpool, k_sel, max_pools, out_ids);
+  const int cap = list_capacity(k_sel);
+  select_kernel<NT, G><<<q_end - q_begin, NT, (size_t)cap * 8, st>>>(
+      logits, ld, q_begin, q_end, cu, cu_pools, B, T, kpool, k_sel, max_pools, cap, out_ids);
 }
 
 void launch_select(const float* logits, int64_t ld, int q_begin, int q_end,
