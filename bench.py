@@ -15,6 +15,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME|IDX]
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -32,6 +33,27 @@ METRIC = "KPool indexer queries/s at 64K ctx; logits TFLOP/s as % of MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_FP8_TFLOPS = 5000.0
 PEAK_HBM_GBS = 8000.0
+
+
+def logits_traffic(wl_name: str):
+    """HBM bytes per logits launch from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE passes (profiles/logits_kernel_traffic_<workload>.txt), scaled
+    by a copy kernel of known size. None when no such file exists or when the
+    logits kernel's sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"logits_kernel_traffic_{wl_name}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line:
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    csrc = os.path.join(ROOT, "sparse_attention_indexer_kpool_amd", "csrc")
+    src = b"".join(open(os.path.join(csrc, f), "rb").read()
+                   for f in ("logits.hip", "kpool_device.h", "kpool_internal.h"))
+    if hashlib.sha256(src).hexdigest() != kv.get("source_sha256"):
+        return None
+    return int(float(kv["hbm_bytes_per_launch"]))
 
 
 def log(msg):
@@ -158,8 +180,11 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="long_T65536_H32_D128")
-    ap.add_argument("--cpu-rows", type=int, default=512)
+    ap.add_argument("--cpu-rows", type=int, default=12288)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="after the bench, run 3 device copies of this many MiB (a kernel of "
+                         "known traffic that calibrates the HBM byte counters of a profiler)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the indexer here runs "
@@ -221,7 +246,8 @@ def main():
                    "index_topk": wl.index_topk, "always_select_tail": wl.tail,
                    "query_chunk": path.qc, "docs": len(inp.doc_lengths), "fp8": wl.fp8},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
-                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": logits_traffic(wl.name),
                      "kernel": "logits_kernel", "launches_per_step": n_chunks,
                      "algorithmic_flops_per_step": flops},
         "phases_ms": {"compress": round(ms_compress, 4), "logits": round(ms_logits, 4),
@@ -242,6 +268,15 @@ def main():
         out["cpu_baseline"] = None
     if rank == 0:
         print(json.dumps(out), flush=True)
+    if args.copy_mib > 0:
+        n = args.copy_mib << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy probe: 3 x {args.copy_mib} MiB read + {args.copy_mib} MiB written")
 
 
 if __name__ == "__main__":
