@@ -76,8 +76,8 @@ int kpool_abi_version(void);
 
 /* Bytes of device workspace kpool_indexer_topk and kpool_logits need for
  * these parameters (0 when T == 0). The workspace holds the FP32 logits tile
- * (query_chunk x kpool_logits_ld floats), the pool ids of one chunk and, with
- * use_fp8, the E4M3 codes and row scales of q and of the pooled keys. */
+ * (query_chunk x kpool_logits_ld floats) and, with use_fp8, the E4M3 codes
+ * and row scales of q and of the pooled keys. */
 size_t kpool_workspace_bytes(const kpool_params* p);
 
 /* Row stride, in floats, of the logits tiles of kpool_logits / kpool_select:

@@ -41,7 +41,7 @@ struct Derived {
   int B, T, H, D, kpool, topk, k_sel, width, max_pools, qc, tail, fp8;
   int64_t ld;
   float scale;
-  size_t off_logits, off_ids, off_qc, off_qs, off_kc, off_ks, total;
+  size_t off_logits, off_qc, off_qs, off_kc, off_ks, total;
 };
 
 kpool_status derive(const kpool_params* p, Derived* d, bool need_heads) {
@@ -92,8 +92,6 @@ kpool_status derive(const kpool_params* p, Derived* d, bool need_heads) {
   size_t off = 0;
   d->off_logits = off;
   off = round_up(off + (size_t)d->qc * d->ld * 4, 256);
-  d->off_ids = off;
-  off = round_up(off + (size_t)d->qc * std::max(d->k_sel, 1) * 4, 256);
   d->off_qc = d->off_qs = d->off_kc = d->off_ks = off;
   if (d->fp8) {
     const size_t qrows = (size_t)d->T * d->H, krows = (size_t)(d->T / d->kpool);
@@ -226,12 +224,10 @@ kpool_status kpool_indexer_topk(const kpool_params* p, const void* q, const floa
     a.q_begin = c0;
     a.q_end = c1;
     kpool::launch_logits(a, st);
-    int32_t* ids = out_pool_idx ? out_pool_idx + (size_t)c0 * d.k_sel
-                                : reinterpret_cast<int32_t*>(ws + d.off_ids);
     kpool::launch_select(a.out, d.ld, c0, c1, cu_seqlens, cu_pools, d.B, d.T, d.kpool, d.k_sel,
-                         d.max_pools, ids, st);
-    kpool::launch_expand(ids, c0, c1, cu_seqlens, cu_pools, d.B, d.T, d.kpool, d.k_sel, d.width,
-                         d.tail, d.max_pools, out_token_idx + (size_t)c0 * d.width, st);
+                         d.width, d.tail, d.max_pools,
+                         out_pool_idx ? out_pool_idx + (size_t)c0 * d.k_sel : nullptr,
+                         out_token_idx + (size_t)c0 * d.width, st);
   }
   return after_launch();
 }
@@ -288,7 +284,7 @@ kpool_status kpool_select(const kpool_params* p, const float* logits, int32_t q_
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   kpool::launch_select(logits, d.ld, q_begin, q_end, cu_seqlens, cu_pools, d.B, d.T, d.kpool,
-                       d.k_sel, d.max_pools, out_pool_idx, st);
+                       d.k_sel, d.width, d.tail, d.max_pools, out_pool_idx, nullptr, st);
   return after_launch();
 }
 

@@ -84,52 +84,65 @@ __device__ __forceinline__ int popc_lt(uint64_t mask) {
                                         __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
+// Cross-lane helpers on DPP (data-parallel primitives: a VALU operand read
+// from another lane of the same row of 16, or broadcast across rows), which
+// cost a few cycles each instead of an LDS permute.
+
+template <typename T>
+__device__ __forceinline__ int bits_of(T v) { return __builtin_bit_cast(int, v); }
+template <typename T>
+__device__ __forceinline__ T from_bits(int b) { return __builtin_bit_cast(T, b); }
+
+// Reduction over the 64 lanes with an idempotent op (min or max); the result
+// is wave-uniform. Quad swaps and row mirrors reduce each row of 16 lanes,
+// row_bcast:15 / row_bcast:31 fold the rows into lane 63, read back with
+// readlane. Rows a broadcast skips keep their value (op(x, x) = x).
+template <typename T, typename Op>
+__device__ __forceinline__ T wave_reduce_idem(T v, Op op) {
+  static_assert(sizeof(T) == 4, "32-bit values");
+  int x = bits_of(v);
+  x = bits_of(op(from_bits<T>(x), from_bits<T>(__builtin_amdgcn_update_dpp(x, x, 0xb1, 0xf, 0xf, false))));
+  x = bits_of(op(from_bits<T>(x), from_bits<T>(__builtin_amdgcn_update_dpp(x, x, 0x4e, 0xf, 0xf, false))));
+  x = bits_of(op(from_bits<T>(x), from_bits<T>(__builtin_amdgcn_update_dpp(x, x, 0x141, 0xf, 0xf, false))));
+  x = bits_of(op(from_bits<T>(x), from_bits<T>(__builtin_amdgcn_update_dpp(x, x, 0x140, 0xf, 0xf, false))));
+  x = bits_of(op(from_bits<T>(x), from_bits<T>(__builtin_amdgcn_update_dpp(x, x, 0x142, 0xa, 0xf, false))));
+  x = bits_of(op(from_bits<T>(x), from_bits<T>(__builtin_amdgcn_update_dpp(x, x, 0x143, 0xc, 0xf, false))));
+  return from_bits<T>(__builtin_amdgcn_readlane(x, 63));
+}
+
 template <typename T>
 __device__ __forceinline__ T wave_max(T v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    T o = __shfl_xor(v, off, kWave);
-    v = v > o ? v : o;
-  }
-  return v;
+  return wave_reduce_idem(v, [](T a, T b) { return a > b ? a : b; });
 }
 
 template <typename T>
 __device__ __forceinline__ T wave_min(T v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    T o = __shfl_xor(v, off, kWave);
-    v = v < o ? v : o;
-  }
+  return wave_reduce_idem(v, [](T a, T b) { return a < b ? a : b; });
+}
+
+// Inclusive prefix sum over the lanes of a wave: row_shr 1, 2, 4, 8 build
+// the sum within each row of 16 (lanes shifted in from outside the row read
+// 0), row_bcast:15 adds row 0's total to row 1 (and row 2's to row 3),
+// row_bcast:31 adds rows 0-1 to rows 2-3.
+__device__ __forceinline__ int wave_prefix_sum(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);
   return v;
 }
 
+// Sum over the wave (wave-uniform).
 __device__ __forceinline__ int wave_sum(int v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
-  return v;
+  return __builtin_amdgcn_readlane(wave_prefix_sum(v), 63);
 }
 
 // Inclusive suffix sum over the lanes of a wave (lane l gets sum of l..63).
 __device__ __forceinline__ int wave_suffix_sum(int v) {
-  int lane = __lane_id();
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    int o = __shfl_down(v, off, kWave);
-    if (lane + off < kWave) v += o;
-  }
-  return v;
-}
-
-// Inclusive prefix sum over the lanes of a wave.
-__device__ __forceinline__ int wave_prefix_sum(int v) {
-  int lane = __lane_id();
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    int o = __shfl_up(v, off, kWave);
-    if (lane >= off) v += o;
-  }
-  return v;
+  const int incl = wave_prefix_sum(v);
+  return __builtin_amdgcn_readlane(incl, 63) - incl + v;
 }
 
 }  // namespace kpool

@@ -38,15 +38,20 @@ struct LogitsArgs {
 };
 void launch_logits(const LogitsArgs& a, hipStream_t st);
 
+// Pool top-k of rows q_begin .. q_end-1 from a logits tile; writes the pool
+// ids (out_ids, may be null) and/or the expanded token rows with the tail
+// (out_tok, may be null), both indexed by row - q_begin.
 void launch_select(const float* logits, int64_t ld, int q_begin, int q_end,
                    const int32_t* cu, const int32_t* cu_pools, int B, int T, int kpool,
-                   int k_sel, int max_pools, int32_t* out_ids, hipStream_t st);
+                   int k_sel, int width, int tail_on, int max_pools, int32_t* out_ids,
+                   int32_t* out_tok, hipStream_t st);
 
 void launch_expand(const int32_t* pool_ids, int q_begin, int q_end, const int32_t* cu,
                    const int32_t* cu_pools, int B, int T, int kpool, int k_sel, int width,
                    int tail, int max_pools, int32_t* out, hipStream_t st);
 
-// Largest max_pools the selection kernel handles (rows live in registers).
+// Largest max_pools the selection kernel handles (its LDS bitmap has one bit
+// per pool of a row).
 constexpr int kMaxSelectPools = 65536;
 
 }  // namespace kpool

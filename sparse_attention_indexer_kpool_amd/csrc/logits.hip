@@ -42,7 +42,15 @@ constexpr int kFp8K = KPOOL_FP8_MFMA_K;
 static_assert(kFp8K == 64 || kFp8K == 16, "FP8 MFMA K");
 
 constexpr int kLogitsWaves = 8;
-constexpr int kPoolTile = 64;      // pools per LDS stage (two 32-wide MFMA tiles)
+#ifndef KPOOL_POOL_TILE
+#define KPOOL_POOL_TILE 64
+#endif
+#ifndef KPOOL_EPI_CHAINS
+#define KPOOL_EPI_CHAINS 1
+#endif
+constexpr int kPoolTile = KPOOL_POOL_TILE;   // pools per LDS stage (32-wide MFMA units)
+constexpr int kUnits = kPoolTile / 32;
+constexpr int kEpiChains = KPOOL_EPI_CHAINS;
 
 template <int H, int D, bool FP8>
 struct LogitsCfg {
@@ -207,6 +215,19 @@ __global__ __launch_bounds__(64 * kLogitsWaves) void logits_kernel(LogitsArgs a)
   const uint32_t nrec = (uint32_t)((size_t)wg_rows * a.ld * 4);
   const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
       a.out + (size_t)(t0 - a.q_begin) * a.ld, 0, (int)nrec, 0x00020000);
+  // LDS byte offset, within a 32-pool unit, of each 16-byte chunk this lane
+  // reads as the B operand (key row n, half g of D, swizzled). The swizzle
+  // depends only on the row's low bits, so the same offsets serve every unit
+  // and both tiles; they are kept in registers (the asm hides them from
+  // rematerialisation) and the unit's base folds into the read's immediate.
+  constexpr int NCH = C::CPR / 2;
+  uint32_t boff[NCH];
+#pragma unroll
+  for (int u = 0; u < NCH; ++u) {
+    boff[u] = (uint32_t)(n * C::ROWB + swz<C::CPR>(n, g * NCH + u) * 16);
+    asm volatile("" : "+v"(boff[u]));
+  }
+
   __syncthreads();
   const int b_lo = seg_lo, b_hi = seg_hi;
 
@@ -236,41 +257,48 @@ __global__ __launch_bounds__(64 * kLogitsWaves) void logits_kernel(LogitsArgs a)
       const int col = cbase + n;
       float kscale = 1.f;
       if constexpr (FP8) kscale = a.k_scale[pool0 + clampi(col, 0, maxnc - 1)];
-      float part[MT][4];
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int J = 0; J < 4; ++J) {
-          float s4 = wq[mt][J * 4] * relu(acc[mt][J * 4]);
-#pragma unroll
-          for (int jj = 1; jj < 4; ++jj) s4 += wq[mt][J * 4 + jj] * relu(acc[mt][J * 4 + jj]);
-          part[mt][J] = s4;
-        }
+      // the lane's rows of one query form one multiply-add chain (one VALU
+      // op per row after the ReLU; the chain's latency hides behind MFMAs)
       float outv[S::N];
       if constexpr (H == 4) {
-        // rows 8J + 4g .. + 3 are query 2J + g of the tile: already complete
+        // rows 8J + 4g .. + 3 are query 2J + g of the tile: complete per lane
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-          for (int J = 0; J < 4; ++J) outv[mt * 4 + J] = part[mt][J];
+          for (int J = 0; J < 4; ++J) {
+            float s4 = wq[mt][J * 4] * relu(acc[mt][J * 4]);
+#pragma unroll
+            for (int jj = 1; jj < 4; ++jj) s4 += wq[mt][J * 4 + jj] * relu(acc[mt][J * 4 + jj]);
+            outv[mt * 4 + J] = s4;
+          }
       } else if constexpr (H == 64) {
         // both row tiles hold the same query; add the two half-waves
-        const float s = ((part[0][0] + part[0][1]) + (part[0][2] + part[0][3])) +
-                        ((part[1][0] + part[1][1]) + (part[1][2] + part[1][3]));
+        float s = wq[0][0] * relu(acc[0][0]);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int j = (mt == 0 ? 1 : 0); j < 16; ++j) s += wq[mt][j] * relu(acc[mt][j]);
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s),
                                                          false, false);
         outv[0] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
       } else {
         constexpr int QPT = 32 / H;                      // queries per 32-row tile
-        constexpr int JPQ = 4 / QPT;                     // row groups per query
+        constexpr int RPQ = 16 / QPT;                    // this lane's rows per query
         float tot[MT * QPT];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
           for (int qq = 0; qq < QPT; ++qq) {
-            float s = part[mt][qq * JPQ];
+            constexpr int NC = kEpiChains < RPQ ? kEpiChains : RPQ;
+            float cs[NC];
 #pragma unroll
-            for (int J = qq * JPQ + 1; J < (qq + 1) * JPQ; ++J) s += part[mt][J];
+            for (int c = 0; c < NC; ++c) cs[c] = wq[mt][qq * RPQ + c] * relu(acc[mt][qq * RPQ + c]);
+#pragma unroll
+            for (int j = qq * RPQ + NC; j < (qq + 1) * RPQ; ++j)
+              cs[j % NC] += wq[mt][j] * relu(acc[mt][j]);
+            float s = cs[0];
+#pragma unroll
+            for (int c = 1; c < NC; ++c) s += cs[c];
             tot[mt * QPT + qq] = s;
           }
         // pair queries 2i and 2i+1: after the swap the low half-wave holds
@@ -296,20 +324,17 @@ __global__ __launch_bounds__(64 * kLogitsWaves) void logits_kernel(LogitsArgs a)
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int j = 0; j < 16; ++j) acc[mt][j] = 0.f;
-      const int r = np * 32 + n;                        // key row of this lane
-      const uint8_t* brow = tb + r * C::ROWB;
+      const uint8_t* unit = tb + np * 32 * C::ROWB;     // constant: folds into the offset
 #pragma unroll
       for (int s = 0; s < C::NSTEP; ++s) {
         if constexpr (FP8 && kFp8K == 16) {
-          const int c = g * (C::CPR / 2) + (s >> 1);
-          const long bf = *reinterpret_cast<const long*>(brow + swz<C::CPR>(r, c) * 16 + (s & 1) * 8);
+          const long bf = *reinterpret_cast<const long*>(unit + boff[s >> 1] + (s & 1) * 8);
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt)
             acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(afrag[mt][s], bf, acc[mt], 0, 0, 0);
         } else if constexpr (FP8) {
-          const int c0 = g * (C::CPR / 2) + 2 * s;
-          const uint4 lo4 = *reinterpret_cast<const uint4*>(brow + swz<C::CPR>(r, c0) * 16);
-          const uint4 hi4 = *reinterpret_cast<const uint4*>(brow + swz<C::CPR>(r, c0 + 1) * 16);
+          const uint4 lo4 = *reinterpret_cast<const uint4*>(unit + boff[2 * s]);
+          const uint4 hi4 = *reinterpret_cast<const uint4*>(unit + boff[2 * s + 1]);
           i32x8_t bf = {(int)lo4.x, (int)lo4.y, (int)lo4.z, (int)lo4.w,
                         (int)hi4.x, (int)hi4.y, (int)hi4.z, (int)hi4.w};
 #pragma unroll
@@ -317,8 +342,7 @@ __global__ __launch_bounds__(64 * kLogitsWaves) void logits_kernel(LogitsArgs a)
             acc[mt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(afrag[mt][s], bf, acc[mt], 0,
                                                                       0, 0, 0, 0, 0);
         } else {
-          const int c = g * (C::CPR / 2) + s;
-          const uint4 v = *reinterpret_cast<const uint4*>(brow + swz<C::CPR>(r, c) * 16);
+          const uint4 v = *reinterpret_cast<const uint4*>(unit + boff[s]);
           const bf16x8_t bf = __builtin_bit_cast(bf16x8_t, v);
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt)
@@ -355,13 +379,16 @@ __global__ __launch_bounds__(64 * kLogitsWaves) void logits_kernel(LogitsArgs a)
       __syncthreads();   // tile jt is in LDS; tile jt - 1 is no longer read
       const int j0 = jt * kPoolTile;
       if (jt + 1 < ntiles) load_key_tile<H, D, FP8>(keys, pool0, j0 + kPoolTile, maxnc, nb, wid, lane);
-      mma(accA, tb, 0);
-      epilogue(accB, prev);
-      interleave();
-      mma(accB, tb, 1);
-      epilogue(accA, j0);
-      interleave();
-      prev = j0 + 32;
+#pragma unroll
+      for (int u = 0; u < kUnits; u += 2) {
+        mma(accA, tb, u);
+        epilogue(accB, prev);
+        interleave();
+        mma(accB, tb, u + 1);
+        epilogue(accA, j0 + 32 * u);
+        interleave();
+        prev = j0 + 32 * u + 32;
+      }
     };
     for (int jt = 0; jt < ntiles; jt += 2) {
       step(jt, tile0, tile1);

@@ -1,10 +1,15 @@
-// Step 3 of the KPool indexer: per-query pool top-k.
+// Steps 3 and 4 of the KPool indexer for one chunk of query rows: per-query
+// pool top-k and, when asked, expansion of the chosen pools to token indices
+// with the tail appended.
 //
 // Megatron-LM PR #7054, section "3. KPool DSA indexer + NoPE": the indexer's
-// top-k runs over pools and keeps index_topk // kpool of them. xtuner PR #2108
-// (selector fix commit) names a radix-select row selector as the production
-// alternative to a full sort; this kernel is an exact selection written for
-// gfx950.
+// top-k runs over pools and keeps index_topk // kpool of them; the chosen
+// pools expand back to token indices and, with always_select_tail, each
+// query keeps its incomplete causal pool. SkyRL PR #2179 ("Limitations /
+// follow-ups") gives the order: score pools, expand to tokens, append the
+// tail pool. xtuner PR #2108 (selector fix commit) names a radix-select row
+// selector as the production alternative to a full sort; this kernel is an
+// exact selection written for gfx950.
 //
 // One workgroup per query row; HBM-bound: each causal score is read once with
 // coalesced 16-byte loads and stays in registers. Selection order: larger
@@ -26,7 +31,10 @@
 //      element (tau, idx_tau). An element is chosen iff it ranks at or above
 //      it.
 //   5. Chosen pools set bits of an LDS bitmap over the row; one prefix sum of
-//      per-thread bit counts turns the bitmap into ascending pool ids.
+//      per-thread bit counts turns the bitmap into ascending output slots.
+//      Each chosen pool writes its global id (optional) and, when token rows
+//      are asked for, its kpool token ids (one 16-byte store for kpool = 4);
+//      the tail tokens and the -1 padding follow.
 //
 // General path (non-finite or constant rows, an unlucky sample): repeated
 // histogram rounds over order-preserving 32-bit keys (NaN -> -inf, -0 -> +0),
@@ -107,28 +115,93 @@ __device__ __forceinline__ int vbin(float x, float lo, float inv) {
   return (int)fminf(fmaxf((x - lo) * inv, 0.f), (float)(kBins - 1));
 }
 
-template <int NT, int G>
-__global__ __launch_bounds__(NT) void select_kernel(
-    const float* __restrict__ logits, int64_t ld, int q_begin, int q_end,
-    const int32_t* __restrict__ cu, const int32_t* __restrict__ cu_pools, int B, int T,
-    int kpool, int k_sel, int max_pools, int list_cap, int32_t* __restrict__ out_ids) {
+struct SelectArgs {
+  const float* logits;
+  int64_t ld;
+  int q_begin, q_end;
+  const int32_t* cu;
+  const int32_t* cu_pools;
+  int B, T, kpool, k_sel, width, tail_on, max_pools, list_cap;
+  int32_t* out_ids;     // [rows, K_sel] global pool ids, or null
+  int32_t* out_tok;     // [rows, width] token ids with the tail, or null
+};
+
+template <int NT, int G, bool VEC4>
+__global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
   constexpr int NW = NT / 64;
   constexpr int E = 4 * G;                       // values per thread
   using Sh = SelectShared<NT, G>;
   __shared__ Sh sh;
   extern __shared__ __attribute__((aligned(16))) uint8_t dyn[];
   uint2* list = reinterpret_cast<uint2*>(dyn);      // list_cap (value bits, index) pairs
+  const float* __restrict__ logits = a.logits;
+  const int64_t ld = a.ld;
+  const int k_sel = a.k_sel, kpool = a.kpool, list_cap = a.list_cap;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wid = tid >> 6;
   const int r = blockIdx.x;
-  const int t = q_begin + r;
-  if (t >= q_end) return;
-  const QueryInfo qi = query_info(cu, cu_pools, B, T, kpool, max_pools, t);
+  const int t = a.q_begin + r;
+  if (t >= a.q_end) return;
+  const QueryInfo qi = query_info(a.cu, a.cu_pools, a.B, a.T, kpool, a.max_pools, t);
   const int n_c = qi.n_c;
-  int32_t* o = out_ids + (size_t)r * k_sel;
+  const int n_sel = n_c < k_sel ? n_c : k_sel;
+  const int tail = a.tail_on ? (qi.i + 1) % kpool : 0;
+  const int tail_base = qi.start + n_c * kpool;
+  int32_t* oid = a.out_ids ? a.out_ids + (size_t)r * k_sel : nullptr;
+  int32_t* otok = a.out_tok ? a.out_tok + (size_t)r * a.width : nullptr;
+
+  // token slots from n_sel * kpool on: the tail tokens, then -1
+  auto write_tail = [&]() {
+    if (!otok) return;
+    const int from = n_sel * kpool;
+    if (VEC4) {
+      for (int gi = (from >> 2) + tid; gi < (a.width >> 2); gi += NT) {
+        int e[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int jj = gi * 4 + c - from;
+          e[c] = jj < tail ? tail_base + jj : -1;
+        }
+        *reinterpret_cast<int4*>(otok + gi * 4) = make_int4(e[0], e[1], e[2], e[3]);
+      }
+    } else {
+      for (int j = from + tid; j < a.width; j += NT) {
+        const int jj = j - from;
+        otok[j] = jj < tail ? tail_base + jj : -1;
+      }
+    }
+  };
+  // doc-local pool p is the pos-th chosen pool
+  auto emit = [&](int pos, int p) {
+    if (oid) oid[pos] = qi.pool0 + p;
+    if (otok) {
+      const int base = qi.start + p * kpool;
+      if (VEC4) {
+        *reinterpret_cast<int4*>(otok + pos * 4) = make_int4(base, base + 1, base + 2, base + 3);
+      } else {
+        for (int c = 0; c < kpool; ++c) otok[pos * kpool + c] = base + c;
+      }
+    }
+  };
+
   if (n_c <= k_sel) {
-    for (int j = tid; j < k_sel; j += NT) o[j] = j < n_c ? qi.pool0 + j : -1;
+    // every causal pool: ids pool0 .., tokens start .. start + n_c kpool + tail - 1
+    if (oid)
+      for (int j = tid; j < k_sel; j += NT) oid[j] = j < n_c ? qi.pool0 + j : -1;
+    if (otok) {
+      const int nt = n_c * kpool + tail;
+      if (VEC4) {
+        for (int gi = tid; gi < (a.width >> 2); gi += NT) {
+          int e[4];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) e[c] = gi * 4 + c < nt ? qi.start + gi * 4 + c : -1;
+          *reinterpret_cast<int4*>(otok + gi * 4) = make_int4(e[0], e[1], e[2], e[3]);
+        }
+      } else {
+        for (int j = tid; j < a.width; j += NT) otok[j] = j < nt ? qi.start + j : -1;
+      }
+    }
     return;
   }
   const int ng = (n_c + 4 * NT - 1) / (4 * NT);      // groups holding valid values
@@ -460,11 +533,12 @@ __global__ __launch_bounds__(NT) void select_kernel(
     uint32_t m = w < nwords ? sh.bitmap[w] : 0u;
     while (m) {
       const int bit = __ffs(m) - 1;
-      if (pos < k_sel) o[pos] = qi.pool0 + w * 32 + bit;
+      if (pos < k_sel) emit(pos, w * 32 + bit);
       ++pos;
       m &= m - 1;
     }
   }
+  write_tail();
 }
 
 // LDS list capacity: room for the survivors of the sampled level (about
@@ -476,27 +550,43 @@ static int list_capacity(int k_sel) {
 }
 
 template <int NT, int G>
-static void launch_sel(const float* logits, int64_t ld, int q_begin, int q_end,
-                       const int32_t* cu, const int32_t* cu_pools, int B, int T, int kpool,
-                       int k_sel, int max_pools, int32_t* out_ids, hipStream_t st) {
-  const int cap = list_capacity(k_sel);
-  select_kernel<NT, G><<<q_end - q_begin, NT, (size_t)cap * 8, st>>>(
-      logits, ld, q_begin, q_end, cu, cu_pools, B, T, kpool, k_sel, max_pools, cap, out_ids);
+static void launch_sel(const SelectArgs& a, hipStream_t st) {
+  const size_t lds = (size_t)a.list_cap * 8;
+  if (a.kpool == 4 && (a.width & 3) == 0)
+    select_kernel<NT, G, true><<<a.q_end - a.q_begin, NT, lds, st>>>(a);
+  else
+    select_kernel<NT, G, false><<<a.q_end - a.q_begin, NT, lds, st>>>(a);
 }
 
 void launch_select(const float* logits, int64_t ld, int q_begin, int q_end,
                    const int32_t* cu, const int32_t* cu_pools, int B, int T, int kpool,
-                   int k_sel, int max_pools, int32_t* out_ids, hipStream_t st) {
+                   int k_sel, int width, int tail_on, int max_pools, int32_t* out_ids,
+                   int32_t* out_tok, hipStream_t st) {
   if (q_end <= q_begin) return;
-#define KP_SEL(NT, G) launch_sel<NT, G>(logits, ld, q_begin, q_end, cu, cu_pools, B, T, kpool, k_sel, max_pools, out_ids, st)
-  if (max_pools <= 1024) KP_SEL(256, 1);
-  else if (max_pools <= 2048) KP_SEL(256, 2);
-  else if (max_pools <= 4096) KP_SEL(256, 4);
-  else if (max_pools <= 8192) KP_SEL(256, 8);
-  else if (max_pools <= 16384) KP_SEL(256, 16);
-  else if (max_pools <= 32768) KP_SEL(512, 16);
-  else KP_SEL(1024, 16);
-#undef KP_SEL
+  SelectArgs a;
+  a.logits = logits;
+  a.ld = ld;
+  a.q_begin = q_begin;
+  a.q_end = q_end;
+  a.cu = cu;
+  a.cu_pools = cu_pools;
+  a.B = B;
+  a.T = T;
+  a.kpool = kpool;
+  a.k_sel = k_sel;
+  a.width = width;
+  a.tail_on = tail_on;
+  a.max_pools = max_pools;
+  a.list_cap = list_capacity(k_sel);
+  a.out_ids = out_ids;
+  a.out_tok = out_tok;
+  if (max_pools <= 1024) launch_sel<256, 1>(a, st);
+  else if (max_pools <= 2048) launch_sel<256, 2>(a, st);
+  else if (max_pools <= 4096) launch_sel<256, 4>(a, st);
+  else if (max_pools <= 8192) launch_sel<256, 8>(a, st);
+  else if (max_pools <= 16384) launch_sel<256, 16>(a, st);
+  else if (max_pools <= 32768) launch_sel<512, 16>(a, st);
+  else launch_sel<1024, 16>(a, st);
 }
 
 }  // namespace kpool
