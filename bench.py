@@ -124,13 +124,23 @@ class Path:
             c1 = min(self.inp.T, c0 + self.qc)
             kp.kpool_select(self.p, logits[:c1 - c0], c0, c1, self.cu, self.cu_pools, ids[c0:c1])
 
+    def phase_select_expand(self, logits):
+        kp = self.kp
+        for c0 in range(0, self.inp.T, self.qc):
+            c1 = min(self.inp.T, c0 + self.qc)
+            kp.kpool_select_expand(self.p, logits[:c1 - c0], c0, c1, self.cu, self.cu_pools, None,
+                                   self.tok[c0:c1])
+
     def phase_expand(self, ids):
         self.kp.kpool_expand(self.p, ids, self.cu, self.cu_pools, self.tok)
 
 
-def time_region(fn, reps):
-    """Average ms of fn over reps, HIP events on torch's current stream (the
-    stream every launch of the library goes to)."""
+def time_region(fn, reps, warm=1):
+    """Average ms of fn over reps after `warm` untimed calls, HIP events on
+    torch's current stream (the stream every launch of the library goes
+    to)."""
+    for _ in range(warm):
+        fn()
     s = torch.cuda.Event(enable_timing=True)
     e = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -204,7 +214,7 @@ def main():
         path.step()
     torch.cuda.synchronize()
     log(f"timing {args.steps} steps")
-    ms = time_region(path.step, args.steps)
+    ms = time_region(path.step, args.steps, warm=0)
     log(f"{ms:.3f} ms/step")
 
     # phases, each timed live on the launch stream with the same launches
@@ -214,6 +224,7 @@ def main():
     path.phase_logits(logits)      # also leaves the pooled keys / fp8 buffers in place
     ms_compress = time_region(path.phase_compress, reps)
     ms_logits = time_region(lambda: path.phase_logits(logits), reps)
+    ms_select_expand = time_region(lambda: path.phase_select_expand(logits), reps)
     ms_select = time_region(lambda: path.phase_select(logits, ids), reps)
     ms_expand = time_region(lambda: path.phase_expand(ids), reps)
     n_chunks = (T + path.qc - 1) // path.qc
@@ -224,6 +235,7 @@ def main():
     P = sum(L // wl.kpool for L in inp.doc_lengths)
     by_compress = 4 * T * wl.D + 4 * wl.kpool * wl.D + 2 * P * wl.D
     by_select = 4 * need_nc + 4 * T * wl.k_sel
+    by_select_expand = 4 * need_nc + 4 * T * wl.width
     by_expand = 4 * T * (wl.k_sel + wl.width)
 
     def gbs(b, m):
@@ -251,10 +263,15 @@ def main():
                      "kernel": "logits_kernel", "launches_per_step": n_chunks,
                      "algorithmic_flops_per_step": flops},
         "phases_ms": {"compress": round(ms_compress, 4), "logits": round(ms_logits, 4),
+                      "select_expand": round(ms_select_expand, 4),
                       "select": round(ms_select, 4), "expand": round(ms_expand, 4)},
         "phases_hbm": {
             "compress": {"bytes": by_compress, "GB/s": gbs(by_compress, ms_compress),
                          "frac": round(by_compress / (ms_compress * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+            "select_expand": {"bytes": by_select_expand,
+                              "GB/s": gbs(by_select_expand, ms_select_expand),
+                              "frac": round(by_select_expand / (ms_select_expand * 1e-3) / 1e9
+                                            / PEAK_HBM_GBS, 4)},
             "select": {"bytes": by_select, "GB/s": gbs(by_select, ms_select),
                        "frac": round(by_select / (ms_select * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
             "expand": {"bytes": by_expand, "GB/s": gbs(by_expand, ms_expand),

@@ -154,6 +154,17 @@ kpool_status kpool_select(const kpool_params* p, const float* logits, int32_t q_
                           int32_t q_end, const int32_t* cu_seqlens,
                           const int32_t* cu_pools, int32_t* out_pool_idx, void* stream);
 
+/* Steps 3 and 4 together, as kpool_indexer_topk runs them on each query
+ * chunk: the selection of kpool_select on rows q_begin .. q_end-1 of a
+ * logits tile, written directly as token rows (the expansion and tail of
+ * kpool_expand) to out_token_idx [q_end - q_begin, W] and, when
+ * out_pool_idx is not NULL, as pool ids to out_pool_idx
+ * [q_end - q_begin, K_sel]. out_token_idx must be 16-byte aligned. */
+kpool_status kpool_select_expand(const kpool_params* p, const float* logits, int32_t q_begin,
+                                 int32_t q_end, const int32_t* cu_seqlens,
+                                 const int32_t* cu_pools, int32_t* out_pool_idx,
+                                 int32_t* out_token_idx, void* stream);
+
 /* Step 4 alone, for every query t: expands the pool ids of row t of pool_idx
  * [T, K_sel] (global ids, ascending, -1 padded, min(K_sel, n_c(t)) valid) to
  * kpool consecutive tokens each and appends the tail:

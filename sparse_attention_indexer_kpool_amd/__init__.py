@@ -100,6 +100,8 @@ def lib() -> ctypes.CDLL:
         L.kpool_logits.argtypes = [P, vp, vp, vp, vp, vp, i32, i32, vp, sz, vp, i32, vp]
         L.kpool_select.restype = ctypes.c_int
         L.kpool_select.argtypes = [P, vp, i32, i32, vp, vp, vp, vp]
+        L.kpool_select_expand.restype = ctypes.c_int
+        L.kpool_select_expand.argtypes = [P, vp, i32, i32, vp, vp, vp, vp, vp]
         L.kpool_expand.restype = ctypes.c_int
         L.kpool_expand.argtypes = [P, vp, vp, vp, vp, vp]
         L.kpool_fp8_quantize.restype = ctypes.c_int
@@ -113,7 +115,8 @@ def lib() -> ctypes.CDLL:
 
 
 EXPORTS = ["kpool_abi_version", "kpool_workspace_bytes", "kpool_logits_ld", "kpool_compress",
-           "kpool_indexer_topk", "kpool_logits", "kpool_select", "kpool_expand",
+           "kpool_indexer_topk", "kpool_logits", "kpool_select", "kpool_select_expand",
+           "kpool_expand",
            "kpool_fp8_quantize", "kpool_status_string", "kpool_last_error"]
 
 
@@ -183,6 +186,13 @@ def kpool_select(p: Params, logits, q_begin, q_end, cu_seqlens, cu_pools, out_po
     _check(lib().kpool_select(ctypes.byref(p.c()), _ptr(logits), int(q_begin), int(q_end),
                               _ptr(cu_seqlens), _ptr(cu_pools), _ptr(out_pool_idx),
                               _stream(stream)))
+
+
+def kpool_select_expand(p: Params, logits, q_begin, q_end, cu_seqlens, cu_pools, out_pool_idx,
+                        out_token_idx, stream=None) -> None:
+    _check(lib().kpool_select_expand(ctypes.byref(p.c()), _ptr(logits), int(q_begin), int(q_end),
+                                     _ptr(cu_seqlens), _ptr(cu_pools), _ptr(out_pool_idx),
+                                     _ptr(out_token_idx), _stream(stream)))
 
 
 def kpool_expand(p: Params, pool_idx, cu_seqlens, cu_pools, out_token_idx, stream=None) -> None:

@@ -187,7 +187,6 @@ kpool_status kpool_compress(const kpool_params* p, const void* k, const void* ga
   }
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  kpool::launch_cu_pools(cu_seqlens, d.B, d.kpool, cu_pools, st);
   kpool::launch_compress(reinterpret_cast<const uint16_t*>(k),
                          reinterpret_cast<const uint16_t*>(gate), ape, cu_seqlens, cu_pools, d.B,
                          d.T, d.D, d.kpool, reinterpret_cast<uint16_t*>(pooled), st);
@@ -285,6 +284,27 @@ kpool_status kpool_select(const kpool_params* p, const float* logits, int32_t q_
   (void)hipGetLastError();
   kpool::launch_select(logits, d.ld, q_begin, q_end, cu_seqlens, cu_pools, d.B, d.T, d.kpool,
                        d.k_sel, d.width, d.tail, d.max_pools, out_pool_idx, nullptr, st);
+  return after_launch();
+}
+
+kpool_status kpool_select_expand(const kpool_params* p, const float* logits, int32_t q_begin,
+                                 int32_t q_end, const int32_t* cu_seqlens,
+                                 const int32_t* cu_pools, int32_t* out_pool_idx,
+                                 int32_t* out_token_idx, void* stream) {
+  Derived d;
+  CHECK(derive(p, &d, true));
+  if (q_begin < 0 || q_end < q_begin || q_end > d.T)
+    return fail(KPOOL_E_INVALID, "query rows [%d, %d) outside [0, %d]", q_begin, q_end, d.T);
+  if (q_end == q_begin) return ok();
+  CHECK(check_ptr(logits, 16, "logits"));
+  CHECK(check_ptr(cu_seqlens, 4, "cu_seqlens"));
+  CHECK(check_ptr(cu_pools, 4, "cu_pools"));
+  CHECK(check_ptr(out_token_idx, 16, "out_token_idx"));
+  if (out_pool_idx) CHECK(check_ptr(out_pool_idx, 4, "out_pool_idx"));
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  kpool::launch_select(logits, d.ld, q_begin, q_end, cu_seqlens, cu_pools, d.B, d.T, d.kpool,
+                       d.k_sel, d.width, d.tail, d.max_pools, out_pool_idx, out_token_idx, st);
   return after_launch();
 }
 

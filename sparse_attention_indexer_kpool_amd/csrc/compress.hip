@@ -47,21 +47,71 @@ __global__ __launch_bounds__(1024) void cu_pools_kernel(const int32_t* __restric
   }
 }
 
+// Documents whose pool offsets the compress kernel computes itself (one
+// prefix over the documents per workgroup, in LDS); beyond this a separate
+// cu_pools launch comes first.
+constexpr int kFusedDocs = 1024;
+
 // KP = kpool when it is a compile-time constant, 0 for a runtime kpool.
-template <int D, int KP>
+// FUSED: the workgroup derives cu_pools from cu_seqlens (B <= kFusedDocs)
+// and workgroup 0 writes it; otherwise cu_pools is an input.
+template <int D, int KP, bool FUSED>
 __global__ __launch_bounds__(256) void compress_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ gate,
     const float* __restrict__ ape, const int32_t* __restrict__ cu,
-    const int32_t* __restrict__ cu_pools, int B, int T, int kpool_rt,
+    int32_t* __restrict__ cu_pools, int B, int T, int kpool_rt,
     uint16_t* __restrict__ pooled) {
   constexpr int TPP = D / 8;                  // threads per pool
   constexpr int PPB = 256 / TPP;              // pools per workgroup
   const int kpool = KP > 0 ? KP : kpool_rt;
   const int pool_cap = T / kpool;
-  const int total = clampi(cu_pools[B], 0, pool_cap);
-  const int p = blockIdx.x * PPB + threadIdx.x / TPP;
+  const int tid = threadIdx.x;
+
+  __shared__ int s_cup[FUSED ? kFusedDocs + 1 : 1];
+  __shared__ int s_wsum[4];
+  const int32_t* cup = cu_pools;
+  if constexpr (FUSED) {
+    // cuP[b + 1] = sum over b' <= b of floor(L_b' / kpool): thread tid owns
+    // documents tid * per .. tid * per + per - 1; a block prefix sum of the
+    // per-thread totals places them (negative lengths count as zero pools)
+    const int per = (B + 255) >> 8;           // <= 4
+    int cnt[4], tsum = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int b = tid * per + j;
+      int c = 0;
+      if (j < per && b < B) {
+        const int len = cu[b + 1] - cu[b];
+        c = len > 0 ? len / kpool : 0;
+      }
+      cnt[j] = c;
+      tsum += c;
+    }
+    const int lane = tid & 63, wid = tid >> 6;
+    const int incl = wave_prefix_sum(tsum);
+    if (lane == 63) s_wsum[wid] = incl;
+    __syncthreads();
+    int run = incl - tsum;
+    for (int w = 0; w < wid; ++w) run += s_wsum[w];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int b = tid * per + j;
+      if (j < per && b < B) {
+        run += cnt[j];
+        s_cup[b + 1] = run;
+      }
+    }
+    if (tid == 0) s_cup[0] = 0;
+    __syncthreads();
+    if (blockIdx.x == 0)
+      for (int b = tid; b <= B; b += 256) cu_pools[b] = s_cup[b];
+    cup = s_cup;
+  }
+
+  const int total = clampi(cup[B], 0, pool_cap);
+  const int p = blockIdx.x * PPB + tid / TPP;
   if (p >= total) return;
-  const int d0 = (threadIdx.x % TPP) * 8;
+  const int d0 = (tid % TPP) * 8;
 
   // Document of pool p: the first pool of the wave is looked up by binary
   // search, the rest of the wave walks forward past the few boundaries it
@@ -70,39 +120,61 @@ __global__ __launch_bounds__(256) void compress_kernel(
   int lo = 0, hi = B - 1;
   while (lo < hi) {
     int mid = (lo + hi + 1) >> 1;
-    if (cu_pools[mid] <= p_first) lo = mid; else hi = mid - 1;
+    if (cup[mid] <= p_first) lo = mid; else hi = mid - 1;
   }
   int b = lo;
-  while (b + 1 < B && cu_pools[b + 1] <= p) ++b;
-  const int local = p - cu_pools[b];
+  while (b + 1 < B && cup[b + 1] <= p) ++b;
+  const int local = p - cup[b];
   const int t0 = clampi(cu[b] + local * kpool, 0, T - kpool);
 
-  float m[8];
+  auto lo_hi = [](uint32_t w, int half) { return bf16_bits_to_f32((w >> (16 * half)) & 0xffffu); };
+  float z[8], acc[8], m[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) m[e] = -INFINITY;
-  // pass 1: the per-dimension maximum of the slot logits
+  for (int e = 0; e < 8; ++e) { z[e] = 0.f; acc[e] = 0.f; m[e] = -INFINITY; }
+  if constexpr (KP > 0) {
+    // all slot slices of the pool in registers: one read of gate and k
+    uint4 g4[KP], k4[KP];
 #pragma unroll
-  for (int s = 0; s < (KP > 0 ? KP : 1); ++s) {
-    for (int ss = s; ss < (KP > 0 ? s + 1 : kpool); ++ss) {
+    for (int s = 0; s < KP; ++s) {
+      g4[s] = *reinterpret_cast<const uint4*>(gate + (size_t)(t0 + s) * D + d0);
+      k4[s] = *reinterpret_cast<const uint4*>(k + (size_t)(t0 + s) * D + d0);
+    }
+    float a[KP][8];
+#pragma unroll
+    for (int s = 0; s < KP; ++s) {
+      const float4 a0 = *reinterpret_cast<const float4*>(ape + s * D + d0);
+      const float4 a1 = *reinterpret_cast<const float4*>(ape + s * D + d0 + 4);
+      const uint32_t gw[4] = {g4[s].x, g4[s].y, g4[s].z, g4[s].w};
+      const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        a[s][e] = lo_hi(gw[e >> 1], e & 1) + av[e];        // slot logit, FP32
+        m[e] = fmaxf(m[e], a[s][e]);
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < KP; ++s) {
+      const uint32_t kw[4] = {k4[s].x, k4[s].y, k4[s].z, k4[s].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float ex = expf(a[s][e] - m[e]);
+        z[e] += ex;
+        acc[e] += ex * lo_hi(kw[e >> 1], e & 1);
+      }
+    }
+  } else {
+    // runtime kpool: pass 1 finds the per-dimension maximum, pass 2 the
+    // weights, their sum and the weighted keys
+    for (int ss = 0; ss < kpool; ++ss) {
       const uint4 g4 = *reinterpret_cast<const uint4*>(gate + (size_t)(t0 + ss) * D + d0);
       const float4 a0 = *reinterpret_cast<const float4*>(ape + ss * D + d0);
       const float4 a1 = *reinterpret_cast<const float4*>(ape + ss * D + d0 + 4);
       const uint32_t gw[4] = {g4.x, g4.y, g4.z, g4.w};
       const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float g = bf16_bits_to_f32((gw[e >> 1] >> (16 * (e & 1))) & 0xffffu);
-        m[e] = fmaxf(m[e], g + av[e]);
-      }
+      for (int e = 0; e < 8; ++e) m[e] = fmaxf(m[e], lo_hi(gw[e >> 1], e & 1) + av[e]);
     }
-  }
-  // pass 2: weights, their sum and the weighted keys, all in FP32
-  float z[8], acc[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) { z[e] = 0.f; acc[e] = 0.f; }
-#pragma unroll
-  for (int s = 0; s < (KP > 0 ? KP : 1); ++s) {
-    for (int ss = s; ss < (KP > 0 ? s + 1 : kpool); ++ss) {
+    for (int ss = 0; ss < kpool; ++ss) {
       const uint4 g4 = *reinterpret_cast<const uint4*>(gate + (size_t)(t0 + ss) * D + d0);
       const uint4 k4 = *reinterpret_cast<const uint4*>(k + (size_t)(t0 + ss) * D + d0);
       const float4 a0 = *reinterpret_cast<const float4*>(ape + ss * D + d0);
@@ -112,11 +184,9 @@ __global__ __launch_bounds__(256) void compress_kernel(
       const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        float g = bf16_bits_to_f32((gw[e >> 1] >> (16 * (e & 1))) & 0xffffu);
-        float kv = bf16_bits_to_f32((kw[e >> 1] >> (16 * (e & 1))) & 0xffffu);
-        float ex = expf((g + av[e]) - m[e]);
+        const float ex = expf((lo_hi(gw[e >> 1], e & 1) + av[e]) - m[e]);
         z[e] += ex;
-        acc[e] += ex * kv;
+        acc[e] += ex * lo_hi(kw[e >> 1], e & 1);
       }
     }
   }
@@ -131,32 +201,40 @@ __global__ __launch_bounds__(256) void compress_kernel(
       make_uint4(outw[0], outw[1], outw[2], outw[3]);
 }
 
-template <int D>
-static void launch_compress_d(const uint16_t* k, const uint16_t* gate, const float* ape,
-                              const int32_t* cu, const int32_t* cu_pools, int B, int T,
-                              int kpool, uint16_t* pooled, hipStream_t st) {
+template <int D, bool FUSED>
+static void launch_compress_df(const uint16_t* k, const uint16_t* gate, const float* ape,
+                               const int32_t* cu, int32_t* cu_pools, int B, int T, int kpool,
+                               uint16_t* pooled, hipStream_t st) {
   constexpr int PPB = 256 / (D / 8);
   const int pool_cap = T / kpool;
-  if (pool_cap <= 0) return;
   dim3 grid((pool_cap + PPB - 1) / PPB), block(256);
+#define KP_C(KPV) compress_kernel<D, KPV, FUSED><<<grid, block, 0, st>>>(k, gate, ape, cu, cu_pools, B, T, kpool, pooled)
   switch (kpool) {
-    case 1: compress_kernel<D, 1><<<grid, block, 0, st>>>(k, gate, ape, cu, cu_pools, B, T, kpool, pooled); break;
-    case 2: compress_kernel<D, 2><<<grid, block, 0, st>>>(k, gate, ape, cu, cu_pools, B, T, kpool, pooled); break;
-    case 4: compress_kernel<D, 4><<<grid, block, 0, st>>>(k, gate, ape, cu, cu_pools, B, T, kpool, pooled); break;
-    case 8: compress_kernel<D, 8><<<grid, block, 0, st>>>(k, gate, ape, cu, cu_pools, B, T, kpool, pooled); break;
-    default: compress_kernel<D, 0><<<grid, block, 0, st>>>(k, gate, ape, cu, cu_pools, B, T, kpool, pooled); break;
+    case 1: KP_C(1); break;
+    case 2: KP_C(2); break;
+    case 4: KP_C(4); break;
+    case 8: KP_C(8); break;
+    default: KP_C(0); break;
   }
-}
-
-void launch_cu_pools(const int32_t* cu, int B, int kpool, int32_t* cu_pools, hipStream_t st) {
-  cu_pools_kernel<<<1, 1024, 0, st>>>(cu, B, kpool, cu_pools);
+#undef KP_C
 }
 
 void launch_compress(const uint16_t* k, const uint16_t* gate, const float* ape,
-                     const int32_t* cu, const int32_t* cu_pools, int B, int T, int D,
-                     int kpool, uint16_t* pooled, hipStream_t st) {
-  if (D == 128) launch_compress_d<128>(k, gate, ape, cu, cu_pools, B, T, kpool, pooled, st);
-  else launch_compress_d<64>(k, gate, ape, cu, cu_pools, B, T, kpool, pooled, st);
+                     const int32_t* cu, int32_t* cu_pools, int B, int T, int D, int kpool,
+                     uint16_t* pooled, hipStream_t st) {
+  const bool fused = B <= kFusedDocs;
+  if (T / kpool <= 0) {                       // no pools: only the offsets
+    cu_pools_kernel<<<1, 1024, 0, st>>>(cu, B, kpool, cu_pools);
+    return;
+  }
+  if (!fused) cu_pools_kernel<<<1, 1024, 0, st>>>(cu, B, kpool, cu_pools);
+  if (D == 128) {
+    if (fused) launch_compress_df<128, true>(k, gate, ape, cu, cu_pools, B, T, kpool, pooled, st);
+    else launch_compress_df<128, false>(k, gate, ape, cu, cu_pools, B, T, kpool, pooled, st);
+  } else {
+    if (fused) launch_compress_df<64, true>(k, gate, ape, cu, cu_pools, B, T, kpool, pooled, st);
+    else launch_compress_df<64, false>(k, gate, ape, cu, cu_pools, B, T, kpool, pooled, st);
+  }
 }
 
 }  // namespace kpool

@@ -7,11 +7,10 @@
 
 namespace kpool {
 
-void launch_cu_pools(const int32_t* cu, int B, int kpool, int32_t* cu_pools, hipStream_t st);
-
+// Key compression; also writes cu_pools (the per-document pool offsets).
 void launch_compress(const uint16_t* k, const uint16_t* gate, const float* ape,
-                     const int32_t* cu, const int32_t* cu_pools, int B, int T, int D,
-                     int kpool, uint16_t* pooled, hipStream_t st);
+                     const int32_t* cu, int32_t* cu_pools, int B, int T, int D, int kpool,
+                     uint16_t* pooled, hipStream_t st);
 
 // FP8 input path over `rows` rows of 128 BF16 values. When rows_dev is not
 // null, rows at or beyond *rows_dev are skipped (the count lives on the

@@ -353,12 +353,15 @@ __global__ __launch_bounds__(64 * kLogitsWaves) void logits_kernel(LogitsArgs a)
 
     // interleave the MFMAs of one unit with the epilogue VALU work of the
     // previous unit so the matrix core and the vector ALU work together
+    // (measured on gfx950: for BF16 the LDS read is best placed after its
+    // slot's MFMA, for FP8 before it)
     auto interleave = [&]() {
 #pragma unroll
       for (int i = 0; i < C::NSTEP * MT; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);   // VALU
+        if constexpr (FP8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                      // MFMA
+        if constexpr (!FP8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);                      // VALU
       }
     };
 

@@ -48,6 +48,7 @@
 namespace kpool {
 
 constexpr int kBins = 1024;         // value-linear bins
+constexpr int kListPerLane = 8;     // list entries per lane of a wave segment
 constexpr int kLogKeyBins = 10;     // key-space bins of the general path
 constexpr int kKeyBins = 1 << kLogKeyBins;
 
@@ -296,7 +297,7 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
     // prefix, the running count stays scalar, and a (value, index) pair is one
     // 8-byte LDS write. A wave that would overflow its segment stops writing;
     // its count still records the overflow.
-    const int seg_cap = list_cap / NW;
+    const int seg_cap = list_cap / NW;                 // at most 64 * kListPerLane
     uint2* seg = list + wid * seg_cap;
     int running = 0;
     forget(v);
@@ -318,33 +319,34 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
     if (lane == 0) sh.seg_cnt[wid] = running;
     for (int j = tid; j <= kBins; j += NT) sh.hist[j] = 0u;
     __syncthreads();
-    // segment offsets of the packed list [0, total)
-    int seg_off[NW + 1];
+    int total = 0;
     bool overflow = false;
-    seg_off[0] = 0;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
       const int c = sh.seg_cnt[w];
       overflow |= c > seg_cap;
-      seg_off[w + 1] = seg_off[w] + c;
+      total += c;
     }
-    const int total = seg_off[NW];
-    // entry k of the packed list
-    auto entry = [&](int k) -> uint2 {
-      int w = 0;
-#pragma unroll
-      for (int u = 1; u < NW; ++u) w += k >= seg_off[u];
-      return list[w * seg_cap + (k - seg_off[w])];
-    };
     if (overflow || total < k_sel) {
       fast = false;                                    // the level missed: general path
     } else {
-      // ---- 4. exact threshold on the list
+      // ---- 4. exact threshold on the list. Each wave takes its own segment
+      // into registers once (lane l holds entries l, l + 64, ...); min / max,
+      // histogram, candidate gather and marking all work from there.
+      float ev[kListPerLane];
+      int ei[kListPerLane];
+#pragma unroll
+      for (int i = 0; i < kListPerLane; ++i) {
+        const int j = lane + 64 * i;
+        const uint2 e = seg[j < running ? j : 0];
+        ev[i] = j < running ? __uint_as_float(e.x) : NAN;   // list values are never NaN
+        ei[i] = (int)e.y;
+      }
       float lmn = INFINITY, lmx = -INFINITY;
-      for (int j = tid; j < total; j += NT) {
-        const float x = __uint_as_float(entry(j).x);
-        lmn = fminf(lmn, x);
-        lmx = fmaxf(lmx, x);
+#pragma unroll
+      for (int i = 0; i < kListPerLane; ++i) {
+        lmn = fminf(lmn, ev[i]);
+        lmx = fmaxf(lmx, ev[i]);
       }
       lmn = wave_min(lmn);
       lmx = wave_max(lmx);
@@ -358,8 +360,9 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
         fast = false;                                  // ties or infinities: general path
       } else {
         const float linv = (float)kBins / lrange;
-        for (int j = tid; j < total; j += NT)
-          atomicAdd(&sh.hist[vbin(__uint_as_float(entry(j).x), lmn, linv)], 1u);
+#pragma unroll
+        for (int i = 0; i < kListPerLane; ++i)
+          if (ev[i] == ev[i]) atomicAdd(&sh.hist[vbin(ev[i], lmn, linv)], 1u);
         __syncthreads();
         find_bin<NT, G, kBins>(sh, k_sel);
         const int bstar = sh.res[0];
@@ -368,13 +371,12 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
         if (c_in > NT) {
           fast = false;                                // crowded bin: general path
         } else {
-          for (int j = tid; j < total; j += NT) {
-            const uint2 en = entry(j);
-            const float x = __uint_as_float(en.x);
-            if (vbin(x, lmn, linv) == bstar) {
+#pragma unroll
+          for (int i = 0; i < kListPerLane; ++i) {
+            if (ev[i] == ev[i] && vbin(ev[i], lmn, linv) == bstar) {
               const int slot = atomicAdd(&sh.cand_cnt, 1);
-              sh.cand_key[slot] = f32_order_key(x);
-              sh.cand_idx[slot] = (int)en.y;
+              sh.cand_key[slot] = f32_order_key(ev[i]);
+              sh.cand_idx[slot] = ei[i];
             }
           }
           __syncthreads();
@@ -392,11 +394,12 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
           const uint32_t tk = sh.th_key;
           const int ti = sh.th_idx;
           // ---- 5a. chosen list entries set their bitmap bits
-          for (int j = tid; j < total; j += NT) {
-            const uint2 en = entry(j);
-            const uint32_t kx = f32_order_key(__uint_as_float(en.x));
-            const int ix = (int)en.y;
-            if (kx > tk || (kx == tk && ix <= ti)) atomicOr(&sh.bitmap[ix >> 5], 1u << (ix & 31));
+#pragma unroll
+          for (int i = 0; i < kListPerLane; ++i) {
+            if (ev[i] == ev[i]) {
+              const uint32_t kx = f32_order_key(ev[i]);
+              if (kx > tk || (kx == tk && ei[i] <= ti)) atomicOr(&sh.bitmap[ei[i] >> 5], 1u << (ei[i] & 31));
+            }
           }
         }
       }
@@ -541,16 +544,15 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
   write_tail();
 }
 
-// LDS list capacity: room for the survivors of the sampled level (about
-// 1.25 K_sel plus a few sample standard deviations, scaled by the sampling).
-static int list_capacity(int k_sel) {
-  int cap = 3 * k_sel + 1024;
-  cap = cap < 2048 ? 2048 : cap;
-  return cap > 8192 ? 8192 : cap;
-}
+// LDS list capacity: one segment of 64 * kListPerLane entries per wave. The
+// sampled level keeps about 1.25 K_sel plus a few sample standard deviations
+// in all, spread evenly over the waves; rows whose share overflows a segment
+// take the general path.
+static int list_capacity(int nt) { return (nt / 64) * 64 * kListPerLane; }
 
 template <int NT, int G>
-static void launch_sel(const SelectArgs& a, hipStream_t st) {
+static void launch_sel(SelectArgs a, hipStream_t st) {
+  a.list_cap = list_capacity(NT);
   const size_t lds = (size_t)a.list_cap * 8;
   if (a.kpool == 4 && (a.width & 3) == 0)
     select_kernel<NT, G, true><<<a.q_end - a.q_begin, NT, lds, st>>>(a);
@@ -577,7 +579,6 @@ void launch_select(const float* logits, int64_t ld, int q_begin, int q_end,
   a.width = width;
   a.tail_on = tail_on;
   a.max_pools = max_pools;
-  a.list_cap = list_capacity(k_sel);
   a.out_ids = out_ids;
   a.out_tok = out_tok;
   if (max_pools <= 1024) launch_sel<256, 1>(a, st);

@@ -188,11 +188,21 @@ def test_logits_fp8_sampled():
 # ---------------------------------------------------------------------------
 
 def _select_exact(d, logits_dev, q_begin, q_end):
+    """kpool_select, and kpool_select_expand (the kernel the indexer runs per
+    chunk: ids and token rows), against the oracle's selection and expansion
+    of the same logits, bit for bit."""
     p = d.p
-    out = torch.full((q_end - q_begin, p.k_sel), -999, dtype=torch.int32, device=DEV)
+    rows = q_end - q_begin
+    out = torch.full((rows, p.k_sel), -999, dtype=torch.int32, device=DEV)
     kp.kpool_select(p, logits_dev, q_begin, q_end, d.cu, d.cu_pools, out)
+    ids2 = torch.full((rows, p.k_sel), -999, dtype=torch.int32, device=DEV)
+    tok = torch.full((rows, p.width), -999, dtype=torch.int32, device=DEV)
+    kp.kpool_select_expand(p, logits_dev, q_begin, q_end, d.cu, d.cu_pools, ids2, tok)
+    tok_only = torch.full((rows, p.width), -999, dtype=torch.int32, device=DEV)
+    kp.kpool_select_expand(p, logits_dev, q_begin, q_end, d.cu, d.cu_pools, None, tok_only)
     torch.cuda.synchronize()
     got = out.cpu().numpy()
+    got_ids2, got_tok, got_tok_only = ids2.cpu().numpy(), tok.cpu().numpy(), tok_only.cpu().numpy()
     lg = logits_dev.cpu().numpy()
     cu = d.inp.cu_seqlens.numpy().astype(np.int64)
     cuP = oracle.cu_pools_of(cu, p.kpool)
@@ -203,6 +213,11 @@ def _select_exact(d, logits_dev, q_begin, q_end):
         row = np.full(p.k_sel, -1, np.int64)
         row[:len(ref)] = ref
         assert np.array_equal(got[r], row), f"row {t}"
+        assert np.array_equal(got_ids2[r], row), f"row {t}: select_expand ids"
+        ref_tok = oracle.expand_row(t, cu, cuP, ref, p.kpool, p.index_topk,
+                                    bool(p.always_select_tail))
+        assert np.array_equal(got_tok[r], ref_tok), f"row {t}: select_expand tokens"
+        assert np.array_equal(got_tok_only[r], ref_tok), f"row {t}: tokens without ids"
 
 
 @pytest.mark.parametrize("wl", [0, 1] + SMALL[:3], ids=lambda w: w if isinstance(w, int) else w.name)
