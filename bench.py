@@ -112,11 +112,24 @@ class Path:
                                self.pooled)
 
     def phase_logits(self, logits):
+        """The scoring kernel of every chunk, as the indexer launches it. On
+        the FP8 path the workspace already holds the quantised q and keys of
+        the last step, so only the scoring kernel runs."""
         kp = self.kp
+        flags = kp.KPOOL_LOGITS_SKIP_ALL_SELECTED
+        if self.p.use_fp8:
+            flags |= kp.KPOOL_LOGITS_INPUTS_QUANTIZED
         for c0 in range(0, self.inp.T, self.qc):
             c1 = min(self.inp.T, c0 + self.qc)
             kp.kpool_logits(self.p, self.q, self.w, self.pooled, self.cu, self.cu_pools, c0, c1,
-                            self.ws, logits[:c1 - c0], flags=kp.KPOOL_LOGITS_SKIP_ALL_SELECTED)
+                            self.ws, logits[:c1 - c0], flags=flags)
+
+    def phase_fp8_quant(self, bufs):
+        """The FP8 input path over every q row (t, h) and every pooled key."""
+        qc, qs, kc, ks, P = bufs
+        rows = self.inp.T * self.p.num_heads
+        self.kp.kpool_fp8_quantize(self.q.view(rows, 128), rows, qc, qs)
+        self.kp.kpool_fp8_quantize(self.pooled[:P], P, kc, ks)
 
     def phase_select(self, logits, ids):
         kp = self.kp
@@ -227,16 +240,25 @@ def main():
     ms_select_expand = time_region(lambda: path.phase_select_expand(logits), reps)
     ms_select = time_region(lambda: path.phase_select(logits, ids), reps)
     ms_expand = time_region(lambda: path.phase_expand(ids), reps)
+    ms_fp8 = None
+    P = sum(L // wl.kpool for L in inp.doc_lengths)
+    if wl.fp8:
+        rows = T * wl.H
+        bufs = (torch.empty(rows, 128, dtype=torch.uint8, device="cuda:0"),
+                torch.empty(rows, dtype=torch.float32, device="cuda:0"),
+                torch.empty(max(P, 1), 128, dtype=torch.uint8, device="cuda:0"),
+                torch.empty(max(P, 1), dtype=torch.float32, device="cuda:0"), P)
+        ms_fp8 = time_region(lambda: path.phase_fp8_quant(bufs), reps)
     n_chunks = (T + path.qc - 1) // path.qc
 
     flops = 2.0 * wl.H * wl.D * need_nc
     peak = PEAK_FP8_TFLOPS if wl.fp8 else PEAK_BF16_TFLOPS
     achieved = flops / (ms_logits * 1e-3) / 1e12
-    P = sum(L // wl.kpool for L in inp.doc_lengths)
     by_compress = 4 * T * wl.D + 4 * wl.kpool * wl.D + 2 * P * wl.D
     by_select = 4 * need_nc + 4 * T * wl.k_sel
     by_select_expand = 4 * need_nc + 4 * T * wl.width
     by_expand = 4 * T * (wl.k_sel + wl.width)
+    by_fp8 = (T * wl.H + P) * (256 + 128 + 4)
 
     def gbs(b, m):
         return round(b / (m * 1e-3) / 1e9, 1)
@@ -278,6 +300,11 @@ def main():
                        "frac": round(by_expand / (ms_expand * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
         },
     }
+    if ms_fp8 is not None:
+        out["phases_ms"]["fp8_quant"] = round(ms_fp8, 4)
+        out["phases_hbm"]["fp8_quant"] = {
+            "bytes": by_fp8, "GB/s": gbs(by_fp8, ms_fp8),
+            "frac": round(by_fp8 / (ms_fp8 * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
     if rank == 0 and not args.no_cpu_baseline:
         log(f"cpu baseline on {args.cpu_rows} rows")
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_rows)

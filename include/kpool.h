@@ -136,9 +136,15 @@ kpool_status kpool_indexer_topk(const kpool_params* p, const void* q, const floa
  *   KPOOL_LOGITS_SKIP_ALL_SELECTED  rows whose n_c(t) <= K_sel may be left
  *       unwritten (their selection takes every pool); this is the launch
  *       kpool_indexer_topk makes for each query chunk.
+ *   KPOOL_LOGITS_INPUTS_QUANTIZED  (use_fp8 only) the workspace already
+ *       holds the E4M3 codes and scales of q rows q_begin .. q_end-1 and of
+ *       the pooled keys, as an earlier kpool_logits or kpool_indexer_topk
+ *       call with the same parameters, inputs and workspace left them; the
+ *       quantisation is skipped and only the scoring kernel runs.
  * Columns and rows not covered by the flags are left untouched. */
 #define KPOOL_LOGITS_FILL_MASKED 1
 #define KPOOL_LOGITS_SKIP_ALL_SELECTED 2
+#define KPOOL_LOGITS_INPUTS_QUANTIZED 4
 kpool_status kpool_logits(const kpool_params* p, const void* q, const float* w,
                           const void* pooled, const int32_t* cu_seqlens,
                           const int32_t* cu_pools, int32_t q_begin, int32_t q_end,

@@ -170,6 +170,7 @@ def kpool_indexer_topk(p: Params, q, w, pooled, cu_seqlens, cu_pools, workspace,
 
 KPOOL_LOGITS_FILL_MASKED = 1
 KPOOL_LOGITS_SKIP_ALL_SELECTED = 2
+KPOOL_LOGITS_INPUTS_QUANTIZED = 4
 
 
 def kpool_logits(p: Params, q, w, pooled, cu_seqlens, cu_pools, q_begin, q_end, workspace,

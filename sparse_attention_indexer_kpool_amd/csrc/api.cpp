@@ -238,7 +238,8 @@ kpool_status kpool_logits(const kpool_params* p, const void* q, const float* w,
                           void* stream) {
   Derived d;
   CHECK(derive(p, &d, true));
-  if (flags & ~(KPOOL_LOGITS_FILL_MASKED | KPOOL_LOGITS_SKIP_ALL_SELECTED))
+  if (flags & ~(KPOOL_LOGITS_FILL_MASKED | KPOOL_LOGITS_SKIP_ALL_SELECTED |
+                KPOOL_LOGITS_INPUTS_QUANTIZED))
     return fail(KPOOL_E_INVALID, "unknown logits flags 0x%x", flags);
   if (q_begin < 0 || q_end < q_begin || q_end > d.T)
     return fail(KPOOL_E_INVALID, "query rows [%d, %d) outside [0, %d]", q_begin, q_end, d.T);
@@ -257,7 +258,8 @@ kpool_status kpool_logits(const kpool_params* p, const void* q, const float* w,
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
   (void)hipGetLastError();
-  if (d.fp8) quantize_inputs(d, q, pooled, cu_pools, q_begin, q_end, ws, st);
+  if (d.fp8 && !(flags & KPOOL_LOGITS_INPUTS_QUANTIZED))
+    quantize_inputs(d, q, pooled, cu_pools, q_begin, q_end, ws, st);
   kpool::LogitsArgs a = logits_args(d, q, w, pooled, cu_seqlens, cu_pools, ws);
   a.out = out;
   a.q_begin = q_begin;

@@ -9,9 +9,15 @@
 // smallest integer e such that max|y| <= 448 * 2^e (e = 0 for a zero row);
 // OCP E4M3 (e4m3fn), round to nearest even, subnormals kept.
 //
+// BF16 and E4M3 rounding use gfx950's conversion instructions
+// (v_cvt_pk_bf16_f32, v_cvt_pk_fp8_f32), both round to nearest even; they
+// were checked bit for bit against the definitions over every BF16 input in
+// the E4M3 range, all E4M3 rounding midpoints and 2 M FP32 values with ties.
+//
 // HBM-bound: 256 bytes in and 128 + 4 bytes out per row. Sixteen lanes own a
-// row, eight values per lane; stages h < 8 stay in a lane, stages h >= 8
-// exchange with lane l ^ (h / 8). Every value goes through the same FP32
+// row, eight values per lane, and take four rows in turn (their loads are
+// issued together); stages h < 8 stay in a lane, stages h >= 8 exchange with
+// lane l ^ (h / 8). Every value goes through the same FP32
 // operations in the same order as the stage definition, so codes are exact.
 
 #include "kpool_device.h"
@@ -21,26 +27,12 @@
 
 namespace kpool {
 
-// E4M3 (e4m3fn) code of x, round to nearest even. |x| <= 448 for finite
-// rows; NaN gives 0x7f and larger magnitudes saturate to 448 (broken input
-// only).
-__device__ __forceinline__ uint32_t e4m3_rne(float x) {
-  const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
-  const float a = fabsf(x);
-  if (!(a <= 448.0f)) return sign | (a != a ? 0x7fu : 0x7eu);
-  if (a < 0x1p-6f) {
-    // subnormal range: multiples of 2^-9; rintf rounds halves to even
-    return sign | (uint32_t)rintf(a * 512.0f);
-  }
-  const int E = (int)((__float_as_uint(a) >> 23) & 0xffu) - 127;   // -6 .. 8
-  const float n = rintf(ldexpf(a, 3 - E));                          // 8 .. 16
-  return sign | (uint32_t)(((E + 7) << 3) + ((int)n - 8));
-}
+constexpr int kQuantRows = 4;   // rows per 16-lane group
 
 __global__ __launch_bounds__(256) void fp8_quantize_kernel(
     const uint16_t* __restrict__ x, int rows, const int32_t* __restrict__ rows_dev,
     uint8_t* __restrict__ codes, float* __restrict__ row_scale) {
-  const int row = blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int row0 = (blockIdx.x * 16 + (threadIdx.x >> 4)) * kQuantRows;
   const int l = threadIdx.x & 15;
   int limit = rows;
   if (rows_dev) {
@@ -48,63 +40,84 @@ __global__ __launch_bounds__(256) void fp8_quantize_kernel(
     limit = rd < limit ? (rd > 0 ? rd : 0) : limit;
   }
   // whole 16-lane groups leave together, so the shuffles below see live lanes
-  if (row >= limit) return;
+  if (row0 >= limit) return;
 
-  const uint4 in = *reinterpret_cast<const uint4*>(x + (size_t)row * 128 + l * 8);
-  const uint32_t wv[4] = {in.x, in.y, in.z, in.w};
-  float v[8];
+  // the group's rows are loaded before any is transformed, so a lane keeps
+  // kQuantRows 16-byte loads in flight
+  uint4 in[kQuantRows];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) v[e] = bf16_bits_to_f32((wv[e >> 1] >> (16 * (e & 1))) & 0xffffu);
+  for (int r = 0; r < kQuantRows; ++r)
+    in[r] = row0 + r < limit ? *reinterpret_cast<const uint4*>(x + (size_t)(row0 + r) * 128 + l * 8)
+                             : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+  for (int r = 0; r < kQuantRows; ++r) {
+    const int row = row0 + r;
+    const uint32_t wv[4] = {in[r].x, in[r].y, in[r].z, in[r].w};
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = bf16_bits_to_f32((wv[e >> 1] >> (16 * (e & 1))) & 0xffffu);
 
-  // stages h = 1, 2, 4 inside the lane
+    // stages h = 1, 2, 4 inside the lane
 #pragma unroll
-  for (int h = 1; h < 8; h <<= 1) {
+    for (int h = 1; h < 8; h <<= 1) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      if ((e & h) == 0) {
-        const float a = v[e], b = v[e + h];
-        v[e] = a + b;
-        v[e + h] = a - b;
+      for (int e = 0; e < 8; ++e) {
+        if ((e & h) == 0) {
+          const float a = v[e], b = v[e + h];
+          v[e] = a + b;
+          v[e + h] = a - b;
+        }
       }
     }
-  }
-  // stages h = 8, 16, 32, 64 across lanes l and l ^ (h / 8)
+    // stages h = 8, 16, 32, 64 across lanes l and l ^ (h / 8)
 #pragma unroll
-  for (int s = 1; s < 16; s <<= 1) {
-    const bool upper = (l & s) != 0;
+    for (int s = 1; s < 16; s <<= 1) {
+      const bool upper = (l & s) != 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float other = __shfl_xor(v[e], s, 16);
+        v[e] = upper ? (other - v[e]) : (v[e] + other);
+      }
+    }
+    const float norm = 0.08838834764831845f;   // FP32(128^-1/2)
+    float amax = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float other = __shfl_xor(v[e], s, 16);
-      v[e] = upper ? (other - v[e]) : (v[e] + other);
+      v[e] = (float)(__bf16)(v[e] * norm);      // v_cvt_pk_bf16_f32: round to nearest even
+      amax = fmaxf(amax, fabsf(v[e]));
+    }
+#pragma unroll
+    for (int s = 1; s < 16; s <<= 1) amax = fmaxf(amax, __shfl_xor(amax, s, 16));
+
+    int ex = 0;
+    if (amax > 0.f && amax <= 3.402823466e38f) {
+      int fe;
+      const float f = frexpf(amax, &fe);      // amax = f * 2^fe, f in [0.5, 1)
+      ex = fe - 9 + (f > 0.875f ? 1 : 0);
+    }
+    // v_cvt_pk_fp8_f32: OCP E4M3, round to nearest even, subnormals kept;
+    // |v 2^-ex| <= 448 by the choice of ex, so nothing saturates
+    uint32_t packed[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      int w = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[4 * h], -ex), ldexpf(v[4 * h + 1], -ex), 0,
+                                              false);
+      w = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[4 * h + 2], -ex), ldexpf(v[4 * h + 3], -ex), w,
+                                          true);
+      packed[h] = (uint32_t)w;
+    }
+    if (row < limit) {
+      *reinterpret_cast<uint2*>(codes + (size_t)row * 128 + l * 8) = make_uint2(packed[0], packed[1]);
+      if (l == 0) row_scale[row] = ldexpf(1.0f, ex);
     }
   }
-  const float norm = 0.08838834764831845f;   // FP32(128^-1/2)
-  float amax = 0.f;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    v[e] = bf16_bits_to_f32(f32_to_bf16_bits(v[e] * norm));
-    amax = fmaxf(amax, fabsf(v[e]));
-  }
-#pragma unroll
-  for (int s = 1; s < 16; s <<= 1) amax = fmaxf(amax, __shfl_xor(amax, s, 16));
-
-  int ex = 0;
-  if (amax > 0.f && amax <= 3.402823466e38f) {
-    int fe;
-    const float f = frexpf(amax, &fe);      // amax = f * 2^fe, f in [0.5, 1)
-    ex = fe - 9 + (f > 0.875f ? 1 : 0);
-  }
-  uint32_t packed[2] = {0u, 0u};
-#pragma unroll
-  for (int e = 0; e < 8; ++e) packed[e >> 2] |= e4m3_rne(ldexpf(v[e], -ex)) << (8 * (e & 3));
-  *reinterpret_cast<uint2*>(codes + (size_t)row * 128 + l * 8) = make_uint2(packed[0], packed[1]);
-  if (l == 0) row_scale[row] = ldexpf(1.0f, ex);
 }
 
 void launch_fp8_quantize(const uint16_t* x, int rows, const int32_t* rows_dev,
                          uint8_t* codes, float* row_scale, hipStream_t st) {
   if (rows <= 0) return;
-  fp8_quantize_kernel<<<(rows + 15) / 16, 256, 0, st>>>(x, rows, rows_dev, codes, row_scale);
+  constexpr int RPB = 16 * kQuantRows;   // rows per workgroup
+  fp8_quantize_kernel<<<(rows + RPB - 1) / RPB, 256, 0, st>>>(x, rows, rows_dev, codes, row_scale);
 }
 
 }  // namespace kpool

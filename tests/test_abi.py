@@ -138,3 +138,17 @@ def test_binding_refuses_host_tensors():
     with pytest.raises(ValueError):
         kp.kpool_fp8_quantize(torch.zeros(4, 128, dtype=torch.bfloat16), 4,
                               torch.zeros(4, 128, dtype=torch.uint8), torch.zeros(4))
+
+
+def test_header_constants_match_binding():
+    """The #define constants of include/kpool.h equal the binding's."""
+    import re
+    hdr = open(os.path.join(os.path.dirname(__file__), "..", "include", "kpool.h")).read()
+    defs = dict(re.findall(r"#define\s+(KPOOL_[A-Z_]+)\s+(\d+)", hdr))
+    assert defs, "no constants found"
+    for name, val in defs.items():
+        if hasattr(kp, name):
+            assert getattr(kp, name) == int(val), name
+    for name in ("KPOOL_LOGITS_FILL_MASKED", "KPOOL_LOGITS_SKIP_ALL_SELECTED",
+                 "KPOOL_LOGITS_INPUTS_QUANTIZED"):
+        assert getattr(kp, name) == int(defs[name]), name

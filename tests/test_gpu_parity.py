@@ -264,6 +264,23 @@ def test_select_exact_long_rows():
         _select_exact(d, d.logits(a_, b_), a_, b_)
 
 
+def test_logits_fp8_inputs_quantized_flag():
+    """KPOOL_LOGITS_INPUTS_QUANTIZED reuses the FP8 codes a previous call
+    left in the workspace: identical scores, bit for bit."""
+    d = dev_for(4)
+    p = d.p
+    ld = kp.kpool_logits_ld(p)
+    ws = d.workspace(p)
+    a_, b_ = 20000, 20064
+    out1 = torch.full((b_ - a_, ld), 7.0, dtype=torch.float32, device=DEV)
+    out2 = torch.full((b_ - a_, ld), 7.0, dtype=torch.float32, device=DEV)
+    kp.kpool_logits(p, d.q, d.w, d.pooled, d.cu, d.cu_pools, a_, b_, ws, out1)
+    kp.kpool_logits(p, d.q, d.w, d.pooled, d.cu, d.cu_pools, a_, b_, ws, out2,
+                    flags=kp.KPOOL_LOGITS_FILL_MASKED | kp.KPOOL_LOGITS_INPUTS_QUANTIZED)
+    torch.cuda.synchronize()
+    assert torch.equal(out1.view(torch.int32), out2.view(torch.int32))
+
+
 @pytest.mark.parametrize("wl", [0, 2] + SMALL, ids=lambda w: w if isinstance(w, int) else w.name)
 def test_expand_exact(wl):
     d = dev_for(wl)
