@@ -92,7 +92,21 @@ __device__ __forceinline__ void load_key_tile(const uint8_t* __restrict__ keys, 
     const int c = swz<C::CPR>(r, pos);
     const int jr = j0 + r < maxnc ? j0 + r : maxnc - 1;
     const uint8_t* src = keys + (size_t)(pool0 + jr) * C::ROWB + c * 16;
-    __builtin_amdgcn_global_load_lds(src, lds + (wid * C::LPW + i) * 1024, 16, 0, 0);
+    // global_load_lds_dwordx4 with M0 = the wave's 1 KB LDS block. Issued as
+    // inline asm (M0 saved and restored) so the compiler does not track it:
+    // its conservative tracking would wait for every outstanding store before
+    // each tile; the kernel waits for exactly the DMA instead (see step).
+    const uint32_t dst = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)(lds + (wid * C::LPW + i) * 1024));
+    uint32_t m0_saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "global_load_lds_dwordx4 %2, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(m0_saved)
+        : "s"(dst), "v"(src)
+        : "memory");
   }
 }
 
@@ -106,6 +120,15 @@ __device__ __forceinline__ float relu(float x) {
 __device__ __forceinline__ void wait_vmem_all() {
   // s_waitcnt vmcnt(0), leaving expcnt / lgkmcnt unconstrained
   __builtin_amdgcn_s_waitcnt(0x0f70);
+}
+
+// s_waitcnt vmcnt(N): wait until at most N vector-memory instructions of this
+// wave are outstanding. They complete in issue order, so this waits for
+// everything issued before the last N.
+template <int N>
+__device__ __forceinline__ void wait_vmem_leave() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0f70 | (N & 15) | ((N >> 4) << 14));
 }
 
 // Output slots of one lane per 32-pool unit: the queries whose score for pool
@@ -377,8 +400,12 @@ __global__ __launch_bounds__(64 * kLogitsWaves) void logits_kernel(LogitsArgs a)
 
     // Tiles alternate between tile0 and tile1; the body is instantiated once
     // per buffer so each LDS read names a fixed buffer.
+    // The DMA of tile jt was issued at the start of the previous step, before
+    // that step's kUnits * S::N output stores: waiting until only those
+    // stores are outstanding covers the DMA without waiting for the stores.
     auto step = [&](const int jt, const uint8_t* __restrict__ tb, uint8_t* __restrict__ nb) {
-      wait_vmem_all();
+      if (jt == 0) wait_vmem_all();
+      else wait_vmem_leave<kUnits * S::N>();
       __syncthreads();   // tile jt is in LDS; tile jt - 1 is no longer read
       const int j0 = jt * kPoolTile;
       if (jt + 1 < ntiles) load_key_tile<H, D, FP8>(keys, pool0, j0 + kPoolTile, maxnc, nb, wid, lane);
