@@ -63,11 +63,29 @@ SMALL = [
 ]
 
 
+def _doc_lengths(n, hi, seed):
+    """n seeded document lengths in [0, hi], some of them empty."""
+    return np.random.default_rng(seed).integers(0, hi + 1, n).tolist()
+
+
+# more documents than one workgroup of the compress kernel scans in place
+# (1024): the pool offsets then come from a separate pass
+MANY_DOCS = [
+    wlm.custom("docs1024_k4_h4_d64", doc_lengths=_doc_lengths(1024, 48, 31), H=4, D=64,
+               kpool=4, index_topk=16),
+    wlm.custom("docs1025_k3_h8_d128", doc_lengths=_doc_lengths(1025, 40, 32), H=8, D=128,
+               kpool=3, index_topk=12),
+    wlm.custom("docs1500_k2_h4_d64", doc_lengths=_doc_lengths(1500, 30, 33), H=4, D=64,
+               kpool=2, index_topk=8, tail=False),
+]
+
+
 # ---------------------------------------------------------------------------
 # compress
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("wl", [0, 1, 2, 3, 4] + SMALL, ids=lambda w: w if isinstance(w, int) else w.name)
+@pytest.mark.parametrize("wl", [0, 1, 2, 3, 4] + SMALL + MANY_DOCS,
+                         ids=lambda w: w if isinstance(w, int) else w.name)
 def test_compress(wl):
     d = dev_for(wl)
     log(f"compress {d.inp.wl.name} T={d.inp.T}")
@@ -264,6 +282,85 @@ def test_select_exact_long_rows():
         _select_exact(d, d.logits(a_, b_), a_, b_)
 
 
+def _long_doc(doc_lengths, kpool, index_topk, tail=True):
+    """Params and offsets of documents whose rows are up to 65536 pools long,
+    for selection on synthetic logits (no keys are needed)."""
+    from types import SimpleNamespace
+    lengths = [int(x) for x in doc_lengths]
+    cu = torch.zeros(len(lengths) + 1, dtype=torch.int32)
+    cu[1:] = torch.cumsum(torch.tensor(lengths, dtype=torch.int64), 0).to(torch.int32)
+    cuP = oracle.cu_pools_of(cu.numpy().astype(np.int64), kpool).astype(np.int32)
+    p = kp.Params(num_docs=len(lengths), total_tokens=sum(lengths), max_seqlen=max(lengths),
+                  num_heads=32, head_dim=128, kpool=kpool, index_topk=index_topk,
+                  always_select_tail=int(tail), use_fp8=0, query_chunk=0)
+    return SimpleNamespace(p=p, cu=cu.to(DEV), cu_pools=torch.from_numpy(cuP).to(DEV),
+                           inp=SimpleNamespace(cu_seqlens=cu))
+
+
+def _long_row_logits(n_rows, ld, nt, seed):
+    """Synthetic score rows, one kind per row index mod 11: Gaussian, heavy
+    tailed, heavy ties, constant, NaN, +-inf, sampled outliers that starve
+    the sampled level, one wave's share crowded past its list segment,
+    near-equal values one FP32 ulp apart, subnormals, signed zeros. The
+    crafted kinds assume the nt-thread layout (row element 4 (g nt + tid) + c
+    held by thread tid); the check itself holds whatever path a row takes."""
+    g = torch.Generator().manual_seed(seed)
+    lg = torch.randn(n_rows, ld, generator=g)
+    col = torch.arange(ld)
+    for r in range(n_rows):
+        kind = r % 11
+        if kind == 1:
+            lg[r] = lg[r] ** 3
+        elif kind == 2:
+            lg[r] = torch.randint(-3, 4, (ld,), generator=g).float()
+        elif kind == 3:
+            lg[r] = 0.5
+        elif kind == 4:
+            lg[r, ::11] = float("nan")
+        elif kind == 5:
+            lg[r, ::5] = float("-inf")
+            lg[r, 7::13] = float("inf")
+        elif kind == 6:
+            lg[r, 0:800:4] = 1000.0 + torch.arange(200).float()
+        elif kind == 7:
+            crowd = (col // 4) % nt < 64
+            lg[r, crowd] = 50.0 + torch.rand(int(crowd.sum()), generator=g)
+        elif kind == 8:
+            lg[r] = 1.0 + torch.randint(0, 3, (ld,), generator=g).float() * 2 ** -23
+        elif kind == 9:
+            lg[r] = lg[r] * 1e-40
+        elif kind == 10:
+            lg[r] = torch.where(torch.rand(ld, generator=g) < 0.5, -0.0, 0.0)
+    return lg
+
+
+@pytest.mark.parametrize("lengths,kpool,topk", [
+    ([131072], 4, 2048),                 # 32768 pools: 512-thread rows
+    ([131072, 5000], 4, 2048),           # second document after a long one
+    ([262144], 4, 2048),                 # 65536 pools: 1024-thread rows
+    ([65536], 1, 2048),                  # 65536 pools, K_sel 2048
+    ([262144], 4, 32768),                # K_sel 8192: lists overflow, general path
+    ([100000, 3], 3, 300),               # 33333 pools, kpool 3, ragged last group
+], ids=["p32k", "p32k_two_docs", "p64k", "p64k_k1", "p64k_ksel8192", "p33k_k3"])
+def test_select_exact_max_pools(lengths, kpool, topk):
+    """Exact selection and expansion on rows of up to 65536 pools (the
+    largest document the selection accepts), synthetic scores."""
+    d = _long_doc(lengths, kpool, topk)
+    p = d.p
+    ld = kp.kpool_logits_ld(p)
+    nt = 512 if p.max_seqlen // kpool <= 32768 else 1024
+    T = p.total_tokens
+    ends = [int(x) for x in d.inp.cu_seqlens.tolist()[1:]]
+    spans = [(max(ends[0] - 22, 0), ends[0] + min(11, T - ends[0])),   # end of the long document
+             (ends[0] // 2, ends[0] // 2 + 11),                        # mid length rows
+             (kpool * 300, kpool * 300 + 5),                           # short rows, same kernel
+             (0, 3)]                                                   # fewer pools than K_sel
+    for i, (a_, b_) in enumerate(spans):
+        log(f"select {lengths} kpool {kpool} topk {topk}: rows {a_}..{b_}")
+        lg = _long_row_logits(b_ - a_, ld, nt, 100 + i)
+        _select_exact(d, lg.to(DEV).contiguous(), a_, b_)
+
+
 def test_logits_fp8_inputs_quantized_flag():
     """KPOOL_LOGITS_INPUTS_QUANTIZED reuses the FP8 codes a previous call
     left in the workspace: identical scores, bit for bit."""
@@ -339,6 +436,21 @@ def test_end_to_end_small(wl):
     d = dev_for(wl)
     log(f"end to end {d.inp.wl.name}")
     _end_to_end(d, list(range(d.inp.T)))
+
+
+@pytest.mark.parametrize("wl", MANY_DOCS, ids=lambda w: w.name)
+def test_end_to_end_many_docs(wl):
+    """Over a thousand short documents: every document's first and last row
+    plus strided rows, end to end."""
+    d = dev_for(wl)
+    cu = d.inp.cu_seqlens.tolist()
+    T = d.inp.T
+    rows = set(wlm.strided_rows(T, 256))
+    for a_, b_ in zip(cu[:-1], cu[1:]):
+        if b_ > a_:
+            rows |= {a_, b_ - 1}
+    log(f"end to end {wl.name}: {len(rows)} rows of {T}")
+    _end_to_end(d, sorted(rows))
 
 
 @pytest.mark.parametrize("wl,n", [(1, 192), (2, 192), (3, 96), (4, 64)])
