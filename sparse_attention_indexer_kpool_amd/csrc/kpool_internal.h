@@ -34,6 +34,7 @@ struct LogitsArgs {
   int fill_masked;          // 1: write -inf in columns n_c .. ld-1
   int skip_select_all;      // 1: leave rows with n_c <= k_sel unwritten
   int fp8;
+  int pieces;               // set by the launcher: workgroups per query block
 };
 void launch_logits(const LogitsArgs& a, hipStream_t st);
 

@@ -61,6 +61,7 @@ struct LogitsCfg {
   static constexpr int CPR = ROWB / 16;              // 16-byte chunks per key row
   static constexpr int TILE_BYTES = kPoolTile * ROWB;
   static constexpr int LPW = TILE_BYTES / (1024 * kLogitsWaves);   // 1 KB loads per wave
+  static constexpr int A_BYTES = 32 * MT * ROWB;     // q rows of one wave
   static constexpr int KSTEP = FP8 ? kFp8K : 16;     // K per MFMA
   static constexpr int NSTEP = D / KSTEP;            // MFMAs per 32 x 32 tile
   static_assert(LPW >= 1 && LPW * 1024 * kLogitsWaves == TILE_BYTES, "tile split");
@@ -77,10 +78,44 @@ __device__ __forceinline__ int swz(int r, int c) {
   return CPR == 16 ? (c ^ (r & 15)) : (c ^ ((r >> 1) & 7));
 }
 
-// Issue this wave's share of a key tile straight into LDS (gfx950
-// global_load_lds_dwordx4: lane l of an instruction fills 16 bytes at
-// lds + 16 l). Rows past the causal range read the last causal row instead:
-// their scores are never stored.
+// One gfx950 global_load_lds_dwordx4: lane l copies 16 bytes from src to
+// block + 16 l, block being a 1 KB LDS block of this wave. Issued as inline
+// asm (M0 saved and restored) so the compiler does not track it: its
+// conservative tracking would wait for every outstanding store before each
+// tile; the kernel waits for exactly the copies it needs instead (see step).
+__device__ __forceinline__ void dma16(const uint8_t* src, uint8_t* block) {
+  const uint32_t dst = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)block);
+  uint32_t m0_saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "global_load_lds_dwordx4 %2, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(m0_saved)
+      : "s"(dst), "v"(src)
+      : "memory");
+}
+
+// The same with 4 bytes per lane (global_load_lds_dword): lane l copies
+// src to block + 4 l, block being a 256-byte LDS block of this wave.
+__device__ __forceinline__ void dma4(const float* src, float* block) {
+  const uint32_t dst = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) float*)block);
+  uint32_t m0_saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "global_load_lds_dword %2, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(m0_saved)
+      : "s"(dst), "v"(src)
+      : "memory");
+}
+
+// Issue this wave's share of a key tile straight into LDS. Rows past the
+// causal range read the last causal row instead: their scores are never
+// stored.
 template <int H, int D, bool FP8>
 __device__ __forceinline__ void load_key_tile(const uint8_t* __restrict__ keys, int pool0, int j0,
                                               int maxnc, uint8_t* lds, int wid, int lane) {
@@ -91,22 +126,26 @@ __device__ __forceinline__ void load_key_tile(const uint8_t* __restrict__ keys, 
     const int r = L / C::CPR, pos = L % C::CPR;
     const int c = swz<C::CPR>(r, pos);
     const int jr = j0 + r < maxnc ? j0 + r : maxnc - 1;
-    const uint8_t* src = keys + (size_t)(pool0 + jr) * C::ROWB + c * 16;
-    // global_load_lds_dwordx4 with M0 = the wave's 1 KB LDS block. Issued as
-    // inline asm (M0 saved and restored) so the compiler does not track it:
-    // its conservative tracking would wait for every outstanding store before
-    // each tile; the kernel waits for exactly the DMA instead (see step).
-    const uint32_t dst = __builtin_amdgcn_readfirstlane(
-        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)(lds + (wid * C::LPW + i) * 1024));
-    uint32_t m0_saved;
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %1\n\t"
-        "global_load_lds_dwordx4 %2, off\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(m0_saved)
-        : "s"(dst), "v"(src)
-        : "memory");
+    dma16(keys + (size_t)(pool0 + jr) * C::ROWB + c * 16, lds + (wid * C::LPW + i) * 1024);
+  }
+}
+
+// Issue this wave's 64 rows of q (contiguous in memory from row0) into its
+// LDS staging block, one coalesced 1 KB copy per instruction, with the key
+// tiles' chunk swizzle so that the fragment reads are conflict-free. Rows
+// past row_last (queries past the launch) read row_last instead; their
+// fragments are zeroed after the read.
+template <int H, int D, bool FP8>
+__device__ __forceinline__ void load_q_rows(const uint8_t* __restrict__ q, size_t row0,
+                                            size_t row_last, uint8_t* lds, int lane) {
+  using C = LogitsCfg<H, D, FP8>;
+#pragma unroll
+  for (int i = 0; i < C::A_BYTES / 1024; ++i) {
+    const int L = i * 64 + lane;
+    const int r = L / C::CPR, pos = L % C::CPR;
+    const int c = swz<C::CPR>(r, pos);
+    const size_t row = row0 + r < row_last ? row0 + r : row_last;
+    dma16(q + row * C::ROWB + c * 16, lds + i * 1024);
   }
 }
 
@@ -124,11 +163,13 @@ __device__ __forceinline__ void wait_vmem_all() {
 
 // s_waitcnt vmcnt(N): wait until at most N vector-memory instructions of this
 // wave are outstanding. They complete in issue order, so this waits for
-// everything issued before the last N.
+// everything issued before the last N. The counter field holds at most 63;
+// a larger N waits for 63, which only waits for more.
 template <int N>
 __device__ __forceinline__ void wait_vmem_leave() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt(0x0f70 | (N & 15) | ((N >> 4) << 14));
+  static_assert(N >= 0, "vmcnt range");
+  constexpr int M = N < 63 ? N : 63;
+  __builtin_amdgcn_s_waitcnt(0x0f70 | (M & 15) | ((M >> 4) << 14));
 }
 
 // Output slots of one lane per 32-pool unit: the queries whose score for pool
@@ -153,36 +194,106 @@ __global__ __launch_bounds__(64 * kLogitsWaves) void logits_kernel(LogitsArgs a)
   constexpr int QPW = QPB / kLogitsWaves;
   static_assert(H >= 4 && H <= 64 && (H & (H - 1)) == 0, "H in {4, 8, 16, 32, 64}");
 
-  // two separate LDS objects, so that reads of one provably do not alias the
-  // direct-to-LDS loads filling the other
-  __shared__ __attribute__((aligned(1024))) uint8_t tile0[C::TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t tile1[C::TILE_BYTES];
-  __shared__ int q_doc[QPB], q_nc[QPB];
-  __shared__ int seg_lo, seg_hi;
+  // two key-tile buffers; the second one is larger and first serves as the
+  // staging area of the q rows, read into registers before any key tile
+  // goes there
+  // staging: the q rows of every wave, then the head weights of every wave
+  // (64 FP32 per wave) and, on the FP8 path, the q row scales
+  constexpr int W_OFF = kLogitsWaves * C::A_BYTES;
+  constexpr int QS_OFF = W_OFF + kLogitsWaves * 256;
+  constexpr int STAGE_USED = QS_OFF + (FP8 ? kLogitsWaves * 256 : 0);
+  constexpr int STAGE = C::TILE_BYTES > STAGE_USED ? C::TILE_BYTES : STAGE_USED;
+  static_assert(C::TILE_BYTES + STAGE + 1024 <= 160 * 1024, "LDS budget");
+  // one LDS object with tile0 first, so every tile0 read and most tile1
+  // reads fold their address into the 16-bit instruction offset
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_tiles[C::TILE_BYTES + STAGE];
+  uint8_t* const tile0 = lds_tiles;
+  uint8_t* const tile1 = lds_tiles + C::TILE_BYTES;
+  __shared__ int q_doc[QPB], q_nc[QPB], q_pool0[QPB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wid = tid >> 6;
   const int g = lane >> 5, n = lane & 31;
-  const int t0 = a.q_begin + blockIdx.x * QPB;
+  // workgroup -> (query block, piece of its pool range). Consecutive
+  // workgroups go to consecutive XCDs; the pieces of one block are 8 apart, so
+  // they land on the same XCD at about the same time and read its q rows
+  // through one L2. The largest blocks (latest queries, most causal pools)
+  // are dispatched first.
+  const int nqb = (a.q_end - a.q_begin + QPB - 1) / QPB;
+  const int grp = (int)blockIdx.x / (8 * a.pieces), r8 = (int)blockIdx.x % (8 * a.pieces);
+  const int piece = r8 / 8;
+  const int bi = grp * 8 + r8 % 8;
+  if (bi >= nqb) return;                     // padding of the last group
+  const int qblk = nqb - 1 - bi;
+  const int t0 = a.q_begin + qblk * QPB;
   const uint8_t* keys = reinterpret_cast<const uint8_t*>(a.keys);
 
+  // document, causal range and pool offset of each query: a few dependent
+  // loads, done before the q rows are requested so they do not queue behind
   if (tid < QPB) {
     const int t = t0 + tid;
     if (t < a.q_end) {
       const QueryInfo qi = query_info(a.cu, a.cu_pools, a.B, a.T, a.kpool, a.max_pools, t);
       q_doc[tid] = qi.doc;
       q_nc[tid] = qi.n_c;
+      q_pool0[tid] = qi.pool0;
     } else {
       q_doc[tid] = -1;
       q_nc[tid] = 0;
+      q_pool0[tid] = 0;
     }
   }
   __syncthreads();
-  if (tid == 0) {
-    int lo = 0x7fffffff, hi = -1;
+  int b_lo = 0x7fffffff, b_hi = -1;
+  for (int j = 0; j < QPB; ++j)
+    if (q_doc[j] >= 0) { b_lo = min(b_lo, q_doc[j]); b_hi = max(b_hi, q_doc[j]); }
+
+  // this workgroup's work in document b: widest causal range among its
+  // queries there, first pool, and its share [jt_lo, jt_hi) of the tiles
+  struct DocWork { int maxnc, pool0, jt_lo, jt_hi; };
+  auto doc_work = [&](int b) {
+    DocWork d{0, 0, 0, 0};
     for (int j = 0; j < QPB; ++j)
-      if (q_doc[j] >= 0) { lo = min(lo, q_doc[j]); hi = max(hi, q_doc[j]); }
-    seg_lo = lo; seg_hi = hi;
+      if (q_doc[j] == b && q_nc[j] > d.maxnc) { d.maxnc = q_nc[j]; d.pool0 = q_pool0[j]; }
+    if (d.maxnc == 0 || (a.skip_select_all && d.maxnc <= a.k_sel)) return d;
+    const int ntiles = (d.maxnc + kPoolTile - 1) / kPoolTile;
+    d.jt_lo = ntiles * piece / a.pieces;
+    d.jt_hi = ntiles * (piece + 1) / a.pieces;
+    return d;
+  };
+  int b_first = b_hi + 1;
+  for (int b = b_lo; b <= b_hi; ++b) {
+    const DocWork d = doc_work(b);
+    if (d.jt_lo < d.jt_hi) { b_first = b; break; }
+  }
+  if (b_first > b_hi) return;                // nothing to score (uniform)
+  {
+    // the first key tile and the q rows are in flight together
+    const DocWork d = doc_work(b_first);
+    load_key_tile<H, D, FP8>(keys, d.pool0, d.jt_lo * kPoolTile, d.maxnc, tile0, wid, lane);
+  }
+  {
+    const size_t row0 = (size_t)(t0 + wid * QPW) * H, row_last = (size_t)a.q_end * H - 1;
+    load_q_rows<H, D, FP8>(reinterpret_cast<const uint8_t*>(a.q), row0, row_last,
+                           tile1 + wid * C::A_BYTES, lane);
+    // the wave's 64 head weights (rows past the launch read row_last)
+    const size_t wr = row0 + lane < row_last ? row0 + lane : row_last;
+    dma4(a.w + wr, reinterpret_cast<float*>(tile1 + W_OFF) + wid * 64);
+    if constexpr (FP8) dma4(a.q_scale + wr, reinterpret_cast<float*>(tile1 + QS_OFF) + wid * 64);
+  }
+
+  // LDS byte offset, within a 32-row block, of each 16-byte chunk this lane
+  // reads as an MFMA operand (row n, half g of D, swizzled). The swizzle
+  // depends only on the row's low bits, so the same offsets serve every 32-key
+  // unit of both tiles and both 32-row blocks of q; they are kept in registers
+  // (the asm hides them from rematerialisation) and a block's base folds into
+  // the read's immediate.
+  constexpr int NCH = C::CPR / 2;
+  uint32_t boff[NCH];
+#pragma unroll
+  for (int u = 0; u < NCH; ++u) {
+    boff[u] = (uint32_t)(n * C::ROWB + swz<C::CPR>(n, g * NCH + u) * 16);
+    asm volatile("" : "+v"(boff[u]));
   }
 
   // ---- A operand: this wave's (query, head) rows, held for the whole launch.
@@ -192,43 +303,47 @@ __global__ __launch_bounds__(64 * kLogitsWaves) void logits_kernel(LogitsArgs a)
                                          bf16x8_t>::type;
   Frag afrag[MT][C::NSTEP];
   float wq[MT][16];          // w' of the 16 accumulator rows this lane holds
+  // the q rows, head weights (and the first key tile) have arrived in LDS
+  wait_vmem_all();
+  __syncthreads();
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
-    const int flat = mt * 32 + n;
-    const int qb = wid * QPW + flat / H;
-    const int h = flat % H;
-    const int t = t0 + qb;
-    const bool ok = t < a.q_end;
-    const uint8_t* src = reinterpret_cast<const uint8_t*>(a.q) +
-                         ((size_t)(ok ? t : 0) * H + h) * C::ROWB + g * (C::ROWB / 2);
+#pragma unroll
+    for (int J = 0; J < 4; ++J) {
+      // accumulator rows 8 J + 4 g .. + 3 of tile mt: four consecutive rows
+      // of the wave, one 16-byte read (the same address for a half-wave)
+      const int fr = mt * 32 + J * 8 + g * 4;
+      const float4 w4 = *reinterpret_cast<const float4*>(tile1 + W_OFF + (wid * 64 + fr) * 4);
+      float4 s4 = make_float4(1.f, 1.f, 1.f, 1.f);
+      if constexpr (FP8) s4 = *reinterpret_cast<const float4*>(tile1 + QS_OFF + (wid * 64 + fr) * 4);
+      const bool ok = t0 + wid * QPW + fr / H < a.q_end;   // the four rows share a query
+      wq[mt][J * 4 + 0] = ok ? w4.x * a.scale * s4.x : 0.f;
+      wq[mt][J * 4 + 1] = ok ? w4.y * a.scale * s4.y : 0.f;
+      wq[mt][J * 4 + 2] = ok ? w4.z * a.scale * s4.z : 0.f;
+      wq[mt][J * 4 + 3] = ok ? w4.w * a.scale * s4.w : 0.f;
+    }
+  }
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const bool ok = t0 + wid * QPW + (mt * 32 + n) / H < a.q_end;
+    const uint8_t* blk = tile1 + wid * C::A_BYTES + mt * 32 * C::ROWB;
 #pragma unroll
     for (int s = 0; s < C::NSTEP; ++s) {
       if constexpr (FP8 && kFp8K == 64) {
-        const uint4 lo4 = ok ? *reinterpret_cast<const uint4*>(src + s * 32) : make_uint4(0, 0, 0, 0);
-        const uint4 hi4 = ok ? *reinterpret_cast<const uint4*>(src + s * 32 + 16) : make_uint4(0, 0, 0, 0);
+        uint4 lo4 = *reinterpret_cast<const uint4*>(blk + boff[2 * s]);
+        uint4 hi4 = *reinterpret_cast<const uint4*>(blk + boff[2 * s + 1]);
+        if (!ok) lo4 = hi4 = make_uint4(0, 0, 0, 0);
         i32x8_t f = {(int)lo4.x, (int)lo4.y, (int)lo4.z, (int)lo4.w,
                      (int)hi4.x, (int)hi4.y, (int)hi4.z, (int)hi4.w};
         afrag[mt][s] = f;
       } else if constexpr (FP8) {
-        afrag[mt][s] = ok ? *reinterpret_cast<const long*>(src + s * 8) : 0l;
+        const long v = *reinterpret_cast<const long*>(blk + boff[s >> 1] + (s & 1) * 8);
+        afrag[mt][s] = ok ? v : 0l;
       } else {
-        const uint4 v = ok ? *reinterpret_cast<const uint4*>(src + s * 16) : make_uint4(0, 0, 0, 0);
+        uint4 v = *reinterpret_cast<const uint4*>(blk + boff[s]);
+        if (!ok) v = make_uint4(0, 0, 0, 0);
         afrag[mt][s] = __builtin_bit_cast(bf16x8_t, v);
       }
-    }
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int row = (j >> 2) * 8 + g * 4 + (j & 3);   // accumulator row of slot j
-      const int fr = mt * 32 + row;
-      const int qb2 = wid * QPW + fr / H;
-      const int h2 = fr % H;
-      const int t2 = t0 + qb2;
-      float wv = 0.f;
-      if (t2 < a.q_end) {
-        wv = a.w[(size_t)t2 * H + h2] * a.scale;
-        if constexpr (FP8) wv *= a.q_scale[(size_t)t2 * H + h2];
-      }
-      wq[mt][j] = wv;
     }
   }
 
@@ -238,31 +353,11 @@ __global__ __launch_bounds__(64 * kLogitsWaves) void logits_kernel(LogitsArgs a)
   const uint32_t nrec = (uint32_t)((size_t)wg_rows * a.ld * 4);
   const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
       a.out + (size_t)(t0 - a.q_begin) * a.ld, 0, (int)nrec, 0x00020000);
-  // LDS byte offset, within a 32-pool unit, of each 16-byte chunk this lane
-  // reads as the B operand (key row n, half g of D, swizzled). The swizzle
-  // depends only on the row's low bits, so the same offsets serve every unit
-  // and both tiles; they are kept in registers (the asm hides them from
-  // rematerialisation) and the unit's base folds into the read's immediate.
-  constexpr int NCH = C::CPR / 2;
-  uint32_t boff[NCH];
-#pragma unroll
-  for (int u = 0; u < NCH; ++u) {
-    boff[u] = (uint32_t)(n * C::ROWB + swz<C::CPR>(n, g * NCH + u) * 16);
-    asm volatile("" : "+v"(boff[u]));
-  }
 
-  __syncthreads();
-  const int b_lo = seg_lo, b_hi = seg_hi;
-
-  for (int b = b_lo; b <= b_hi; ++b) {
-    // widest causal range among this workgroup's queries of document b
-    int maxnc = 0;
-    for (int j = 0; j < QPB; ++j)
-      if (q_doc[j] == b) maxnc = max(maxnc, q_nc[j]);
-    if (maxnc == 0) continue;
-    if (a.skip_select_all && maxnc <= a.k_sel) continue;
-    const int pool0 = clampi(a.cu_pools[b], 0, a.T / a.kpool);
-    const int ntiles = (maxnc + kPoolTile - 1) / kPoolTile;
+  for (int b = b_first; b <= b_hi; ++b) {
+    const DocWork dw = doc_work(b);
+    if (dw.jt_lo >= dw.jt_hi) continue;
+    const int maxnc = dw.maxnc, pool0 = dw.pool0, jt_lo = dw.jt_lo, jt_hi = dw.jt_hi;
 
     // per output slot: causal limit (0 for other documents) and row offset
     uint32_t lim[S::N], roff[S::N];
@@ -393,10 +488,15 @@ __global__ __launch_bounds__(64 * kLogitsWaves) void logits_kernel(LogitsArgs a)
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int j = 0; j < 16; ++j) accB[mt][j] = 0.f;
-    int prev = -1;       // first column of the unit held in accB (-1: none)
+    // first column of the unit held in accB; kNoUnit: none (its columns are
+    // negative, so every lane's store is masked)
+    constexpr int kNoUnit = -(1 << 30);
+    int prev = kNoUnit;
 
-    __syncthreads();     // both LDS buffers are free
-    load_key_tile<H, D, FP8>(keys, pool0, 0, maxnc, tile0, wid, lane);
+    if (b != b_first) {  // (the first document's first tile is already on its way)
+      __syncthreads();   // both LDS buffers are free
+      load_key_tile<H, D, FP8>(keys, pool0, jt_lo * kPoolTile, maxnc, tile0, wid, lane);
+    }
 
     // Tiles alternate between tile0 and tile1; the body is instantiated once
     // per buffer so each LDS read names a fixed buffer.
@@ -404,11 +504,11 @@ __global__ __launch_bounds__(64 * kLogitsWaves) void logits_kernel(LogitsArgs a)
     // that step's kUnits * S::N output stores: waiting until only those
     // stores are outstanding covers the DMA without waiting for the stores.
     auto step = [&](const int jt, const uint8_t* __restrict__ tb, uint8_t* __restrict__ nb) {
-      if (jt == 0) wait_vmem_all();
+      if (jt == jt_lo) wait_vmem_all();
       else wait_vmem_leave<kUnits * S::N>();
       __syncthreads();   // tile jt is in LDS; tile jt - 1 is no longer read
       const int j0 = jt * kPoolTile;
-      if (jt + 1 < ntiles) load_key_tile<H, D, FP8>(keys, pool0, j0 + kPoolTile, maxnc, nb, wid, lane);
+      if (jt + 1 < jt_hi) load_key_tile<H, D, FP8>(keys, pool0, j0 + kPoolTile, maxnc, nb, wid, lane);
 #pragma unroll
       for (int u = 0; u < kUnits; u += 2) {
         mma(accA, tb, u);
@@ -420,9 +520,9 @@ __global__ __launch_bounds__(64 * kLogitsWaves) void logits_kernel(LogitsArgs a)
         prev = j0 + 32 * u + 32;
       }
     };
-    for (int jt = 0; jt < ntiles; jt += 2) {
+    for (int jt = jt_lo; jt < jt_hi; jt += 2) {
       step(jt, tile0, tile1);
-      if (jt + 1 < ntiles) step(jt + 1, tile1, tile0);
+      if (jt + 1 < jt_hi) step(jt + 1, tile1, tile0);
     }
     epilogue(accB, prev);
   }
@@ -434,11 +534,22 @@ __global__ void fill_kernel(float* __restrict__ out, size_t count, float v) {
   for (; i < count; i += stride) out[i] = v;
 }
 
+#ifndef KPOOL_LOGITS_PIECES
+#define KPOOL_LOGITS_PIECES 0
+#endif
+
 template <int H, int D, bool FP8>
-static void launch_hdf(const LogitsArgs& a, hipStream_t st) {
+static void launch_hdf(LogitsArgs a, hipStream_t st) {
   constexpr int QPB = LogitsCfg<H, D, FP8>::QPB;
   const int rows = a.q_end - a.q_begin;
-  logits_kernel<H, D, FP8><<<(rows + QPB - 1) / QPB, 64 * kLogitsWaves, 0, st>>>(a);
+  // Each query block is one workgroup of a CU, and its work grows with its
+  // queries' causal range, so one workgroup per block leaves CUs idle while
+  // the longest rows finish. Long rows are split into pieces of the pool
+  // range: the dispatcher hands the next (smaller) piece to whichever CU
+  // frees first.
+  a.pieces = KPOOL_LOGITS_PIECES > 0 ? KPOOL_LOGITS_PIECES : (a.max_pools >= 2048 ? 2 : 1);
+  const int groups = ((rows + QPB - 1) / QPB + 7) / 8;
+  logits_kernel<H, D, FP8><<<groups * 8 * a.pieces, 64 * kLogitsWaves, 0, st>>>(a);
 }
 
 template <int D, bool FP8>
