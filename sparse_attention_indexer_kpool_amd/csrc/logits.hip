@@ -544,10 +544,14 @@ static void launch_hdf(LogitsArgs a, hipStream_t st) {
   const int rows = a.q_end - a.q_begin;
   // Each query block is one workgroup of a CU, and its work grows with its
   // queries' causal range, so one workgroup per block leaves CUs idle while
-  // the longest rows finish. Long rows are split into pieces of the pool
+  // the longest rows finish. Long rows are split into two pieces of the pool
   // range: the dispatcher hands the next (smaller) piece to whichever CU
-  // frees first.
-  a.pieces = KPOOL_LOGITS_PIECES > 0 ? KPOOL_LOGITS_PIECES : (a.max_pools >= 2048 ? 2 : 1);
+  // frees first. Each piece pays the start-up again (about 8 us to bring in
+  // its q rows), so this pays only for long sweeps: measured on the 64K
+  // context (16384 pools, BF16) it gains about 1 %, and it loses at 8192
+  // pools on the FP8 path, whose sweep is half as long per pool.
+  const long sweep = (long)a.max_pools * (FP8 ? 1 : 2);
+  a.pieces = KPOOL_LOGITS_PIECES > 0 ? KPOOL_LOGITS_PIECES : (sweep >= 32768 ? 2 : 1);
   const int groups = ((rows + QPB - 1) / QPB + 7) / 8;
   logits_kernel<H, D, FP8><<<groups * 8 * a.pieces, 64 * kLogitsWaves, 0, st>>>(a);
 }
