@@ -209,7 +209,10 @@ __global__ __launch_bounds__(64 * kLogitsWaves) void logits_kernel(LogitsArgs a)
   __shared__ __attribute__((aligned(1024))) uint8_t lds_tiles[C::TILE_BYTES + STAGE];
   uint8_t* const tile0 = lds_tiles;
   uint8_t* const tile1 = lds_tiles + C::TILE_BYTES;
-  __shared__ int q_doc[QPB], q_nc[QPB], q_pool0[QPB];
+  __shared__ int q_doc[QPB], q_nc[QPB];
+  __shared__ int run_doc[QPB], run_nc[QPB], run_pool0[QPB];
+  constexpr int QW = (QPB + 63) / 64;                // waves holding one query per lane
+  __shared__ int run_cnt[QW];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wid = tid >> 6;
@@ -230,46 +233,60 @@ __global__ __launch_bounds__(64 * kLogitsWaves) void logits_kernel(LogitsArgs a)
 
   // document, causal range and pool offset of each query: a few dependent
   // loads, done before the q rows are requested so they do not queue behind
+  int my_doc = -1, my_nc = 0, my_pool0 = 0;
   if (tid < QPB) {
     const int t = t0 + tid;
     if (t < a.q_end) {
       const QueryInfo qi = query_info(a.cu, a.cu_pools, a.B, a.T, a.kpool, a.max_pools, t);
-      q_doc[tid] = qi.doc;
-      q_nc[tid] = qi.n_c;
-      q_pool0[tid] = qi.pool0;
-    } else {
-      q_doc[tid] = -1;
-      q_nc[tid] = 0;
-      q_pool0[tid] = 0;
+      my_doc = qi.doc;
+      my_nc = qi.n_c;
+      my_pool0 = qi.pool0;
     }
+    q_doc[tid] = my_doc;
+    q_nc[tid] = my_nc;
   }
   __syncthreads();
-  int b_lo = 0x7fffffff, b_hi = -1;
-  for (int j = 0; j < QPB; ++j)
-    if (q_doc[j] >= 0) { b_lo = min(b_lo, q_doc[j]); b_hi = max(b_hi, q_doc[j]); }
+  // Runs of queries in one document. Queries are in token order, so each
+  // document's queries are consecutive and the last one of a run has the
+  // widest causal range; run r goes to slot r of the run_* arrays.
+  const bool run_end = tid < QPB && my_doc >= 0 && (tid == QPB - 1 || q_doc[tid + 1] != my_doc);
+  const uint64_t end_mask = __ballot(run_end);
+  if (wid < QW && lane == 0) run_cnt[wid] = __popcll(end_mask);
+  __syncthreads();
+  int n_runs = 0, runs_before = 0;
+#pragma unroll
+  for (int w = 0; w < QW; ++w) {
+    n_runs += run_cnt[w];
+    runs_before += w < wid ? run_cnt[w] : 0;
+  }
+  if (run_end) {
+    const int r = runs_before + popc_lt(end_mask);
+    run_doc[r] = my_doc;
+    run_nc[r] = my_nc;
+    run_pool0[r] = my_pool0;
+  }
+  __syncthreads();
 
-  // this workgroup's work in document b: widest causal range among its
-  // queries there, first pool, and its share [jt_lo, jt_hi) of the tiles
+  // this workgroup's work in run r: the widest causal range of its queries,
+  // the document's first pool, and its share [jt_lo, jt_hi) of the tiles
   struct DocWork { int maxnc, pool0, jt_lo, jt_hi; };
-  auto doc_work = [&](int b) {
-    DocWork d{0, 0, 0, 0};
-    for (int j = 0; j < QPB; ++j)
-      if (q_doc[j] == b && q_nc[j] > d.maxnc) { d.maxnc = q_nc[j]; d.pool0 = q_pool0[j]; }
+  auto run_work = [&](int r) {
+    DocWork d{run_nc[r], run_pool0[r], 0, 0};
     if (d.maxnc == 0 || (a.skip_select_all && d.maxnc <= a.k_sel)) return d;
     const int ntiles = (d.maxnc + kPoolTile - 1) / kPoolTile;
     d.jt_lo = ntiles * piece / a.pieces;
     d.jt_hi = ntiles * (piece + 1) / a.pieces;
     return d;
   };
-  int b_first = b_hi + 1;
-  for (int b = b_lo; b <= b_hi; ++b) {
-    const DocWork d = doc_work(b);
-    if (d.jt_lo < d.jt_hi) { b_first = b; break; }
+  int r_first = n_runs;
+  for (int r = 0; r < n_runs; ++r) {
+    const DocWork d = run_work(r);
+    if (d.jt_lo < d.jt_hi) { r_first = r; break; }
   }
-  if (b_first > b_hi) return;                // nothing to score (uniform)
+  if (r_first == n_runs) return;             // nothing to score (uniform)
   {
     // the first key tile and the q rows are in flight together
-    const DocWork d = doc_work(b_first);
+    const DocWork d = run_work(r_first);
     load_key_tile<H, D, FP8>(keys, d.pool0, d.jt_lo * kPoolTile, d.maxnc, tile0, wid, lane);
   }
   {
@@ -354,8 +371,9 @@ __global__ __launch_bounds__(64 * kLogitsWaves) void logits_kernel(LogitsArgs a)
   const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
       a.out + (size_t)(t0 - a.q_begin) * a.ld, 0, (int)nrec, 0x00020000);
 
-  for (int b = b_first; b <= b_hi; ++b) {
-    const DocWork dw = doc_work(b);
+  for (int r = r_first; r < n_runs; ++r) {
+    const DocWork dw = run_work(r);
+    const int b = run_doc[r];
     if (dw.jt_lo >= dw.jt_hi) continue;
     const int maxnc = dw.maxnc, pool0 = dw.pool0, jt_lo = dw.jt_lo, jt_hi = dw.jt_hi;
 
@@ -493,7 +511,7 @@ __global__ __launch_bounds__(64 * kLogitsWaves) void logits_kernel(LogitsArgs a)
     constexpr int kNoUnit = -(1 << 30);
     int prev = kNoUnit;
 
-    if (b != b_first) {  // (the first document's first tile is already on its way)
+    if (r != r_first) {  // (the first run's first tile is already on its way)
       __syncthreads();   // both LDS buffers are free
       load_key_tile<H, D, FP8>(keys, pool0, jt_lo * kPoolTile, maxnc, tile0, wid, lane);
     }
