@@ -70,6 +70,91 @@ __global__ __launch_bounds__(256) void compress_kernel(
   __shared__ int s_cup[FUSED ? kFusedDocs + 1 : 1];
   __shared__ int s_wsum[4];
   const int32_t* cup = cu_pools;
+  // the pool starting at token t0 -> pooled row p (16 bytes of it per thread)
+  auto pool_body = [&](int p, int t0) {
+    const int d0 = (tid % TPP) * 8;
+    auto lo_hi = [](uint32_t w, int half) { return bf16_bits_to_f32((w >> (16 * half)) & 0xffffu); };
+    float z[8], acc[8], m[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) { z[e] = 0.f; acc[e] = 0.f; m[e] = -INFINITY; }
+    if constexpr (KP > 0) {
+      // all slot slices of the pool in registers: one read of gate and k
+      uint4 g4[KP], k4[KP];
+#pragma unroll
+      for (int s = 0; s < KP; ++s) {
+        g4[s] = *reinterpret_cast<const uint4*>(gate + (size_t)(t0 + s) * D + d0);
+        k4[s] = *reinterpret_cast<const uint4*>(k + (size_t)(t0 + s) * D + d0);
+      }
+      float a[KP][8];
+#pragma unroll
+      for (int s = 0; s < KP; ++s) {
+        const float4 a0 = *reinterpret_cast<const float4*>(ape + s * D + d0);
+        const float4 a1 = *reinterpret_cast<const float4*>(ape + s * D + d0 + 4);
+        const uint32_t gw[4] = {g4[s].x, g4[s].y, g4[s].z, g4[s].w};
+        const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          a[s][e] = lo_hi(gw[e >> 1], e & 1) + av[e];        // slot logit, FP32
+          m[e] = fmaxf(m[e], a[s][e]);
+        }
+      }
+#pragma unroll
+      for (int s = 0; s < KP; ++s) {
+        const uint32_t kw[4] = {k4[s].x, k4[s].y, k4[s].z, k4[s].w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float ex = expf(a[s][e] - m[e]);
+          z[e] += ex;
+          acc[e] += ex * lo_hi(kw[e >> 1], e & 1);
+        }
+      }
+    } else {
+      // runtime kpool: pass 1 finds the per-dimension maximum, pass 2 the
+      // weights, their sum and the weighted keys
+      for (int ss = 0; ss < kpool; ++ss) {
+        const uint4 g4 = *reinterpret_cast<const uint4*>(gate + (size_t)(t0 + ss) * D + d0);
+        const float4 a0 = *reinterpret_cast<const float4*>(ape + ss * D + d0);
+        const float4 a1 = *reinterpret_cast<const float4*>(ape + ss * D + d0 + 4);
+        const uint32_t gw[4] = {g4.x, g4.y, g4.z, g4.w};
+        const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) m[e] = fmaxf(m[e], lo_hi(gw[e >> 1], e & 1) + av[e]);
+      }
+      for (int ss = 0; ss < kpool; ++ss) {
+        const uint4 g4 = *reinterpret_cast<const uint4*>(gate + (size_t)(t0 + ss) * D + d0);
+        const uint4 k4 = *reinterpret_cast<const uint4*>(k + (size_t)(t0 + ss) * D + d0);
+        const float4 a0 = *reinterpret_cast<const float4*>(ape + ss * D + d0);
+        const float4 a1 = *reinterpret_cast<const float4*>(ape + ss * D + d0 + 4);
+        const uint32_t gw[4] = {g4.x, g4.y, g4.z, g4.w};
+        const uint32_t kw[4] = {k4.x, k4.y, k4.z, k4.w};
+        const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float ex = expf((lo_hi(gw[e >> 1], e & 1) + av[e]) - m[e]);
+          z[e] += ex;
+          acc[e] += ex * lo_hi(kw[e >> 1], e & 1);
+        }
+      }
+    }
+    uint32_t outw[4];
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      uint32_t lo16 = f32_to_bf16_bits(acc[e] / z[e]);
+      uint32_t hi16 = f32_to_bf16_bits(acc[e + 1] / z[e + 1]);
+      outw[e >> 1] = lo16 | (hi16 << 16);
+    }
+    *reinterpret_cast<uint4*>(pooled + (size_t)p * D + d0) =
+        make_uint4(outw[0], outw[1], outw[2], outw[3]);
+  };
+  if (FUSED && B == 1) {
+    // one document: cu = {0, T} by the interface's precondition, so pool p
+    // starts at token p kpool and nothing has to be read before the slices
+    if (blockIdx.x == 0 && tid == 0) { cu_pools[0] = 0; cu_pools[1] = pool_cap; }
+    const int p = blockIdx.x * PPB + tid / TPP;
+    if (p >= pool_cap) return;
+    pool_body(p, p * kpool);
+    return;
+  }
   if constexpr (FUSED) {
     // cuP[b + 1] = sum over b' <= b of floor(L_b' / kpool): thread tid owns
     // documents tid * per .. tid * per + per - 1; a block prefix sum of the
@@ -111,7 +196,6 @@ __global__ __launch_bounds__(256) void compress_kernel(
   const int total = clampi(cup[B], 0, pool_cap);
   const int p = blockIdx.x * PPB + tid / TPP;
   if (p >= total) return;
-  const int d0 = (tid % TPP) * 8;
 
   // Document of pool p: the first pool of the wave is looked up by binary
   // search, the rest of the wave walks forward past the few boundaries it
@@ -127,78 +211,7 @@ __global__ __launch_bounds__(256) void compress_kernel(
   const int local = p - cup[b];
   const int t0 = clampi(cu[b] + local * kpool, 0, T - kpool);
 
-  auto lo_hi = [](uint32_t w, int half) { return bf16_bits_to_f32((w >> (16 * half)) & 0xffffu); };
-  float z[8], acc[8], m[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) { z[e] = 0.f; acc[e] = 0.f; m[e] = -INFINITY; }
-  if constexpr (KP > 0) {
-    // all slot slices of the pool in registers: one read of gate and k
-    uint4 g4[KP], k4[KP];
-#pragma unroll
-    for (int s = 0; s < KP; ++s) {
-      g4[s] = *reinterpret_cast<const uint4*>(gate + (size_t)(t0 + s) * D + d0);
-      k4[s] = *reinterpret_cast<const uint4*>(k + (size_t)(t0 + s) * D + d0);
-    }
-    float a[KP][8];
-#pragma unroll
-    for (int s = 0; s < KP; ++s) {
-      const float4 a0 = *reinterpret_cast<const float4*>(ape + s * D + d0);
-      const float4 a1 = *reinterpret_cast<const float4*>(ape + s * D + d0 + 4);
-      const uint32_t gw[4] = {g4[s].x, g4[s].y, g4[s].z, g4[s].w};
-      const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        a[s][e] = lo_hi(gw[e >> 1], e & 1) + av[e];        // slot logit, FP32
-        m[e] = fmaxf(m[e], a[s][e]);
-      }
-    }
-#pragma unroll
-    for (int s = 0; s < KP; ++s) {
-      const uint32_t kw[4] = {k4[s].x, k4[s].y, k4[s].z, k4[s].w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float ex = expf(a[s][e] - m[e]);
-        z[e] += ex;
-        acc[e] += ex * lo_hi(kw[e >> 1], e & 1);
-      }
-    }
-  } else {
-    // runtime kpool: pass 1 finds the per-dimension maximum, pass 2 the
-    // weights, their sum and the weighted keys
-    for (int ss = 0; ss < kpool; ++ss) {
-      const uint4 g4 = *reinterpret_cast<const uint4*>(gate + (size_t)(t0 + ss) * D + d0);
-      const float4 a0 = *reinterpret_cast<const float4*>(ape + ss * D + d0);
-      const float4 a1 = *reinterpret_cast<const float4*>(ape + ss * D + d0 + 4);
-      const uint32_t gw[4] = {g4.x, g4.y, g4.z, g4.w};
-      const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) m[e] = fmaxf(m[e], lo_hi(gw[e >> 1], e & 1) + av[e]);
-    }
-    for (int ss = 0; ss < kpool; ++ss) {
-      const uint4 g4 = *reinterpret_cast<const uint4*>(gate + (size_t)(t0 + ss) * D + d0);
-      const uint4 k4 = *reinterpret_cast<const uint4*>(k + (size_t)(t0 + ss) * D + d0);
-      const float4 a0 = *reinterpret_cast<const float4*>(ape + ss * D + d0);
-      const float4 a1 = *reinterpret_cast<const float4*>(ape + ss * D + d0 + 4);
-      const uint32_t gw[4] = {g4.x, g4.y, g4.z, g4.w};
-      const uint32_t kw[4] = {k4.x, k4.y, k4.z, k4.w};
-      const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float ex = expf((lo_hi(gw[e >> 1], e & 1) + av[e]) - m[e]);
-        z[e] += ex;
-        acc[e] += ex * lo_hi(kw[e >> 1], e & 1);
-      }
-    }
-  }
-  uint32_t outw[4];
-#pragma unroll
-  for (int e = 0; e < 8; e += 2) {
-    uint32_t lo16 = f32_to_bf16_bits(acc[e] / z[e]);
-    uint32_t hi16 = f32_to_bf16_bits(acc[e + 1] / z[e + 1]);
-    outw[e >> 1] = lo16 | (hi16 << 16);
-  }
-  *reinterpret_cast<uint4*>(pooled + (size_t)p * D + d0) =
-      make_uint4(outw[0], outw[1], outw[2], outw[3]);
+  pool_body(p, t0);
 }
 
 template <int D, bool FUSED>
