@@ -68,6 +68,7 @@ struct SelectShared {
   uint32_t hist[kBins + 1];
   float red_f[2][NW];
   uint32_t red_u[2][NW];
+  int red_n[NW];                                 // sample counts (kept apart from wave_tot)
   int wave_tot[NW];
   int res[3];                                    // b*, count above b*, count in b*
   uint32_t cand_key[NT];
@@ -257,20 +258,19 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
   smn = wave_min(smn);
   smx = wave_max(smx);
   ns = wave_sum(ns);
-  if (lane == 0) { sh.red_f[0][wid] = smn; sh.red_f[1][wid] = smx; sh.wave_tot[wid] = ns; }
+  if (lane == 0) { sh.red_f[0][wid] = smn; sh.red_f[1][wid] = smx; sh.red_n[wid] = ns; }
   for (int j = tid; j <= kBins; j += NT) sh.hist[j] = 0u;
   for (int j = tid; j < nwords; j += NT) sh.bitmap[j] = 0u;
   if (tid == 0) { sh.cand_cnt = 0; sh.res[0] = sh.res[1] = sh.res[2] = 0; }
   __syncthreads();
   smn = sh.red_f[0][0]; smx = sh.red_f[1][0];
-  int S = sh.wave_tot[0];
+  int S = sh.red_n[0];
 #pragma unroll
   for (int w = 1; w < NW; ++w) {
     smn = fminf(smn, sh.red_f[0][w]);
     smx = fmaxf(smx, sh.red_f[1][w]);
-    S += sh.wave_tot[w];
+    S += sh.red_n[w];
   }
-  __syncthreads();                                   // wave_tot is reused below
   const float srange = smx - smn;
   bool fast = S > 0 && (srange > 0.f) && (srange <= 3.0e38f);   // finite, not constant
 
@@ -342,19 +342,10 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
         ev[i] = j < running ? __uint_as_float(e.x) : NAN;   // list values are never NaN
         ei[i] = (int)e.y;
       }
-      float lmn = INFINITY, lmx = -INFINITY;
-#pragma unroll
-      for (int i = 0; i < kListPerLane; ++i) {
-        lmn = fminf(lmn, ev[i]);
-        lmx = fmaxf(lmx, ev[i]);
-      }
-      lmn = wave_min(lmn);
-      lmx = wave_max(lmx);
-      if (lane == 0) { sh.red_f[0][wid] = lmn; sh.red_f[1][wid] = lmx; }
-      __syncthreads();
-      lmn = sh.red_f[0][0]; lmx = sh.red_f[1][0];
-#pragma unroll
-      for (int w = 1; w < NW; ++w) { lmn = fminf(lmn, sh.red_f[0][w]); lmx = fmaxf(lmx, sh.red_f[1][w]); }
+      // histogram range: every list value is >= L, and all but the few
+      // above the sample's maximum are <= smx (those land in the top bin,
+      // which keeps the bins monotone); no reduction over the list needed
+      const float lmn = L, lmx = smx;
       const float lrange = lmx - lmn;
       if (!(lrange > 0.f) || !(lrange <= 3.0e38f)) {
         fast = false;                                  // ties or infinities: general path
@@ -380,19 +371,33 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
             }
           }
           __syncthreads();
-          if (tid < c_in) {
-            const uint32_t mk = sh.cand_key[tid];
-            const int mi = sh.cand_idx[tid];
-            int rank = 0;
-            for (int q = 0; q < c_in; ++q) {
-              const uint32_t okey = sh.cand_key[q];
-              rank += (okey > mk) || (okey == mk && sh.cand_idx[q] < mi);
+          // every wave ranks the few candidates itself (lane l takes
+          // candidates l, l + 64, ...), so the threshold element needs no
+          // second barrier to reach the other waves
+          uint32_t tk = 0u;
+          int ti = 0;
+          for (int c0 = 0; c0 < c_in; c0 += 64) {
+            const int ci = c0 + lane;
+            bool hit = false;
+            uint32_t mk = 0u;
+            int mi = 0;
+            if (ci < c_in) {
+              mk = sh.cand_key[ci];
+              mi = sh.cand_idx[ci];
+              int rank = 0;
+              for (int q = 0; q < c_in; ++q) {
+                const uint32_t okey = sh.cand_key[q];
+                rank += (okey > mk) || (okey == mk && sh.cand_idx[q] < mi);
+              }
+              hit = rank == k_in - 1;
             }
-            if (rank == k_in - 1) { sh.th_key = mk; sh.th_idx = mi; }
+            const uint64_t hm = __ballot(hit);
+            if (hm) {
+              const int src = __ffsll((unsigned long long)hm) - 1;
+              tk = (uint32_t)__builtin_amdgcn_readlane((int)mk, src);
+              ti = __builtin_amdgcn_readlane(mi, src);
+            }
           }
-          __syncthreads();
-          const uint32_t tk = sh.th_key;
-          const int ti = sh.th_idx;
           // ---- 5a. chosen list entries set their bitmap bits
 #pragma unroll
           for (int i = 0; i < kListPerLane; ++i) {

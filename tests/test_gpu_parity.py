@@ -270,6 +270,10 @@ def test_select_exact_adversarial():
     # kernel must take its general path
     for r0 in range(10, T, 97):
         lg[r0, 0:120:4] = 1000.0 + torch.arange(30).float()
+    # rows whose sampled slots all lie far below the rest
+    sampled = _sampled_slots(ld, 256)
+    for r0 in range(11, T, 89):
+        lg[r0, sampled] = -50.0
     _select_exact(d, lg.to(DEV).contiguous(), 0, T)
 
 
@@ -297,18 +301,29 @@ def _long_doc(doc_lengths, kpool, index_topk, tail=True):
                            inp=SimpleNamespace(cu_seqlens=cu))
 
 
+def _sampled_slots(ld, nt):
+    """Row elements the selection kernel samples for its level with nt
+    threads per row: element (g, (g / 2) mod 4) of every even group g, the
+    row element of slot (g, c) of thread tid being 4 (g nt + tid) + c."""
+    groups = (ld + 4 * nt - 1) // (4 * nt)
+    pos = [4 * (g * nt + tid) + ((g >> 1) & 3) for g in range(0, groups, 2) for tid in range(nt)]
+    return torch.tensor([p for p in pos if p < ld], dtype=torch.long)
+
+
 def _long_row_logits(n_rows, ld, nt, seed):
-    """Synthetic score rows, one kind per row index mod 11: Gaussian, heavy
+    """Synthetic score rows, one kind per row index mod 12: Gaussian, heavy
     tailed, heavy ties, constant, NaN, +-inf, sampled outliers that starve
     the sampled level, one wave's share crowded past its list segment,
-    near-equal values one FP32 ulp apart, subnormals, signed zeros. The
-    crafted kinds assume the nt-thread layout (row element 4 (g nt + tid) + c
-    held by thread tid); the check itself holds whatever path a row takes."""
+    near-equal values one FP32 ulp apart, subnormals, signed zeros, and
+    sampled slots all far below the rest (so almost every listed value lies
+    above the sample's maximum). The crafted kinds assume the nt-thread
+    layout; the check itself holds whatever path a row takes."""
     g = torch.Generator().manual_seed(seed)
     lg = torch.randn(n_rows, ld, generator=g)
     col = torch.arange(ld)
+    sampled = _sampled_slots(ld, nt)
     for r in range(n_rows):
-        kind = r % 11
+        kind = r % 12
         if kind == 1:
             lg[r] = lg[r] ** 3
         elif kind == 2:
@@ -331,6 +346,8 @@ def _long_row_logits(n_rows, ld, nt, seed):
             lg[r] = lg[r] * 1e-40
         elif kind == 10:
             lg[r] = torch.where(torch.rand(ld, generator=g) < 0.5, -0.0, 0.0)
+        elif kind == 11:
+            lg[r, sampled] = -50.0 + 0.01 * torch.randn(len(sampled), generator=g)
     return lg
 
 
