@@ -17,8 +17,9 @@
 // HBM-bound: 256 bytes in and 128 + 4 bytes out per row. Sixteen lanes own a
 // row, eight values per lane, and take four rows in turn (their loads are
 // issued together); stages h < 8 stay in a lane, stages h >= 8 exchange with
-// lane l ^ (h / 8). Every value goes through the same FP32
-// operations in the same order as the stage definition, so codes are exact.
+// lane l ^ (h / 8) through DPP and ds_swizzle lane permutations (neither
+// touches LDS memory). Every value goes through the same FP32 operations in
+// the same order as the stage definition, so codes are exact.
 
 #include "kpool_device.h"
 #include "kpool_internal.h"
@@ -69,14 +70,17 @@ __global__ __launch_bounds__(256) void fp8_quantize_kernel(
         }
       }
     }
-    // stages h = 8, 16, 32, 64 across lanes l and l ^ (h / 8)
+    // stages h = 8, 16, 32, 64 across lanes l and l ^ (h / 8): the lower
+    // lane keeps v + other, the upper one other - v, both as one
+    // fma(+-1, v, other), which rounds exactly as the addition or
+    // subtraction does
 #pragma unroll
     for (int s = 1; s < 16; s <<= 1) {
-      const bool upper = (l & s) != 0;
+      const float sgn = (l & s) != 0 ? -1.f : 1.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float other = __shfl_xor(v[e], s, 16);
-        v[e] = upper ? (other - v[e]) : (v[e] + other);
+        const float other = xor_lane16(v[e], s);
+        v[e] = fmaf(sgn, v[e], other);
       }
     }
     const float norm = 0.08838834764831845f;   // FP32(128^-1/2)
@@ -87,7 +91,7 @@ __global__ __launch_bounds__(256) void fp8_quantize_kernel(
       amax = fmaxf(amax, fabsf(v[e]));
     }
 #pragma unroll
-    for (int s = 1; s < 16; s <<= 1) amax = fmaxf(amax, __shfl_xor(amax, s, 16));
+    for (int s = 1; s < 16; s <<= 1) amax = fmaxf(amax, xor_lane16(amax, s));
 
     int ex = 0;
     if (amax > 0.f && amax <= 3.402823466e38f) {

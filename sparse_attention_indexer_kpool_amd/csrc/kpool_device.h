@@ -93,6 +93,20 @@ __device__ __forceinline__ int bits_of(T v) { return __builtin_bit_cast(int, v);
 template <typename T>
 __device__ __forceinline__ T from_bits(int b) { return __builtin_bit_cast(T, b); }
 
+// Value of lane l ^ m (m = 1, 2, 4 or 8; a constant once loops unroll)
+// within each row of 16 lanes: a DPP quad_perm swap for 1 and 2, and a
+// ds_swizzle in bit mode (source lane (l & 31) ^ m) for 4 and 8, which
+// measured faster than the two DPP moves those masks would need.
+__device__ __forceinline__ float xor_lane16(float v, int m) {
+  const int x = bits_of(v);
+  switch (m) {
+    case 1: return from_bits<float>(__builtin_amdgcn_update_dpp(x, x, 0xb1, 0xf, 0xf, false));
+    case 2: return from_bits<float>(__builtin_amdgcn_update_dpp(x, x, 0x4e, 0xf, 0xf, false));
+    case 4: return from_bits<float>(__builtin_amdgcn_ds_swizzle(x, (4 << 10) | 0x1f));
+    default: return from_bits<float>(__builtin_amdgcn_ds_swizzle(x, (8 << 10) | 0x1f));
+  }
+}
+
 // Reduction over the 64 lanes with an idempotent op (min or max); the result
 // is wave-uniform. Quad swaps and row mirrors reduce each row of 16 lanes,
 // row_bcast:15 / row_bcast:31 fold the rows into lane 63, read back with
