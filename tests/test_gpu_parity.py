@@ -481,6 +481,43 @@ def test_end_to_end_full_size_sampled(wl, n):
     _end_to_end(d, rows, fp8=bool(d.inp.wl.fp8))
 
 
+def test_end_to_end_max_pools():
+    """The longest document the indexer takes (65536 pools: T = 262144,
+    kpool 4), end to end at 4 heads and D = 64: the scoring sweep at its
+    longest (two pieces per query block), the 1024-thread selection and the
+    expansion, on sampled rows."""
+    wl = wlm.custom("long_T262144_H4_D64", T=262144, H=4, D=64, kpool=4, index_topk=2048,
+                    heavy_frac=0.05)
+    log(f"inputs {wl.name}")
+    inp = wlm.make_inputs(wl)
+    d = Dev(inp)
+    d.compress()
+    p = d.p
+    T = inp.T
+    ws = d.workspace(p)
+    tok = torch.full((T, p.width), -12345, dtype=torch.int32, device=DEV)
+    pid = torch.full((T, p.k_sel), -12345, dtype=torch.int32, device=DEV)
+    kp.kpool_indexer_topk(p, d.q, d.w, d.pooled, d.cu, d.cu_pools, ws, tok, pid)
+    torch.cuda.synchronize()
+    rows = sorted(set(wlm.strided_rows(T, 48)) | {0, 1, 2047, 2048, 2051, T - 2, T - 1})
+    sel = torch.tensor(rows, dtype=torch.long, device=DEV)
+    got_tok, got_pid = tok[sel].cpu().numpy(), pid[sel].cpu().numpy()
+    del tok, pid, ws
+    q, k, gate, w, ape, cu = oracle_inputs(inp)
+    pooled = d.pooled.float().cpu().numpy()
+    cuP = oracle.cu_pools_of(cu, p.kpool)
+    log(f"end to end {wl.name}: {len(rows)} sampled rows")
+    _, opid, osc = oracle.indexer_topk(q, w, pooled[:int(cuP[-1])], cu, p.kpool, p.index_topk,
+                                       True, rows=rows, return_scores=True)
+    for r, t in enumerate(rows):
+        okk, why = sets_match_up_to_ties(got_pid[r], opid[r], osc[r], 0, p.k_sel)
+        assert okk, f"row {t}: {why}"
+        gids = [x for x in got_pid[r] if x >= 0]
+        assert gids == sorted(gids)
+        assert np.array_equal(got_tok[r], oracle.expand_row(t, cu, cuP, gids, p.kpool,
+                                                            p.index_topk, True)), f"row {t}"
+
+
 def test_chunking_and_pool_idx_invariance():
     """Any query_chunk, and asking or not for pool ids, gives identical rows."""
     d = dev_for(2)
