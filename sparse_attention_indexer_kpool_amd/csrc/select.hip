@@ -295,8 +295,8 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
     // ---- 3. compact every value >= L into the LDS list. Each wave appends
     // to its own segment of seg_cap entries: a ballot gives each lane its
     // prefix, the running count stays scalar, and a (value, index) pair is one
-    // 8-byte LDS write. A wave that would overflow its segment stops writing;
-    // its count still records the overflow.
+    // 8-byte LDS write. A wave that overflows its segment keeps writing into
+    // the segment's last slot; its count records the overflow.
     const int seg_cap = list_cap / NW;                 // at most 64 * kListPerLane
     uint2* seg = list + wid * seg_cap;
     int running = 0;
@@ -308,11 +308,14 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
         for (int c = 0; c < 4; ++c) {
           const bool keep = v[4 * g + c] >= L;
           const uint64_t m = __ballot(keep);
-          const int cnt = __popcll(m);
-          if (running + cnt <= seg_cap) {
-            if (keep) seg[running + popc_lt(m)] = make_uint2(__float_as_uint(v[4 * g + c]), (uint32_t)idx_of(g, c));
+          // entries past the segment's end all land in its last slot; the
+          // count still records the overflow, which sends the row to the
+          // general path
+          if (keep) {
+            const int pos = min(running + popc_lt(m), seg_cap - 1);
+            seg[pos] = make_uint2(__float_as_uint(v[4 * g + c]), (uint32_t)idx_of(g, c));
           }
-          running += cnt;
+          running += __popcll(m);
         }
       }
     }
