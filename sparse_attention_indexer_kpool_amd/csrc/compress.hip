@@ -103,7 +103,9 @@ __global__ __launch_bounds__(256) void compress_kernel(
         const uint32_t kw[4] = {k4[s].x, k4[s].y, k4[s].z, k4[s].w};
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float ex = expf(a[s][e] - m[e]);
+          // hardware exp2 of the argument times log2(e): a few FP32 ulps
+          // from the exact exponential, far inside the BF16 result's ulp
+          const float ex = __expf(a[s][e] - m[e]);
           z[e] += ex;
           acc[e] += ex * lo_hi(kw[e >> 1], e & 1);
         }
@@ -130,7 +132,7 @@ __global__ __launch_bounds__(256) void compress_kernel(
         const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float ex = expf((lo_hi(gw[e >> 1], e & 1) + av[e]) - m[e]);
+          const float ex = __expf((lo_hi(gw[e >> 1], e & 1) + av[e]) - m[e]);
           z[e] += ex;
           acc[e] += ex * lo_hi(kw[e >> 1], e & 1);
         }
@@ -139,8 +141,10 @@ __global__ __launch_bounds__(256) void compress_kernel(
     uint32_t outw[4];
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
-      uint32_t lo16 = f32_to_bf16_bits(acc[e] / z[e]);
-      uint32_t hi16 = f32_to_bf16_bits(acc[e + 1] / z[e + 1]);
+      // z >= 1 (the largest slot contributes exp(0)); the hardware
+      // reciprocal is within 1 FP32 ulp
+      uint32_t lo16 = f32_to_bf16_bits(acc[e] * __builtin_amdgcn_rcpf(z[e]));
+      uint32_t hi16 = f32_to_bf16_bits(acc[e + 1] * __builtin_amdgcn_rcpf(z[e + 1]));
       outw[e >> 1] = lo16 | (hi16 << 16);
     }
     *reinterpret_cast<uint4*>(pooled + (size_t)p * D + d0) =
