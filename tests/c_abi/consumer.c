@@ -1,0 +1,58 @@
+/* A plain C consumer of libkpool.so: the header compiles as ISO C11 with
+ * every warning an error, and the library answers its host-only entry
+ * points (version, sizes, status strings, argument validation) without a
+ * GPU. Prints one line per check; exits non-zero on the first failure.
+ * Built and run by tests/test_c_abi.py. */
+#include <stdio.h>
+#include <string.h>
+
+#include "kpool.h"
+
+#define CHECK(cond)                                                   \
+  do {                                                                \
+    if (!(cond)) {                                                    \
+      fprintf(stderr, "FAILED line %d: %s\n", __LINE__, #cond);       \
+      return 1;                                                       \
+    }                                                                 \
+    printf("ok: %s\n", #cond);                                        \
+  } while (0)
+
+int main(void) {
+  kpool_params p;
+  static _Alignas(256) char fake[256];
+  size_t ws;
+  memset(&p, 0, sizeof p);
+  p.num_docs = 1;
+  p.total_tokens = 65536;
+  p.max_seqlen = 65536;
+  p.num_heads = 32;
+  p.head_dim = 128;
+  p.kpool = 4;
+  p.index_topk = 2048;
+  p.always_select_tail = 1;
+  p.query_chunk = 4096;
+
+  CHECK(kpool_abi_version() == KPOOL_ABI_VERSION);
+  CHECK(kpool_logits_ld(&p) == 16384);
+  ws = kpool_workspace_bytes(&p);
+  CHECK(ws >= (size_t)4096 * 16384 * 4);
+  CHECK(strcmp(kpool_status_string(KPOOL_OK), "ok") == 0);
+  CHECK(strcmp(kpool_status_string(KPOOL_E_WORKSPACE), "workspace too small") == 0);
+
+  /* validation happens before any launch: these calls touch no device */
+  CHECK(kpool_indexer_topk(NULL, fake, (const float*)fake, fake, (const int32_t*)fake,
+                           (const int32_t*)fake, fake, ws, (int32_t*)fake, NULL, NULL) ==
+        KPOOL_E_INVALID);
+  CHECK(strlen(kpool_last_error()) > 0);
+  p.num_heads = 48;
+  CHECK(kpool_indexer_topk(&p, fake, (const float*)fake, fake, (const int32_t*)fake,
+                           (const int32_t*)fake, fake, ws, (int32_t*)fake, NULL, NULL) ==
+        KPOOL_E_UNSUPPORTED);
+  p.num_heads = 32;
+  CHECK(kpool_indexer_topk(&p, fake, (const float*)fake, fake, (const int32_t*)fake,
+                           (const int32_t*)fake, fake, ws - 1, (int32_t*)fake, NULL, NULL) ==
+        KPOOL_E_WORKSPACE);
+  CHECK(kpool_fp8_quantize(fake, -1, (uint8_t*)fake, (float*)fake, NULL) == KPOOL_E_INVALID);
+  printf("all checks passed\n");
+  return 0;
+}
