@@ -556,11 +556,14 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
 // sampled level keeps about 1.25 K_sel plus a few sample standard deviations
 // in all, spread evenly over the waves; rows whose share overflows a segment
 // take the general path.
-static int list_capacity(int nt) { return (nt / 64) * 64 * kListPerLane; }
+// A wave of a G-group row holds at most 4 G values, so short rows need less.
+static int list_capacity(int nt, int g) {
+  return (nt / 64) * 64 * (4 * g < kListPerLane ? 4 * g : kListPerLane);
+}
 
 template <int NT, int G>
 static void launch_sel(SelectArgs a, hipStream_t st) {
-  a.list_cap = list_capacity(NT);
+  a.list_cap = list_capacity(NT, G);
   const size_t lds = (size_t)a.list_cap * 8;
   if (a.kpool == 4 && (a.width & 3) == 0)
     select_kernel<NT, G, true><<<a.q_end - a.q_begin, NT, lds, st>>>(a);
@@ -586,6 +589,11 @@ void launch_select(const float* logits, int64_t ld, int q_begin, int q_end,
   a.k_sel = k_sel;
   a.width = width;
   a.tail_on = tail_on;
+  // n_c(t) <= (t + 1) / kpool <= q_end / kpool whatever the documents are,
+  // so a chunk of early rows takes the variant sized for its longest row
+  // (fewer registers, more rows in flight per CU)
+  const int bound = q_end / kpool;
+  if (bound < max_pools) max_pools = bound < 1 ? 1 : bound;
   a.max_pools = max_pools;
   a.out_ids = out_ids;
   a.out_tok = out_tok;
