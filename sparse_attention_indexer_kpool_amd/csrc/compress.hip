@@ -47,6 +47,14 @@ __global__ __launch_bounds__(1024) void cu_pools_kernel(const int32_t* __restric
   }
 }
 
+// Two FP32 values -> packed BF16 pair (low half first), round to nearest
+// even by gfx950's conversion instruction (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
 // Documents whose pool offsets the compress kernel computes itself (one
 // prefix over the documents per workgroup, in LDS); beyond this a separate
 // cu_pools launch comes first.
@@ -78,18 +86,29 @@ __global__ __launch_bounds__(256) void compress_kernel(
 #pragma unroll
     for (int e = 0; e < 8; ++e) { z[e] = 0.f; acc[e] = 0.f; m[e] = -INFINITY; }
     if constexpr (KP > 0) {
-      // all slot slices of the pool in registers: one read of gate and k
+      // all slot slices of the pool in registers: one read of gate and k.
+      // The memory clobber and the scheduling barrier keep every load issued
+      // before the first use; left alone, the scheduler sinks the k loads to
+      // their uses and each then waits a full memory round trip of its own.
       uint4 g4[KP], k4[KP];
+      float4 ap[KP][2];
 #pragma unroll
       for (int s = 0; s < KP; ++s) {
         g4[s] = *reinterpret_cast<const uint4*>(gate + (size_t)(t0 + s) * D + d0);
         k4[s] = *reinterpret_cast<const uint4*>(k + (size_t)(t0 + s) * D + d0);
       }
+#pragma unroll
+      for (int s = 0; s < KP; ++s) {
+        ap[s][0] = *reinterpret_cast<const float4*>(ape + s * D + d0);
+        ap[s][1] = *reinterpret_cast<const float4*>(ape + s * D + d0 + 4);
+      }
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
       float a[KP][8];
 #pragma unroll
       for (int s = 0; s < KP; ++s) {
-        const float4 a0 = *reinterpret_cast<const float4*>(ape + s * D + d0);
-        const float4 a1 = *reinterpret_cast<const float4*>(ape + s * D + d0 + 4);
+        const float4 a0 = ap[s][0];
+        const float4 a1 = ap[s][1];
         const uint32_t gw[4] = {g4[s].x, g4[s].y, g4[s].z, g4[s].w};
         const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
 #pragma unroll
@@ -143,9 +162,8 @@ __global__ __launch_bounds__(256) void compress_kernel(
     for (int e = 0; e < 8; e += 2) {
       // z >= 1 (the largest slot contributes exp(0)); the hardware
       // reciprocal is within 1 FP32 ulp
-      uint32_t lo16 = f32_to_bf16_bits(acc[e] * __builtin_amdgcn_rcpf(z[e]));
-      uint32_t hi16 = f32_to_bf16_bits(acc[e + 1] * __builtin_amdgcn_rcpf(z[e + 1]));
-      outw[e >> 1] = lo16 | (hi16 << 16);
+      outw[e >> 1] = pack_bf16x2(acc[e] * __builtin_amdgcn_rcpf(z[e]),
+                                 acc[e + 1] * __builtin_amdgcn_rcpf(z[e + 1]));
     }
     *reinterpret_cast<uint4*>(pooled + (size_t)p * D + d0) =
         make_uint4(outw[0], outw[1], outw[2], outw[3]);
