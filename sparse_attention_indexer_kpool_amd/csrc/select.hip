@@ -601,6 +601,9 @@ void launch_select(const float* logits, int64_t ld, int q_begin, int q_end,
   else if (max_pools <= 2048) launch_sel<256, 2>(a, st);
   else if (max_pools <= 4096) launch_sel<256, 4>(a, st);
   else if (max_pools <= 8192) launch_sel<256, 8>(a, st);
+  else if (max_pools <= 10240) launch_sel<256, 10>(a, st);
+  else if (max_pools <= 12288) launch_sel<256, 12>(a, st);
+  else if (max_pools <= 14336) launch_sel<256, 14>(a, st);
   else if (max_pools <= 16384) launch_sel<256, 16>(a, st);
   else if (max_pools <= 32768) launch_sel<512, 16>(a, st);
   else launch_sel<1024, 16>(a, st);

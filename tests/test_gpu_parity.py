@@ -351,6 +351,26 @@ def _long_row_logits(n_rows, ld, nt, seed):
     return lg
 
 
+@pytest.mark.parametrize("lengths,kpool,topk,spans", [
+    ([16384], 4, 2048, [(16300, 16384), (8150, 8192), (4060, 4096), (2000, 2060)]),
+    ([16384], 4, 128, [(16330, 16384), (3000, 3100)]),
+    ([4096], 1, 300, [(3990, 4096), (1000, 1040)]),
+    ([3000, 9001], 3, 600, [(2900, 3100), (11900, 12001)]),
+    ([65536], 4, 2048, [(40900, 40960), (49100, 49152), (57300, 57344)]),
+], ids=["p4k_k512", "p4k_k32", "p4k_kpool1", "two_docs_kpool3", "p10k_12k_14k"])
+def test_select_exact_short_rows(lengths, kpool, topk, spans):
+    """Chunks whose rows are shorter than the document's longest (the kernel
+    variants sized for the chunk's last row: up to 1024 ... 14336 pools):
+    synthetic rows of every kind, crafted for 256 threads per row, so the
+    sampled level fails and the general path runs too."""
+    d = _long_doc(lengths, kpool, topk)
+    ld = kp.kpool_logits_ld(d.p)
+    for i, (a_, b_) in enumerate(spans):
+        log(f"select short rows {lengths} kpool {kpool} topk {topk}: rows {a_}..{b_}")
+        lg = _long_row_logits(b_ - a_, ld, 256, 200 + i)
+        _select_exact(d, lg.to(DEV).contiguous(), a_, b_)
+
+
 @pytest.mark.parametrize("lengths,kpool,topk", [
     ([131072], 4, 2048),                 # 32768 pools: 512-thread rows
     ([131072, 5000], 4, 2048),           # second document after a long one
