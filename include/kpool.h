@@ -192,6 +192,59 @@ kpool_status kpool_expand(const kpool_params* p, const int32_t* pool_idx,
 kpool_status kpool_fp8_quantize(const void* x, int32_t rows, uint8_t* codes,
                                 float* row_scale, void* stream);
 
+/* ---- Serving: one query per sequence, pooled keys kept in a cache -------
+ * ([MLM] sections 3 and 4: the indexer of the serving path scores pools of
+ * keys compressed as tokens arrive.) A sequence of L tokens holds its
+ * floor(L / kpool) complete pools in the caller's cache of pooled rows; its
+ * query is its token L - 1, whose indexer row is the one kpool_indexer_topk
+ * computes for the last token of a document of L tokens.
+ *
+ * kpool_compress_pools: step 1 for pools that have just completed, given by
+ * their slot tokens. Pool n of the call is tokens n*kpool .. n*kpool+kpool-1
+ * of k and gate; its pooled key (the same arithmetic as kpool_compress) goes
+ * to row dst_rows[n] of pooled; rows outside [0, pooled_rows) are skipped.
+ *   k, gate    BF16 [num_pools * kpool, D]
+ *   ape        FP32 [kpool, D]
+ *   dst_rows   int32 [num_pools]
+ *   pooled     BF16 [pooled_rows, D], rows dst_rows[n] written
+ * Uses params: head_dim, kpool. */
+kpool_status kpool_compress_pools(const kpool_params* p, const void* k, const void* gate,
+                                  const float* ape, int32_t num_pools, const int32_t* dst_rows,
+                                  int32_t pooled_rows, void* pooled, void* stream);
+
+/* Bytes of workspace kpool_decode_topk needs (0 for invalid parameters):
+ * the scores of every sequence, B rows of kpool_logits_ld floats. */
+size_t kpool_decode_workspace_bytes(const kpool_params* p);
+
+/* Steps 2-4 for B = num_docs sequences, one query each. Sequence b has
+ * L_b = seq_lens[b] tokens (0 <= L_b <= max_seqlen; 0: an all -1 row); its
+ * n_c = floor(L_b / kpool) complete pools are pooled rows pool_start[b] ..
+ * pool_start[b] + n_c - 1, and its token ids start at token_base[b] (0 when
+ * token_base is NULL). Row b of the outputs:
+ *   score[j] = sum_h w[b, h] * ReLU(scale * q[b, h, :] . pooled[pool_start[b] + j, :])
+ *   for j < n_c; the min(K_sel, n_c) best (ties to the lower j), expanded
+ *   in ascending order to token_base[b] + j*kpool + s, s < kpool; then the
+ *   tail token_base[b] + n_c*kpool .. token_base[b] + L_b - 1 (when
+ *   always_select_tail); then -1 to width W.
+ *   q           BF16 [B, H, D]
+ *   w           FP32 [B, H]
+ *   pooled      BF16 [pooled_rows, D]: the cache (reads are kept inside it;
+ *               the rows named above must lie in it for a meaningful result)
+ *   pool_start, seq_lens  int32 [B];  token_base  int32 [B] or NULL
+ *   workspace   at least kpool_decode_workspace_bytes(p) bytes, 256-byte aligned
+ *   out_token_idx  out int32 [B, W];  out_pool_idx  out int32 [B, K_sel]
+ *               (may be NULL): pool_start[b] + j, ascending, -1 pad
+ * Uses params: num_docs (= B), max_seqlen (a bound on every L_b), num_heads,
+ * head_dim, kpool, index_topk, always_select_tail, scale; use_fp8 must be 0
+ * (KPOOL_E_UNSUPPORTED otherwise); total_tokens and query_chunk are not used.
+ * Lengths above max_seqlen are scored over their first floor(max_seqlen /
+ * kpool) pools. */
+kpool_status kpool_decode_topk(const kpool_params* p, const void* q, const float* w,
+                               const void* pooled, int32_t pooled_rows, const int32_t* pool_start,
+                               const int32_t* seq_lens, const int32_t* token_base,
+                               void* workspace, size_t workspace_bytes,
+                               int32_t* out_token_idx, int32_t* out_pool_idx, void* stream);
+
 /* Static description of a status code. */
 const char* kpool_status_string(kpool_status s);
 

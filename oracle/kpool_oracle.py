@@ -333,3 +333,43 @@ def indexer_topk(q, w, pooled, cu_seqlens, kpool: int, index_topk: int,
     if return_scores:
         return tok, pid, all_scores
     return tok, pid
+
+
+# ---------------------------------------------------------------------------
+# Serving: one query per sequence over its cached pools ([MLM] sections 3
+# and 4: the serving indexer scores the pools of a growing sequence)
+# ---------------------------------------------------------------------------
+
+def decode_topk(q, w, pooled, pool_start, seq_lens, kpool: int, index_topk: int,
+                tail_on: bool, scale: float = 0.0, token_base=None):
+    """Token rows [B, index_topk + kpool] and pool ids [B, index_topk //
+    kpool] for B sequences, one query each: sequence b has L_b = seq_lens[b]
+    tokens, its query is token L_b - 1, and its floor(L_b / kpool) complete
+    pools are pooled rows pool_start[b] onwards. Row b is the row
+    indexer_topk gives the last token of a document of L_b tokens (pool ids
+    offset by pool_start[b], token ids by token_base[b]); L_b = 0 gives a row
+    of -1. q: [B, H, D]; w: [B, H] FP32; pooled: [P, D] (BF16 values)."""
+    q = np.asarray(q, dtype=F32)
+    w = np.asarray(w, dtype=F32)
+    pooled = np.asarray(pooled, dtype=F32)
+    B, H, D = q.shape
+    if scale == 0.0:
+        scale = float(F32(1.0 / np.sqrt(D)))
+    k_sel = index_topk // kpool
+    W = index_topk + kpool
+    tok = np.full((B, W), -1, dtype=np.int32)
+    pid = np.full((B, k_sel), -1, dtype=np.int32)
+    for b in range(B):
+        L = int(seq_lens[b])
+        if L <= 0:
+            continue
+        base = 0 if token_base is None else int(token_base[b])
+        n_c = causal_pools(L - 1, kpool)
+        keys = pooled[int(pool_start[b]):int(pool_start[b]) + n_c]
+        chosen = select_pools(row_scores(q[b], w[b], keys, scale), k_sel)
+        pid[b, :len(chosen)] = chosen + int(pool_start[b])
+        # the expansion of the last token of a one-document batch [0, L)
+        row = expand_row(L - 1, [0, L], [0, L // kpool], chosen, kpool, index_topk, tail_on)
+        tok[b] = np.where(row >= 0, row + base, -1)
+    return tok, pid
+

@@ -106,6 +106,12 @@ def lib() -> ctypes.CDLL:
         L.kpool_expand.argtypes = [P, vp, vp, vp, vp, vp]
         L.kpool_fp8_quantize.restype = ctypes.c_int
         L.kpool_fp8_quantize.argtypes = [vp, i32, vp, vp, vp]
+        L.kpool_compress_pools.restype = ctypes.c_int
+        L.kpool_compress_pools.argtypes = [P, vp, vp, vp, i32, vp, i32, vp, vp]
+        L.kpool_decode_workspace_bytes.restype = sz
+        L.kpool_decode_workspace_bytes.argtypes = [P]
+        L.kpool_decode_topk.restype = ctypes.c_int
+        L.kpool_decode_topk.argtypes = [P, vp, vp, vp, i32, vp, vp, vp, vp, sz, vp, vp, vp]
         L.kpool_status_string.restype = ctypes.c_char_p
         L.kpool_status_string.argtypes = [ctypes.c_int]
         L.kpool_last_error.restype = ctypes.c_char_p
@@ -117,7 +123,8 @@ def lib() -> ctypes.CDLL:
 EXPORTS = ["kpool_abi_version", "kpool_workspace_bytes", "kpool_logits_ld", "kpool_compress",
            "kpool_indexer_topk", "kpool_logits", "kpool_select", "kpool_select_expand",
            "kpool_expand",
-           "kpool_fp8_quantize", "kpool_status_string", "kpool_last_error"]
+           "kpool_fp8_quantize", "kpool_compress_pools", "kpool_decode_workspace_bytes",
+           "kpool_decode_topk", "kpool_status_string", "kpool_last_error"]
 
 
 def _check(status: int) -> None:
@@ -204,6 +211,26 @@ def kpool_expand(p: Params, pool_idx, cu_seqlens, cu_pools, out_token_idx, strea
 def kpool_fp8_quantize(x, rows, codes, row_scale, stream=None) -> None:
     _check(lib().kpool_fp8_quantize(_ptr(x), int(rows), _ptr(codes), _ptr(row_scale),
                                     _stream(stream)))
+
+
+def kpool_compress_pools(p: Params, k, gate, ape, num_pools, dst_rows, pooled,
+                         stream=None) -> None:
+    _check(lib().kpool_compress_pools(ctypes.byref(p.c()), _ptr(k), _ptr(gate), _ptr(ape),
+                                      int(num_pools), _ptr(dst_rows), int(pooled.shape[0]),
+                                      _ptr(pooled), _stream(stream)))
+
+
+def kpool_decode_workspace_bytes(p: Params) -> int:
+    return int(lib().kpool_decode_workspace_bytes(ctypes.byref(p.c())))
+
+
+def kpool_decode_topk(p: Params, q, w, pooled, pool_start, seq_lens, workspace, out_token_idx,
+                      out_pool_idx=None, token_base=None, stream=None) -> None:
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().kpool_decode_topk(ctypes.byref(p.c()), _ptr(q), _ptr(w), _ptr(pooled),
+                                   int(pooled.shape[0]), _ptr(pool_start), _ptr(seq_lens), _ptr(token_base),
+                                   _ptr(workspace), ws_bytes, _ptr(out_token_idx),
+                                   _ptr(out_pool_idx), _stream(stream)))
 
 
 def kpool_status_string(status: int) -> str:

@@ -15,7 +15,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libkpool.so")
 
-SOURCES = ["api.cpp", "compress.hip", "expand.hip", "fp8_quant.hip", "logits.hip", "select.hip"]
+SOURCES = ["api.cpp", "compress.hip", "decode.hip", "expand.hip", "fp8_quant.hip", "logits.hip",
+           "select.hip"]
 
 ARCH = "gfx950"
 FLAGS = [

@@ -154,6 +154,51 @@ void quantize_inputs(const Derived& d, const void* q, const void* pooled, const 
                              cuP + d.B, ws + d.off_kc, reinterpret_cast<float*>(ws + d.off_ks), st);
 }
 
+// Parameters of a decode call: num_docs = B sequences, max_seqlen bounds
+// every sequence length; total_tokens and query_chunk are not used.
+struct DecodeDerived {
+  int B, H, D, kpool, k_sel, width, max_pools, tail;
+  int64_t ld;
+  float scale;
+  size_t total;
+};
+
+kpool_status derive_decode(const kpool_params* p, DecodeDerived* d) {
+  if (!p) return fail(KPOOL_E_INVALID, "params is null");
+  d->B = p->num_docs;
+  d->H = p->num_heads;
+  d->D = p->head_dim;
+  d->kpool = p->kpool;
+  d->tail = p->always_select_tail;
+  if (d->B < 1) return fail(KPOOL_E_INVALID, "num_docs (sequences) must be >= 1 (got %d)", d->B);
+  if (p->max_seqlen < 0) return fail(KPOOL_E_INVALID, "max_seqlen must be >= 0");
+  if (d->kpool < 1 || d->kpool > 64)
+    return fail(KPOOL_E_UNSUPPORTED, "kpool must be in [1, 64] (got %d)", d->kpool);
+  if (d->D != 64 && d->D != 128)
+    return fail(KPOOL_E_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", d->D);
+  if (d->H != 4 && d->H != 8 && d->H != 16 && d->H != 32 && d->H != 64)
+    return fail(KPOOL_E_UNSUPPORTED, "num_heads must be 4, 8, 16, 32 or 64 (got %d)", d->H);
+  if (d->tail != 0 && d->tail != 1)
+    return fail(KPOOL_E_INVALID, "always_select_tail must be 0 or 1");
+  if (p->use_fp8 != 0)
+    return fail(KPOOL_E_UNSUPPORTED, "the decode entry points take BF16 q and keys (use_fp8 = 0)");
+  if (p->index_topk < d->kpool)
+    return fail(KPOOL_E_INVALID, "index_topk (%d) must be >= kpool (%d)", p->index_topk, d->kpool);
+  if (p->index_topk > (1 << 24)) return fail(KPOOL_E_UNSUPPORTED, "index_topk too large");
+  if (!(p->scale >= 0.f) || p->scale > 1e30f)
+    return fail(KPOOL_E_INVALID, "scale must be finite and >= 0 (0 = head_dim^-1/2)");
+  d->k_sel = p->index_topk / d->kpool;
+  d->width = p->index_topk + d->kpool;
+  d->max_pools = p->max_seqlen / d->kpool;
+  if (d->max_pools > kpool::kMaxSelectPools)
+    return fail(KPOOL_E_UNSUPPORTED, "max_seqlen / kpool = %d exceeds %d pools per sequence",
+                d->max_pools, kpool::kMaxSelectPools);
+  d->ld = (int64_t)round_up((size_t)std::max(d->max_pools, 1), 64);
+  d->scale = p->scale > 0.f ? p->scale : 1.0f / sqrtf((float)d->D);
+  d->total = round_up((size_t)d->B * d->ld * 4, 256);
+  return KPOOL_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -324,6 +369,76 @@ kpool_status kpool_expand(const kpool_params* p, const int32_t* pool_idx,
   (void)hipGetLastError();
   kpool::launch_expand(pool_idx, 0, d.T, cu_seqlens, cu_pools, d.B, d.T, d.kpool, d.k_sel,
                        d.width, d.tail, d.max_pools, out_token_idx, st);
+  return after_launch();
+}
+
+size_t kpool_decode_workspace_bytes(const kpool_params* p) {
+  DecodeDerived d;
+  if (derive_decode(p, &d) != KPOOL_OK) return 0;
+  return d.total;
+}
+
+kpool_status kpool_decode_topk(const kpool_params* p, const void* q, const float* w,
+                               const void* pooled, int32_t pooled_rows, const int32_t* pool_start,
+                               const int32_t* seq_lens, const int32_t* token_base,
+                               void* workspace, size_t workspace_bytes,
+                               int32_t* out_token_idx, int32_t* out_pool_idx, void* stream) {
+  DecodeDerived d;
+  CHECK(derive_decode(p, &d));
+  CHECK(check_ptr(q, 16, "q"));
+  CHECK(check_ptr(w, 4, "w"));
+  CHECK(check_ptr(pool_start, 4, "pool_start"));
+  CHECK(check_ptr(seq_lens, 4, "seq_lens"));
+  if (token_base) CHECK(check_ptr(token_base, 4, "token_base"));
+  CHECK(check_ptr(out_token_idx, 16, "out_token_idx"));
+  if (out_pool_idx) CHECK(check_ptr(out_pool_idx, 4, "out_pool_idx"));
+  if (pooled_rows < 0) return fail(KPOOL_E_INVALID, "pooled_rows must be >= 0 (got %d)", pooled_rows);
+  if (d.max_pools > 0 && pooled_rows > 0) CHECK(check_ptr(pooled, 16, "pooled"));
+  CHECK(check_ptr(workspace, 256, "workspace"));
+  if (workspace_bytes < d.total)
+    return fail(KPOOL_E_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, d.total);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  float* scores = reinterpret_cast<float*>(workspace);
+  (void)hipGetLastError();
+  kpool::DecodeLogitsArgs a{};
+  a.q = reinterpret_cast<const uint16_t*>(q);
+  a.w = w;
+  a.keys = reinterpret_cast<const uint16_t*>(pooled);
+  a.pooled_rows = pooled_rows;
+  a.pool_start = pool_start;
+  a.seq_lens = seq_lens;
+  a.B = d.B; a.H = d.H; a.D = d.D; a.kpool = d.kpool; a.max_pools = d.max_pools;
+  a.scale = d.scale;
+  a.out = scores;
+  a.ld = d.ld;
+  kpool::launch_decode_logits(a, st);
+  kpool::launch_select_decode(scores, d.ld, d.B, seq_lens, pool_start, token_base, d.kpool,
+                              d.k_sel, d.width, d.tail, d.max_pools, out_pool_idx, out_token_idx,
+                              st);
+  return after_launch();
+}
+
+kpool_status kpool_compress_pools(const kpool_params* p, const void* k, const void* gate,
+                                  const float* ape, int32_t num_pools, const int32_t* dst_rows,
+                                  int32_t pooled_rows, void* pooled, void* stream) {
+  if (!p) return fail(KPOOL_E_INVALID, "params is null");
+  const int D = p->head_dim, kp = p->kpool;
+  if (kp < 1 || kp > 64) return fail(KPOOL_E_UNSUPPORTED, "kpool must be in [1, 64] (got %d)", kp);
+  if (D != 64 && D != 128) return fail(KPOOL_E_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", D);
+  if (num_pools < 0) return fail(KPOOL_E_INVALID, "num_pools must be >= 0 (got %d)", num_pools);
+  if (pooled_rows < 0) return fail(KPOOL_E_INVALID, "pooled_rows must be >= 0 (got %d)", pooled_rows);
+  if ((int64_t)num_pools * kp > INT32_MAX) return fail(KPOOL_E_UNSUPPORTED, "too many tokens");
+  if (num_pools == 0) return ok();
+  CHECK(check_ptr(k, 16, "k"));
+  CHECK(check_ptr(gate, 16, "gate"));
+  CHECK(check_ptr(ape, 16, "ape"));
+  CHECK(check_ptr(dst_rows, 4, "dst_rows"));
+  CHECK(check_ptr(pooled, 16, "pooled"));
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  kpool::launch_compress_pools(reinterpret_cast<const uint16_t*>(k),
+                               reinterpret_cast<const uint16_t*>(gate), ape, num_pools, D, kp,
+                               dst_rows, pooled_rows, reinterpret_cast<uint16_t*>(pooled), st);
   return after_launch();
 }
 

@@ -63,12 +63,16 @@ constexpr int kFusedDocs = 1024;
 // KP = kpool when it is a compile-time constant, 0 for a runtime kpool.
 // FUSED: the workgroup derives cu_pools from cu_seqlens (B <= kFusedDocs)
 // and workgroup 0 writes it; otherwise cu_pools is an input.
-template <int D, int KP, bool FUSED>
+// SCATTER: the T tokens are T / kpool complete pools given back to back (one
+// document); pool p goes to pooled row dst_rows[p], skipped when that row is
+// outside [0, dst_cap); cu and cu_pools are not used.
+template <int D, int KP, bool FUSED, bool SCATTER = false>
 __global__ __launch_bounds__(256) void compress_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ gate,
     const float* __restrict__ ape, const int32_t* __restrict__ cu,
     int32_t* __restrict__ cu_pools, int B, int T, int kpool_rt,
-    uint16_t* __restrict__ pooled) {
+    uint16_t* __restrict__ pooled, const int32_t* __restrict__ dst_rows = nullptr,
+    int dst_cap = 0) {
   constexpr int TPP = D / 8;                  // threads per pool
   constexpr int PPB = 256 / TPP;              // pools per workgroup
   const int kpool = KP > 0 ? KP : kpool_rt;
@@ -168,6 +172,14 @@ __global__ __launch_bounds__(256) void compress_kernel(
     *reinterpret_cast<uint4*>(pooled + (size_t)p * D + d0) =
         make_uint4(outw[0], outw[1], outw[2], outw[3]);
   };
+  if constexpr (SCATTER) {
+    const int p = blockIdx.x * PPB + tid / TPP;
+    if (p >= pool_cap) return;
+    const int row = dst_rows[p];
+    if (row < 0 || row >= dst_cap) return;
+    pool_body(row, p * kpool);
+    return;
+  }
   if (FUSED && B == 1) {
     // one document: cu = {0, T} by the interface's precondition, so pool p
     // starts at token p kpool and nothing has to be read before the slices
@@ -270,6 +282,30 @@ void launch_compress(const uint16_t* k, const uint16_t* gate, const float* ape,
     if (fused) launch_compress_df<64, true>(k, gate, ape, cu, cu_pools, B, T, kpool, pooled, st);
     else launch_compress_df<64, false>(k, gate, ape, cu, cu_pools, B, T, kpool, pooled, st);
   }
+}
+
+void launch_compress_pools(const uint16_t* k, const uint16_t* gate, const float* ape, int N,
+                           int D, int kpool, const int32_t* dst_rows, int dst_cap,
+                           uint16_t* pooled, hipStream_t st) {
+  if (N <= 0) return;
+  const int T = N * kpool;
+  const int ppb = 256 / (D / 8);
+  const dim3 grid((N + ppb - 1) / ppb), block(256);
+#define KP_S(DV, KPV)                                                                          \
+  compress_kernel<DV, KPV, true, true><<<grid, block, 0, st>>>(k, gate, ape, nullptr, nullptr, \
+                                                                1, T, kpool, pooled, dst_rows,  \
+                                                                dst_cap)
+#define KP_SD(DV)                   \
+  switch (kpool) {                  \
+    case 1: KP_S(DV, 1); break;     \
+    case 2: KP_S(DV, 2); break;     \
+    case 4: KP_S(DV, 4); break;     \
+    case 8: KP_S(DV, 8); break;     \
+    default: KP_S(DV, 0); break;    \
+  }
+  if (D == 128) { KP_SD(128) } else { KP_SD(64) }
+#undef KP_SD
+#undef KP_S
 }
 
 }  // namespace kpool

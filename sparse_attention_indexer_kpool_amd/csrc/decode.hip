@@ -1,0 +1,147 @@
+// Decode step of the KPool indexer: one new query per sequence, scored against
+// that sequence's cached pooled keys.
+//
+// Megatron-LM PR #7054, section "3. KPool DSA indexer + NoPE": the indexer
+// scores pools, keeps index_topk // kpool of them and expands them to tokens,
+// always adding the query's incomplete pool; the same section and section "4.
+// DSA indexer FP8 precision split" place that indexer in serving, where a
+// sequence grows one token per step and its pooled keys are kept in a cache.
+// The query of a sequence of L tokens is its token L - 1, so its causal pools
+// are the floor(L / kpool) complete pools of the cache and its tail the last
+// L mod kpool tokens: the row the prefill indexer computes for that token.
+//
+//   score[b, j] = sum_h w[b, h] * ReLU(scale * q[b, h, :] . pooled[start_b + j, :])
+//
+// HBM-bound: every causal pooled key of every sequence is read once (2 D bytes
+// per pool); the arithmetic is 2 H D FLOP per pool, a few percent of what the
+// matrix cores could do in that time. Still a contraction, so it runs on
+// v_mfma_f32_32x32x16_bf16: the A operand is the sequence's H head rows of q
+// (zero rows up to a multiple of 32), held in registers; the B operand is a
+// block of 32 keys, each lane reading one contiguous half of a key row (the
+// K index is permuted identically for A and B, as in the prefill kernel,
+// which leaves every dot product unchanged). The epilogue multiplies each
+// lane's 16 head rows by w' = w * scale, clamps at 0, sums them and adds the
+// other half-wave's 16 rows.
+
+#include "kpool_device.h"
+#include "kpool_internal.h"
+
+namespace kpool {
+
+constexpr int kDecWaves = 4;                       // waves per workgroup
+constexpr int kDecBlocksPerWave = 4;               // 32-pool blocks per wave
+constexpr int kDecPoolsPerGroup = 32 * kDecWaves * kDecBlocksPerWave;   // 512
+
+template <int H, int D>
+__global__ __launch_bounds__(64 * kDecWaves) void decode_logits_kernel(DecodeLogitsArgs a) {
+  constexpr int MT = H > 32 ? H / 32 : 1;          // 32-row tiles of heads
+  constexpr int NSTEP = D / 16;                    // MFMAs per 32 x 32 tile
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int b = (int)blockIdx.x / a.pieces;
+  const int piece = (int)blockIdx.x % a.pieces;
+  const int L = max(a.seq_lens[b], 0);
+  const int n_c = min(L / a.kpool, a.max_pools);
+  const int p_lo = piece * kDecPoolsPerGroup + 32 * wid;   // this wave's first pool
+  if (p_lo >= n_c) return;                         // nothing for this wave (no barrier below)
+  const int n = lane & 31, g = lane >> 5;
+  const int pool0 = a.pool_start[b];
+
+  // A: head rows of q[b]; lane (n, g) holds row n of each tile at dims
+  // g D/2 + 8 s .. + 7 for step s
+  bf16x8_t afrag[MT][NSTEP];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int head = mt * 32 + n;
+    const uint16_t* qrow = a.q + ((size_t)b * H + (head < H ? head : 0)) * D + g * (D / 2);
+#pragma unroll
+    for (int s = 0; s < NSTEP; ++s) {
+      const uint4 v = head < H ? *reinterpret_cast<const uint4*>(qrow + 8 * s) : make_uint4(0, 0, 0, 0);
+      afrag[mt][s] = __builtin_bit_cast(bf16x8_t, v);
+    }
+  }
+  // w' of this lane's accumulator rows: element v of a 32 x 32 accumulator is
+  // row 8 (v / 4) + 4 g + (v mod 4)
+  float wq[MT][16];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int head = mt * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
+      wq[mt][v] = head < H ? a.w[(size_t)b * H + head] * a.scale : 0.f;
+    }
+
+  // B of block i: key row p_lo + 32 kDecWaves i + n, clamped into the causal
+  // range (clamped columns are never stored) and into the cache
+  auto load_b = [&](int i, uint4 (&bf)[NSTEP]) {
+    const int p = min(p_lo + 32 * kDecWaves * i + n, n_c - 1);
+    const int row = clampi(pool0 + p, 0, a.pooled_rows - 1);
+    const uint16_t* krow = a.keys + (size_t)row * D + g * (D / 2);
+#pragma unroll
+    for (int s = 0; s < NSTEP; ++s) bf[s] = *reinterpret_cast<const uint4*>(krow + 8 * s);
+  };
+  float* __restrict__ out = a.out + (size_t)b * a.ld;
+  uint4 bfr[2][NSTEP];
+  load_b(0, bfr[0]);
+#pragma unroll
+  for (int i = 0; i < kDecBlocksPerWave; ++i) {
+    const int c0 = p_lo + 32 * kDecWaves * i;      // first column of block i
+    if (c0 >= n_c) break;
+    // the next block's keys are requested before this block's MFMAs; the
+    // memory clobber and the scheduling barrier keep those loads here
+    if (i + 1 < kDecBlocksPerWave && c0 + 32 * kDecWaves < n_c) load_b(i + 1, bfr[(i + 1) & 1]);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    f32x16_t acc[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[mt][v] = 0.f;
+#pragma unroll
+    for (int s = 0; s < NSTEP; ++s) {
+      const bf16x8_t bf = __builtin_bit_cast(bf16x8_t, bfr[i & 1][s]);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afrag[mt][s], bf, acc[mt], 0, 0, 0);
+    }
+    // w' * ReLU over this lane's head rows (ReLU as an integer max: FP32
+    // values of either sign order like their bit patterns against +0)
+    float sum = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        sum += wq[mt][v] * __int_as_float(max(__float_as_int(acc[mt][v]), 0));
+    // add the other half-wave's rows of the same column
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(sum), __float_as_uint(sum),
+                                                     false, false);
+    const float score = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    if (g == 0 && c0 + n < n_c) out[c0 + n] = score;
+  }
+}
+
+template <int H, int D>
+static void launch_hd(const DecodeLogitsArgs& a0, hipStream_t st) {
+  DecodeLogitsArgs a = a0;
+  a.pieces = (a.max_pools + kDecPoolsPerGroup - 1) / kDecPoolsPerGroup;
+  if (a.pieces < 1) a.pieces = 1;
+  decode_logits_kernel<H, D><<<a.B * a.pieces, 64 * kDecWaves, 0, st>>>(a);
+}
+
+template <int D>
+static void launch_d(const DecodeLogitsArgs& a, hipStream_t st) {
+  switch (a.H) {
+    case 4: launch_hd<4, D>(a, st); break;
+    case 8: launch_hd<8, D>(a, st); break;
+    case 16: launch_hd<16, D>(a, st); break;
+    case 32: launch_hd<32, D>(a, st); break;
+    default: launch_hd<64, D>(a, st); break;
+  }
+}
+
+void launch_decode_logits(const DecodeLogitsArgs& a, hipStream_t st) {
+  if (a.B <= 0 || a.max_pools <= 0 || a.pooled_rows <= 0) return;
+  if (a.D == 128) launch_d<128>(a, st);
+  else launch_d<64>(a, st);
+}
+
+}  // namespace kpool

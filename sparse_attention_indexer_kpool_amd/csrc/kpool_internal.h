@@ -50,6 +50,39 @@ void launch_expand(const int32_t* pool_ids, int q_begin, int q_end, const int32_
                    const int32_t* cu_pools, int B, int T, int kpool, int k_sel, int width,
                    int tail, int max_pools, int32_t* out, hipStream_t st);
 
+// Decode: one query per sequence b (its token seq_lens[b] - 1) against the
+// sequence's floor(seq_lens[b] / kpool) cached pools at pooled rows
+// pool_start[b] ...; scores to out [B, ld].
+struct DecodeLogitsArgs {
+  const uint16_t* q;           // BF16 [B, H, D]
+  const float* w;              // FP32 [B, H]
+  const uint16_t* keys;        // BF16 pooled rows [pooled_rows, D]
+  int pooled_rows;             // reads are clamped into this many rows
+  const int32_t* pool_start;   // [B]
+  const int32_t* seq_lens;     // [B]
+  int B, H, D, kpool, max_pools;
+  float scale;
+  float* out;                  // FP32 [B, ld]
+  int64_t ld;
+  int pieces;                  // set by the launcher
+};
+void launch_decode_logits(const DecodeLogitsArgs& a, hipStream_t st);
+
+// Selection + expansion of decode rows: row r is the query of sequence r
+// (length seq_lens[r], pools at pool_start[r], token ids from token_base[r],
+// or 0 when token_base is null).
+void launch_select_decode(const float* scores, int64_t ld, int B, const int32_t* seq_lens,
+                          const int32_t* pool_start, const int32_t* token_base, int kpool,
+                          int k_sel, int width, int tail_on, int max_pools, int32_t* out_ids,
+                          int32_t* out_tok, hipStream_t st);
+
+// Compression of N complete pools given their slot tokens: pool n is tokens
+// n kpool .. n kpool + kpool - 1 of k / gate, written to pooled row
+// dst_rows[n] (rows outside [0, dst_cap) are skipped).
+void launch_compress_pools(const uint16_t* k, const uint16_t* gate, const float* ape, int N,
+                           int D, int kpool, const int32_t* dst_rows, int dst_cap,
+                           uint16_t* pooled, hipStream_t st);
+
 // Largest max_pools the selection kernel handles (its LDS bitmap has one bit
 // per pool of a row).
 constexpr int kMaxSelectPools = 65536;

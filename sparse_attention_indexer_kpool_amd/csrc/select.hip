@@ -126,7 +126,25 @@ struct SelectArgs {
   int B, T, kpool, k_sel, width, tail_on, max_pools, list_cap;
   int32_t* out_ids;     // [rows, K_sel] global pool ids, or null
   int32_t* out_tok;     // [rows, width] token ids with the tail, or null
+  // decode rows (dec_len not null): row r is the last token of a sequence of
+  // dec_len[r] tokens whose pools start at row dec_pool0[r] and whose token
+  // ids start at dec_base[r] (0 when dec_base is null)
+  const int32_t* dec_len;
+  const int32_t* dec_pool0;
+  const int32_t* dec_base;
 };
+
+// Row facts of decode row r, in the form query_info gives a prefill row.
+__device__ __forceinline__ QueryInfo decode_info(const SelectArgs& a, int r) {
+  QueryInfo qi;
+  const int L = max(a.dec_len[r], 0);
+  qi.doc = r;
+  qi.start = a.dec_base ? a.dec_base[r] : 0;
+  qi.pool0 = a.dec_pool0[r];
+  qi.i = L - 1;
+  qi.n_c = min(L / a.kpool, a.max_pools);
+  return qi;
+}
 
 template <int NT, int G, bool VEC4>
 __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
@@ -145,7 +163,8 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
   const int r = blockIdx.x;
   const int t = a.q_begin + r;
   if (t >= a.q_end) return;
-  const QueryInfo qi = query_info(a.cu, a.cu_pools, a.B, a.T, kpool, a.max_pools, t);
+  const QueryInfo qi = a.dec_len ? decode_info(a, r)
+                                 : query_info(a.cu, a.cu_pools, a.B, a.T, kpool, a.max_pools, t);
   const int n_c = qi.n_c;
   const int n_sel = n_c < k_sel ? n_c : k_sel;
   const int tail = a.tail_on ? (qi.i + 1) % kpool : 0;
@@ -571,12 +590,26 @@ static void launch_sel(SelectArgs a, hipStream_t st) {
     select_kernel<NT, G, false><<<a.q_end - a.q_begin, NT, lds, st>>>(a);
 }
 
+static void launch_select_args(SelectArgs& a, hipStream_t st) {
+  const int max_pools = a.max_pools;
+  if (max_pools <= 1024) launch_sel<256, 1>(a, st);
+  else if (max_pools <= 2048) launch_sel<256, 2>(a, st);
+  else if (max_pools <= 4096) launch_sel<256, 4>(a, st);
+  else if (max_pools <= 8192) launch_sel<256, 8>(a, st);
+  else if (max_pools <= 10240) launch_sel<256, 10>(a, st);
+  else if (max_pools <= 12288) launch_sel<256, 12>(a, st);
+  else if (max_pools <= 14336) launch_sel<256, 14>(a, st);
+  else if (max_pools <= 16384) launch_sel<256, 16>(a, st);
+  else if (max_pools <= 32768) launch_sel<512, 16>(a, st);
+  else launch_sel<1024, 16>(a, st);
+}
+
 void launch_select(const float* logits, int64_t ld, int q_begin, int q_end,
                    const int32_t* cu, const int32_t* cu_pools, int B, int T, int kpool,
                    int k_sel, int width, int tail_on, int max_pools, int32_t* out_ids,
                    int32_t* out_tok, hipStream_t st) {
   if (q_end <= q_begin) return;
-  SelectArgs a;
+  SelectArgs a{};
   a.logits = logits;
   a.ld = ld;
   a.q_begin = q_begin;
@@ -597,16 +630,31 @@ void launch_select(const float* logits, int64_t ld, int q_begin, int q_end,
   a.max_pools = max_pools;
   a.out_ids = out_ids;
   a.out_tok = out_tok;
-  if (max_pools <= 1024) launch_sel<256, 1>(a, st);
-  else if (max_pools <= 2048) launch_sel<256, 2>(a, st);
-  else if (max_pools <= 4096) launch_sel<256, 4>(a, st);
-  else if (max_pools <= 8192) launch_sel<256, 8>(a, st);
-  else if (max_pools <= 10240) launch_sel<256, 10>(a, st);
-  else if (max_pools <= 12288) launch_sel<256, 12>(a, st);
-  else if (max_pools <= 14336) launch_sel<256, 14>(a, st);
-  else if (max_pools <= 16384) launch_sel<256, 16>(a, st);
-  else if (max_pools <= 32768) launch_sel<512, 16>(a, st);
-  else launch_sel<1024, 16>(a, st);
+  launch_select_args(a, st);
+}
+
+void launch_select_decode(const float* scores, int64_t ld, int B, const int32_t* seq_lens,
+                          const int32_t* pool_start, const int32_t* token_base, int kpool,
+                          int k_sel, int width, int tail_on, int max_pools, int32_t* out_ids,
+                          int32_t* out_tok, hipStream_t st) {
+  if (B <= 0) return;
+  SelectArgs a{};
+  a.logits = scores;
+  a.ld = ld;
+  a.q_begin = 0;
+  a.q_end = B;
+  a.B = B;
+  a.kpool = kpool;
+  a.k_sel = k_sel;
+  a.width = width;
+  a.tail_on = tail_on;
+  a.max_pools = max_pools < 1 ? 1 : max_pools;
+  a.out_ids = out_ids;
+  a.out_tok = out_tok;
+  a.dec_len = seq_lens;
+  a.dec_pool0 = pool_start;
+  a.dec_base = token_base;
+  launch_select_args(a, st);
 }
 
 }  // namespace kpool

@@ -569,4 +569,47 @@ def pin_fp8_end_to_end_library(o):
     assert changed > 0
 
 
+def pin_decode_is_last_token_row(o):
+    """Serving: the decode row of a sequence of L tokens equals the prefill
+    row of the last token of a document of L tokens, with the sequence's
+    pools anywhere in a shared cache (pool ids offset by its start) and its
+    token ids offset by its base; L = 0 gives a row of -1. Lengths cross
+    every case: no pool, fewer pools than K_sel, more, ragged tails; kpool
+    1, 3, 4; tail on and off."""
+    H, D = 3, 8
+    lens = [0, 1, 3, 4, 5, 37, 64, 90, 23]
+    for kp in (1, 3, 4):
+        for tail in (True, False):
+            topk = 4 * kp
+            B = len(lens)
+            q_rows, w_rows, cache, starts, per_doc = [], [], [], [], []
+            cursor = 5                                    # the cache starts with unrelated rows
+            cache.append(rnd((5, D), 950).astype(F32))
+            for b, L in enumerate(lens):
+                q, k, gate, w, ape, cu = _tiny_case(900 + 10 * b + kp, [max(L, 1)], H, D, kp)
+                pb, _ = o.compress(k[:L], gate[:L], ape, [0, L], kp)
+                starts.append(cursor)
+                cache.append(pb)
+                cursor += len(pb)
+                cache.append(rnd((2, D), 960 + b).astype(F32))   # a gap between sequences
+                cursor += 2
+                q_rows.append(q[max(L, 1) - 1])
+                w_rows.append(w[max(L, 1) - 1])
+                if L > 0:
+                    tok, pid = o.indexer_topk(q[:L], w[:L], pb, [0, L], kp, topk, tail,
+                                              rows=[L - 1])
+                else:
+                    tok = np.full((1, topk + kp), -1, np.int32)
+                    pid = np.full((1, topk // kp), -1, np.int32)
+                per_doc.append((tok[0], pid[0]))
+            pooled = np.concatenate(cache).astype(F32)
+            base = [1000 * b + 7 for b in range(B)]
+            dtok, dpid = o.decode_topk(np.stack(q_rows), np.stack(w_rows), pooled, starts, lens,
+                                       kp, topk, tail, token_base=base)
+            for b in range(B):
+                tok, pid = per_doc[b]
+                assert np.array_equal(dtok[b], np.where(tok >= 0, tok + base[b], -1)), (kp, tail, b)
+                assert np.array_equal(dpid[b], np.where(pid >= 0, pid + starts[b], -1)), (kp, tail, b)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -128,6 +128,55 @@ def make_inputs(wl: Workload, seed: Optional[int] = None) -> Inputs:
                   doc_lengths=lengths)
 
 
+@dataclass
+class DecodeInputs:
+    """CPU tensors of one serving (decode) step: B sequences, one query each,
+    their complete pools in a shared cache of pooled rows."""
+    q: torch.Tensor           # bf16 [B, H, D]
+    w: torch.Tensor           # f32  [B, H]
+    pooled: torch.Tensor      # bf16 [rows, D]: the cache
+    pool_start: torch.Tensor  # int32 [B]: first cache row of each sequence
+    seq_lens: torch.Tensor    # int32 [B]: tokens of each sequence so far
+    token_base: torch.Tensor  # int32 [B]: id of each sequence's token 0
+    kpool: int
+
+    @property
+    def B(self) -> int:
+        return int(self.q.shape[0])
+
+
+def make_decode_inputs(seq_lens, H: int, D: int, kpool: int, seed: int = 0, gap: int = 3,
+                       heavy_frac: float = 0.05) -> DecodeInputs:
+    """Seeded decode inputs. q ~ N(0, 1), w ~ N(0, 1) / sqrt(H); the cache
+    holds `gap` unrelated rows before each sequence's floor(L / kpool) rows,
+    all ~ N(0, 1), with heavy_frac of them scaled by 4 (heavy-tailed scores,
+    as in the long prefill workloads). Token ids are laid out as in a packed
+    batch (token_base = running sum of the lengths)."""
+    g = torch.Generator().manual_seed(seed)
+    lens = [int(x) for x in seq_lens]
+    B = len(lens)
+    starts, cursor = [], 0
+    for L in lens:
+        cursor += gap
+        starts.append(cursor)
+        cursor += L // kpool
+    rows = cursor + gap
+    q = torch.randn(B, H, D, generator=g)
+    w = torch.randn(B, H, generator=g) / math.sqrt(H)
+    pooled = torch.randn(rows, D, generator=g)
+    if heavy_frac > 0 and rows > 0:
+        heavy = torch.randperm(rows, generator=g)[: int(round(heavy_frac * rows))]
+        pooled[heavy] *= 4.0
+    base = [0]
+    for L in lens[:-1]:
+        base.append(base[-1] + L)
+    return DecodeInputs(q=q.to(torch.bfloat16), w=w.to(torch.float32).contiguous(),
+                        pooled=pooled.to(torch.bfloat16),
+                        pool_start=torch.tensor(starts, dtype=torch.int32),
+                        seq_lens=torch.tensor(lens, dtype=torch.int32),
+                        token_base=torch.tensor(base, dtype=torch.int32), kpool=kpool)
+
+
 def custom(name="custom", **kw) -> Workload:
     """A workload with explicit fields (tests use this for small cases)."""
     return replace(Workload(name), **kw)
