@@ -215,6 +215,32 @@ def cpu_baseline(inp: wlm.Inputs, n_rows: int):
                       f"NumPy FP32 on {os.cpu_count()} host CPUs"}
 
 
+def decode_bench(reps: int, B: int = 64, L: int = 65536):
+    """The serving step: kpool_decode_topk for B sequences of L tokens each
+    (one query per sequence over L / 4 cached pooled keys), H = 32, D = 128,
+    kpool = 4, index_topk = 2048. Returns the JSON object of its line."""
+    import sparse_attention_indexer_kpool_amd as kp
+    H, D, KP, TOPK = 32, 128, 4, 2048
+    di = wlm.make_decode_inputs([L] * B, H, D, KP, seed=7)
+    p = kp.Params(num_docs=B, total_tokens=0, max_seqlen=L, num_heads=H, head_dim=D, kpool=KP,
+                  index_topk=TOPK, always_select_tail=1)
+    dev = "cuda:0"
+    q, w, pooled = di.q.to(dev), di.w.to(dev), di.pooled.to(dev)
+    ps, sl, tb = di.pool_start.to(dev), di.seq_lens.to(dev), di.token_base.to(dev)
+    ws = torch.empty(kp.kpool_decode_workspace_bytes(p), dtype=torch.uint8, device=dev)
+    tok = torch.empty(B, p.width, dtype=torch.int32, device=dev)
+    run = lambda: kp.kpool_decode_topk(p, q, w, pooled, ps, sl, ws, tok, token_base=tb)
+    ms = time_region(run, reps, warm=2)
+    n_c = L // KP
+    by = B * n_c * (2 * D + 4 + 4) + B * H * (2 * D + 4) + 4 * B * p.width
+    return {"workload": f"decode_B{B}_L{L}_H{H}_D{D}", "ms": round(ms, 4),
+            "queries_per_s": round(B / (ms * 1e-3), 1),
+            "hbm": {"bytes": by, "GB/s": round(by / (ms * 1e-3) / 1e9, 1),
+                    "frac": round(by / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+            "note": "keys read once (2 D bytes per pool), scores written and read once, "
+                    "token rows written"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -223,6 +249,8 @@ def main():
     ap.add_argument("--workload", default="long_T65536_H32_D128")
     ap.add_argument("--cpu-rows", type=int, default=12288)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip the serving-step measurement (kpool_decode_topk)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after the bench, run 3 device copies of this many MiB (a kernel of "
                          "known traffic that calibrates the HBM byte counters of a profiler)")
@@ -323,6 +351,9 @@ def main():
         out["phases_hbm"]["fp8_quant"] = {
             "bytes": by_fp8, "GB/s": gbs(by_fp8, ms_fp8),
             "frac": round(by_fp8 / (ms_fp8 * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    if not args.no_decode and wl.name == "long_T65536_H32_D128":
+        log("decode step, 64 sequences of 64K tokens")
+        out["decode"] = decode_bench(reps)
     if rank == 0 and not args.no_cpu_baseline:
         log(f"cpu baseline on {args.cpu_rows} rows")
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_rows)

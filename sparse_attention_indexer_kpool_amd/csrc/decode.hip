@@ -17,9 +17,8 @@
 // matrix cores could do in that time. Still a contraction, so it runs on
 // v_mfma_f32_32x32x16_bf16: the A operand is the sequence's H head rows of q
 // (zero rows up to a multiple of 32), held in registers; the B operand is a
-// block of 32 keys, each lane reading one contiguous half of a key row (the
-// K index is permuted identically for A and B, as in the prefill kernel,
-// which leaves every dot product unchanged). The epilogue multiplies each
+// block of 32 keys, each lane pair reading 32 adjacent bytes of a key row
+// per step. The epilogue multiplies each
 // lane's 16 head rows by w' = w * scale, clamps at 0, sums them and adds the
 // other half-wave's 16 rows.
 
@@ -31,6 +30,14 @@ namespace kpool {
 constexpr int kDecWaves = 4;                       // waves per workgroup
 constexpr int kDecBlocksPerWave = 4;               // 32-pool blocks per wave
 constexpr int kDecPoolsPerGroup = 32 * kDecWaves * kDecBlocksPerWave;   // 512
+
+// Dims of MFMA step s held by lane half g (the same map for A and B, so the
+// dot products are whatever order K is taken in): step s covers dims 16 s ..
+// 16 s + 15, so the two lanes of a pair read 32 adjacent bytes of a row and
+// one load instruction touches 32 rows' cache lines. (Giving each lane one
+// contiguous half of the row instead touches 64 lines per instruction:
+// 229 against 212 us for 256 sequences of 64K tokens.)
+#define KOFF(s, g) (16 * (s) + 8 * (g))
 
 template <int H, int D>
 __global__ __launch_bounds__(64 * kDecWaves) void decode_logits_kernel(DecodeLogitsArgs a) {
@@ -47,15 +54,15 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_logits_kernel(DecodeLog
   const int pool0 = a.pool_start[b];
 
   // A: head rows of q[b]; lane (n, g) holds row n of each tile at dims
-  // g D/2 + 8 s .. + 7 for step s
+  // KOFF(s, g) .. + 7 for step s
   bf16x8_t afrag[MT][NSTEP];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int head = mt * 32 + n;
-    const uint16_t* qrow = a.q + ((size_t)b * H + (head < H ? head : 0)) * D + g * (D / 2);
+    const uint16_t* qrow = a.q + ((size_t)b * H + (head < H ? head : 0)) * D;
 #pragma unroll
     for (int s = 0; s < NSTEP; ++s) {
-      const uint4 v = head < H ? *reinterpret_cast<const uint4*>(qrow + 8 * s) : make_uint4(0, 0, 0, 0);
+      const uint4 v = head < H ? *reinterpret_cast<const uint4*>(qrow + KOFF(s, g)) : make_uint4(0, 0, 0, 0);
       afrag[mt][s] = __builtin_bit_cast(bf16x8_t, v);
     }
   }
@@ -75,9 +82,9 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_logits_kernel(DecodeLog
   auto load_b = [&](int i, uint4 (&bf)[NSTEP]) {
     const int p = min(p_lo + 32 * kDecWaves * i + n, n_c - 1);
     const int row = clampi(pool0 + p, 0, a.pooled_rows - 1);
-    const uint16_t* krow = a.keys + (size_t)row * D + g * (D / 2);
+    const uint16_t* krow = a.keys + (size_t)row * D;
 #pragma unroll
-    for (int s = 0; s < NSTEP; ++s) bf[s] = *reinterpret_cast<const uint4*>(krow + 8 * s);
+    for (int s = 0; s < NSTEP; ++s) bf[s] = *reinterpret_cast<const uint4*>(krow + KOFF(s, g));
   };
   float* __restrict__ out = a.out + (size_t)b * a.ld;
   uint4 bfr[2][NSTEP];
