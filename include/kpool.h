@@ -194,26 +194,34 @@ kpool_status kpool_fp8_quantize(const void* x, int32_t rows, uint8_t* codes,
 
 /* ---- Serving: one query per sequence, pooled keys kept in a cache -------
  * ([MLM] sections 3 and 4: the indexer of the serving path scores pools of
- * keys compressed as tokens arrive.) A sequence of L tokens holds its
- * floor(L / kpool) complete pools in the caller's cache of pooled rows; its
- * query is its token L - 1, whose indexer row is the one kpool_indexer_topk
- * computes for the last token of a document of L tokens.
+ * keys compressed as tokens arrive, with an FP8 key store.) A sequence of L
+ * tokens holds its floor(L / kpool) complete pools in the caller's cache of
+ * pooled rows; its query is its token L - 1, whose indexer row is the one
+ * kpool_indexer_topk computes for the last token of a document of L tokens.
+ * The cache holds BF16 rows [pooled_rows, D], or with use_fp8 the E4M3 codes
+ * [pooled_rows, 128] (uint8) and power-of-two scales [pooled_rows] (FP32)
+ * that kpool_fp8_quantize gives the BF16 rows.
  *
  * kpool_compress_pools: step 1 for pools that have just completed, given by
  * their slot tokens. Pool n of the call is tokens n*kpool .. n*kpool+kpool-1
  * of k and gate; its pooled key (the same arithmetic as kpool_compress) goes
- * to row dst_rows[n] of pooled; rows outside [0, pooled_rows) are skipped.
+ * to row dst_rows[n] of the cache (with use_fp8: its codes and scale, the
+ * FP8 input path applied to the BF16 pooled row); rows outside
+ * [0, pooled_rows) are skipped.
  *   k, gate    BF16 [num_pools * kpool, D]
  *   ape        FP32 [kpool, D]
  *   dst_rows   int32 [num_pools]
- *   pooled     BF16 [pooled_rows, D], rows dst_rows[n] written
- * Uses params: head_dim, kpool. */
+ *   pooled     BF16 [pooled_rows, D], or uint8 codes [pooled_rows, 128]
+ *   pooled_scale  FP32 [pooled_rows] with use_fp8, else ignored (may be NULL)
+ * Uses params: head_dim, kpool, use_fp8 (which needs head_dim == 128). */
 kpool_status kpool_compress_pools(const kpool_params* p, const void* k, const void* gate,
                                   const float* ape, int32_t num_pools, const int32_t* dst_rows,
-                                  int32_t pooled_rows, void* pooled, void* stream);
+                                  int32_t pooled_rows, void* pooled, float* pooled_scale,
+                                  void* stream);
 
 /* Bytes of workspace kpool_decode_topk needs (0 for invalid parameters):
- * the scores of every sequence, B rows of kpool_logits_ld floats. */
+ * the scores of every sequence, B rows of kpool_logits_ld floats, and with
+ * use_fp8 the codes and scales of the B H query rows. */
 size_t kpool_decode_workspace_bytes(const kpool_params* p);
 
 /* Steps 2-4 for B = num_docs sequences, one query each. Sequence b has
@@ -228,19 +236,25 @@ size_t kpool_decode_workspace_bytes(const kpool_params* p);
  *   always_select_tail); then -1 to width W.
  *   q           BF16 [B, H, D]
  *   w           FP32 [B, H]
- *   pooled      BF16 [pooled_rows, D]: the cache (reads are kept inside it;
- *               the rows named above must lie in it for a meaningful result)
+ *   pooled      the cache, BF16 [pooled_rows, D] or (use_fp8) E4M3 codes
+ *               [pooled_rows, 128]; reads are kept inside it, and the rows
+ *               named above must lie in it for a meaningful result
+ *   pooled_scale  FP32 [pooled_rows] with use_fp8 (may be NULL otherwise)
  *   pool_start, seq_lens  int32 [B];  token_base  int32 [B] or NULL
  *   workspace   at least kpool_decode_workspace_bytes(p) bytes, 256-byte aligned
  *   out_token_idx  out int32 [B, W];  out_pool_idx  out int32 [B, K_sel]
  *               (may be NULL): pool_start[b] + j, ascending, -1 pad
+ * With use_fp8 the q rows (b, h) go through the FP8 input path (into the
+ * workspace) and are scored from their codes against the cached key codes,
+ * as kpool_indexer_topk's FP8 path scores them.
  * Uses params: num_docs (= B), max_seqlen (a bound on every L_b), num_heads,
- * head_dim, kpool, index_topk, always_select_tail, scale; use_fp8 must be 0
- * (KPOOL_E_UNSUPPORTED otherwise); total_tokens and query_chunk are not used.
+ * head_dim, kpool, index_topk, always_select_tail, use_fp8 (head_dim 128),
+ * scale; total_tokens and query_chunk are not used.
  * Lengths above max_seqlen are scored over their first floor(max_seqlen /
  * kpool) pools. */
 kpool_status kpool_decode_topk(const kpool_params* p, const void* q, const float* w,
-                               const void* pooled, int32_t pooled_rows, const int32_t* pool_start,
+                               const void* pooled, int32_t pooled_rows,
+                               const float* pooled_scale, const int32_t* pool_start,
                                const int32_t* seq_lens, const int32_t* token_base,
                                void* workspace, size_t workspace_bytes,
                                int32_t* out_token_idx, int32_t* out_pool_idx, void* stream);

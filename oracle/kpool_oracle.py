@@ -341,14 +341,16 @@ def indexer_topk(q, w, pooled, cu_seqlens, kpool: int, index_topk: int,
 # ---------------------------------------------------------------------------
 
 def decode_topk(q, w, pooled, pool_start, seq_lens, kpool: int, index_topk: int,
-                tail_on: bool, scale: float = 0.0, token_base=None):
+                tail_on: bool, scale: float = 0.0, token_base=None, fp8: bool = False):
     """Token rows [B, index_topk + kpool] and pool ids [B, index_topk //
     kpool] for B sequences, one query each: sequence b has L_b = seq_lens[b]
     tokens, its query is token L_b - 1, and its floor(L_b / kpool) complete
     pools are pooled rows pool_start[b] onwards. Row b is the row
     indexer_topk gives the last token of a document of L_b tokens (pool ids
     offset by pool_start[b], token ids by token_base[b]); L_b = 0 gives a row
-    of -1. q: [B, H, D]; w: [B, H] FP32; pooled: [P, D] (BF16 values)."""
+    of -1. q: [B, H, D]; w: [B, H] FP32; pooled: [P, D] (BF16 values). With
+    fp8, q rows (b, h) and the pooled rows are replaced by their dequantised
+    FP8 values before scoring, as in indexer_topk."""
     q = np.asarray(q, dtype=F32)
     w = np.asarray(w, dtype=F32)
     pooled = np.asarray(pooled, dtype=F32)
@@ -366,7 +368,11 @@ def decode_topk(q, w, pooled, pool_start, seq_lens, kpool: int, index_topk: int,
         base = 0 if token_base is None else int(token_base[b])
         n_c = causal_pools(L - 1, kpool)
         keys = pooled[int(pool_start[b]):int(pool_start[b]) + n_c]
-        chosen = select_pools(row_scores(q[b], w[b], keys, scale), k_sel)
+        q_b = q[b]
+        if fp8:
+            _, _, keys = fp8_quantize_rows(keys)
+            _, _, q_b = fp8_quantize_rows(q_b)
+        chosen = select_pools(row_scores(q_b, w[b], keys, scale), k_sel)
         pid[b, :len(chosen)] = chosen + int(pool_start[b])
         # the expansion of the last token of a one-document batch [0, L)
         row = expand_row(L - 1, [0, L], [0, L // kpool], chosen, kpool, index_topk, tail_on)

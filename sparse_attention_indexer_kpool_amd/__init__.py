@@ -107,11 +107,11 @@ def lib() -> ctypes.CDLL:
         L.kpool_fp8_quantize.restype = ctypes.c_int
         L.kpool_fp8_quantize.argtypes = [vp, i32, vp, vp, vp]
         L.kpool_compress_pools.restype = ctypes.c_int
-        L.kpool_compress_pools.argtypes = [P, vp, vp, vp, i32, vp, i32, vp, vp]
+        L.kpool_compress_pools.argtypes = [P, vp, vp, vp, i32, vp, i32, vp, vp, vp]
         L.kpool_decode_workspace_bytes.restype = sz
         L.kpool_decode_workspace_bytes.argtypes = [P]
         L.kpool_decode_topk.restype = ctypes.c_int
-        L.kpool_decode_topk.argtypes = [P, vp, vp, vp, i32, vp, vp, vp, vp, sz, vp, vp, vp]
+        L.kpool_decode_topk.argtypes = [P, vp, vp, vp, i32, vp, vp, vp, vp, vp, sz, vp, vp, vp]
         L.kpool_status_string.restype = ctypes.c_char_p
         L.kpool_status_string.argtypes = [ctypes.c_int]
         L.kpool_last_error.restype = ctypes.c_char_p
@@ -214,10 +214,10 @@ def kpool_fp8_quantize(x, rows, codes, row_scale, stream=None) -> None:
 
 
 def kpool_compress_pools(p: Params, k, gate, ape, num_pools, dst_rows, pooled,
-                         stream=None) -> None:
+                         pooled_scale=None, stream=None) -> None:
     _check(lib().kpool_compress_pools(ctypes.byref(p.c()), _ptr(k), _ptr(gate), _ptr(ape),
                                       int(num_pools), _ptr(dst_rows), int(pooled.shape[0]),
-                                      _ptr(pooled), _stream(stream)))
+                                      _ptr(pooled), _ptr(pooled_scale), _stream(stream)))
 
 
 def kpool_decode_workspace_bytes(p: Params) -> int:
@@ -225,10 +225,11 @@ def kpool_decode_workspace_bytes(p: Params) -> int:
 
 
 def kpool_decode_topk(p: Params, q, w, pooled, pool_start, seq_lens, workspace, out_token_idx,
-                      out_pool_idx=None, token_base=None, stream=None) -> None:
+                      out_pool_idx=None, token_base=None, pooled_scale=None,
+                      stream=None) -> None:
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib().kpool_decode_topk(ctypes.byref(p.c()), _ptr(q), _ptr(w), _ptr(pooled),
-                                   int(pooled.shape[0]), _ptr(pool_start), _ptr(seq_lens), _ptr(token_base),
+                                   int(pooled.shape[0]), _ptr(pooled_scale), _ptr(pool_start), _ptr(seq_lens), _ptr(token_base),
                                    _ptr(workspace), ws_bytes, _ptr(out_token_idx),
                                    _ptr(out_pool_idx), _stream(stream)))
 

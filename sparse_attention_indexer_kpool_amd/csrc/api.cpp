@@ -157,10 +157,10 @@ void quantize_inputs(const Derived& d, const void* q, const void* pooled, const 
 // Parameters of a decode call: num_docs = B sequences, max_seqlen bounds
 // every sequence length; total_tokens and query_chunk are not used.
 struct DecodeDerived {
-  int B, H, D, kpool, k_sel, width, max_pools, tail;
+  int B, H, D, kpool, k_sel, width, max_pools, tail, fp8;
   int64_t ld;
   float scale;
-  size_t total;
+  size_t off_qc, off_qs, total;    // workspace: scores, then (FP8) q codes and scales
 };
 
 kpool_status derive_decode(const kpool_params* p, DecodeDerived* d) {
@@ -180,8 +180,10 @@ kpool_status derive_decode(const kpool_params* p, DecodeDerived* d) {
     return fail(KPOOL_E_UNSUPPORTED, "num_heads must be 4, 8, 16, 32 or 64 (got %d)", d->H);
   if (d->tail != 0 && d->tail != 1)
     return fail(KPOOL_E_INVALID, "always_select_tail must be 0 or 1");
-  if (p->use_fp8 != 0)
-    return fail(KPOOL_E_UNSUPPORTED, "the decode entry points take BF16 q and keys (use_fp8 = 0)");
+  d->fp8 = p->use_fp8;
+  if (d->fp8 != 0 && d->fp8 != 1) return fail(KPOOL_E_INVALID, "use_fp8 must be 0 or 1");
+  if (d->fp8 && d->D != 128)
+    return fail(KPOOL_E_UNSUPPORTED, "the FP8 path needs head_dim == 128 (got %d)", d->D);
   if (p->index_topk < d->kpool)
     return fail(KPOOL_E_INVALID, "index_topk (%d) must be >= kpool (%d)", p->index_topk, d->kpool);
   if (p->index_topk > (1 << 24)) return fail(KPOOL_E_UNSUPPORTED, "index_topk too large");
@@ -195,7 +197,15 @@ kpool_status derive_decode(const kpool_params* p, DecodeDerived* d) {
                 d->max_pools, kpool::kMaxSelectPools);
   d->ld = (int64_t)round_up((size_t)std::max(d->max_pools, 1), 64);
   d->scale = p->scale > 0.f ? p->scale : 1.0f / sqrtf((float)d->D);
-  d->total = round_up((size_t)d->B * d->ld * 4, 256);
+  size_t off = round_up((size_t)d->B * d->ld * 4, 256);
+  d->off_qc = d->off_qs = off;
+  if (d->fp8) {
+    d->off_qc = off;
+    off = round_up(off + (size_t)d->B * d->H * 128, 256);
+    d->off_qs = off;
+    off = round_up(off + (size_t)d->B * d->H * 4, 256);
+  }
+  d->total = off;
   return KPOOL_OK;
 }
 
@@ -379,7 +389,8 @@ size_t kpool_decode_workspace_bytes(const kpool_params* p) {
 }
 
 kpool_status kpool_decode_topk(const kpool_params* p, const void* q, const float* w,
-                               const void* pooled, int32_t pooled_rows, const int32_t* pool_start,
+                               const void* pooled, int32_t pooled_rows,
+                               const float* pooled_scale, const int32_t* pool_start,
                                const int32_t* seq_lens, const int32_t* token_base,
                                void* workspace, size_t workspace_bytes,
                                int32_t* out_token_idx, int32_t* out_pool_idx, void* stream) {
@@ -393,17 +404,31 @@ kpool_status kpool_decode_topk(const kpool_params* p, const void* q, const float
   CHECK(check_ptr(out_token_idx, 16, "out_token_idx"));
   if (out_pool_idx) CHECK(check_ptr(out_pool_idx, 4, "out_pool_idx"));
   if (pooled_rows < 0) return fail(KPOOL_E_INVALID, "pooled_rows must be >= 0 (got %d)", pooled_rows);
-  if (d.max_pools > 0 && pooled_rows > 0) CHECK(check_ptr(pooled, 16, "pooled"));
+  if (d.max_pools > 0 && pooled_rows > 0) {
+    CHECK(check_ptr(pooled, 16, "pooled"));
+    if (d.fp8) CHECK(check_ptr(pooled_scale, 4, "pooled_scale"));
+  }
   CHECK(check_ptr(workspace, 256, "workspace"));
   if (workspace_bytes < d.total)
     return fail(KPOOL_E_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, d.total);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   float* scores = reinterpret_cast<float*>(workspace);
+  uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
   (void)hipGetLastError();
   kpool::DecodeLogitsArgs a{};
-  a.q = reinterpret_cast<const uint16_t*>(q);
+  if (d.fp8) {
+    // the FP8 input path on the B H query rows; the cache already holds codes
+    kpool::launch_fp8_quantize(reinterpret_cast<const uint16_t*>(q), d.B * d.H, nullptr,
+                               ws + d.off_qc, reinterpret_cast<float*>(ws + d.off_qs), st);
+    a.q = ws + d.off_qc;
+    a.q_scale = reinterpret_cast<const float*>(ws + d.off_qs);
+    a.k_scale = pooled_scale;
+  } else {
+    a.q = q;
+  }
+  a.fp8 = d.fp8;
   a.w = w;
-  a.keys = reinterpret_cast<const uint16_t*>(pooled);
+  a.keys = pooled;
   a.pooled_rows = pooled_rows;
   a.pool_start = pool_start;
   a.seq_lens = seq_lens;
@@ -420,9 +445,13 @@ kpool_status kpool_decode_topk(const kpool_params* p, const void* q, const float
 
 kpool_status kpool_compress_pools(const kpool_params* p, const void* k, const void* gate,
                                   const float* ape, int32_t num_pools, const int32_t* dst_rows,
-                                  int32_t pooled_rows, void* pooled, void* stream) {
+                                  int32_t pooled_rows, void* pooled, float* pooled_scale,
+                                  void* stream) {
   if (!p) return fail(KPOOL_E_INVALID, "params is null");
   const int D = p->head_dim, kp = p->kpool;
+  if (p->use_fp8 != 0 && p->use_fp8 != 1) return fail(KPOOL_E_INVALID, "use_fp8 must be 0 or 1");
+  if (p->use_fp8 && D != 128)
+    return fail(KPOOL_E_UNSUPPORTED, "the FP8 path needs head_dim == 128 (got %d)", D);
   if (kp < 1 || kp > 64) return fail(KPOOL_E_UNSUPPORTED, "kpool must be in [1, 64] (got %d)", kp);
   if (D != 64 && D != 128) return fail(KPOOL_E_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", D);
   if (num_pools < 0) return fail(KPOOL_E_INVALID, "num_pools must be >= 0 (got %d)", num_pools);
@@ -434,11 +463,13 @@ kpool_status kpool_compress_pools(const kpool_params* p, const void* k, const vo
   CHECK(check_ptr(ape, 16, "ape"));
   CHECK(check_ptr(dst_rows, 4, "dst_rows"));
   CHECK(check_ptr(pooled, 16, "pooled"));
+  if (p->use_fp8) CHECK(check_ptr(pooled_scale, 4, "pooled_scale"));
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   kpool::launch_compress_pools(reinterpret_cast<const uint16_t*>(k),
                                reinterpret_cast<const uint16_t*>(gate), ape, num_pools, D, kp,
-                               dst_rows, pooled_rows, reinterpret_cast<uint16_t*>(pooled), st);
+                               dst_rows, pooled_rows, reinterpret_cast<uint16_t*>(pooled),
+                               p->use_fp8 ? pooled_scale : nullptr, st);
   return after_launch();
 }
 

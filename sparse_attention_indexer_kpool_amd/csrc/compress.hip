@@ -13,6 +13,7 @@
 
 #include "kpool_device.h"
 #include "kpool_internal.h"
+#include "fp8_row.h"
 
 namespace kpool {
 
@@ -66,13 +67,17 @@ constexpr int kFusedDocs = 1024;
 // SCATTER: the T tokens are T / kpool complete pools given back to back (one
 // document); pool p goes to pooled row dst_rows[p], skipped when that row is
 // outside [0, dst_cap); cu and cu_pools are not used.
-template <int D, int KP, bool FUSED, bool SCATTER = false>
+// FP8OUT (with SCATTER, D = 128): the BF16 pooled row goes on through the FP8
+// input path; its E4M3 codes are written to row dst_rows[p] of `pooled`
+// viewed as uint8 [dst_cap, 128] and its scale to row_scale[dst_rows[p]].
+template <int D, int KP, bool FUSED, bool SCATTER = false, bool FP8OUT = false>
 __global__ __launch_bounds__(256) void compress_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ gate,
     const float* __restrict__ ape, const int32_t* __restrict__ cu,
     int32_t* __restrict__ cu_pools, int B, int T, int kpool_rt,
     uint16_t* __restrict__ pooled, const int32_t* __restrict__ dst_rows = nullptr,
-    int dst_cap = 0) {
+    int dst_cap = 0, float* __restrict__ row_scale = nullptr) {
+  static_assert(!FP8OUT || (SCATTER && D == 128), "FP8 output: scattered pools, D = 128");
   constexpr int TPP = D / 8;                  // threads per pool
   constexpr int PPB = 256 / TPP;              // pools per workgroup
   const int kpool = KP > 0 ? KP : kpool_rt;
@@ -169,8 +174,22 @@ __global__ __launch_bounds__(256) void compress_kernel(
       outw[e >> 1] = pack_bf16x2(acc[e] * __builtin_amdgcn_rcpf(z[e]),
                                  acc[e + 1] * __builtin_amdgcn_rcpf(z[e + 1]));
     }
-    *reinterpret_cast<uint4*>(pooled + (size_t)p * D + d0) =
-        make_uint4(outw[0], outw[1], outw[2], outw[3]);
+    if constexpr (FP8OUT) {
+      // the 16 lanes of the pool hold its row, 8 BF16 values each, in the
+      // layout of the FP8 quantiser
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = bf16_bits_to_f32((outw[e >> 1] >> (16 * (e & 1))) & 0xffffu);
+      uint32_t packed[2];
+      const int l = tid % TPP;
+      const int ex = fp8_row_codes(v, l, packed);
+      uint8_t* codes = reinterpret_cast<uint8_t*>(pooled);
+      *reinterpret_cast<uint2*>(codes + (size_t)p * 128 + l * 8) = make_uint2(packed[0], packed[1]);
+      if (l == 0) row_scale[p] = ldexpf(1.0f, ex);
+    } else {
+      *reinterpret_cast<uint4*>(pooled + (size_t)p * D + d0) =
+          make_uint4(outw[0], outw[1], outw[2], outw[3]);
+    }
   };
   if constexpr (SCATTER) {
     const int p = blockIdx.x * PPB + tid / TPP;
@@ -286,24 +305,25 @@ void launch_compress(const uint16_t* k, const uint16_t* gate, const float* ape,
 
 void launch_compress_pools(const uint16_t* k, const uint16_t* gate, const float* ape, int N,
                            int D, int kpool, const int32_t* dst_rows, int dst_cap,
-                           uint16_t* pooled, hipStream_t st) {
+                           uint16_t* pooled, float* row_scale, hipStream_t st) {
   if (N <= 0) return;
   const int T = N * kpool;
   const int ppb = 256 / (D / 8);
   const dim3 grid((N + ppb - 1) / ppb), block(256);
-#define KP_S(DV, KPV)                                                                          \
-  compress_kernel<DV, KPV, true, true><<<grid, block, 0, st>>>(k, gate, ape, nullptr, nullptr, \
-                                                                1, T, kpool, pooled, dst_rows,  \
-                                                                dst_cap)
-#define KP_SD(DV)                   \
-  switch (kpool) {                  \
-    case 1: KP_S(DV, 1); break;     \
-    case 2: KP_S(DV, 2); break;     \
-    case 4: KP_S(DV, 4); break;     \
-    case 8: KP_S(DV, 8); break;     \
-    default: KP_S(DV, 0); break;    \
+#define KP_S(DV, KPV, F8)                                                                \
+  compress_kernel<DV, KPV, true, true, F8><<<grid, block, 0, st>>>(                      \
+      k, gate, ape, nullptr, nullptr, 1, T, kpool, pooled, dst_rows, dst_cap, row_scale)
+#define KP_SD(DV, F8)                   \
+  switch (kpool) {                      \
+    case 1: KP_S(DV, 1, F8); break;     \
+    case 2: KP_S(DV, 2, F8); break;     \
+    case 4: KP_S(DV, 4, F8); break;     \
+    case 8: KP_S(DV, 8, F8); break;     \
+    default: KP_S(DV, 0, F8); break;    \
   }
-  if (D == 128) { KP_SD(128) } else { KP_SD(64) }
+  if (row_scale) { KP_SD(128, true) }
+  else if (D == 128) { KP_SD(128, false) }
+  else { KP_SD(64, false) }
 #undef KP_SD
 #undef KP_S
 }

@@ -22,6 +22,8 @@
 // lane's 16 head rows by w' = w * scale, clamps at 0, sums them and adds the
 // other half-wave's 16 rows.
 
+#include <type_traits>
+
 #include "kpool_device.h"
 #include "kpool_internal.h"
 
@@ -31,18 +33,26 @@ constexpr int kDecWaves = 4;                       // waves per workgroup
 constexpr int kDecBlocksPerWave = 4;               // 32-pool blocks per wave
 constexpr int kDecPoolsPerGroup = 32 * kDecWaves * kDecBlocksPerWave;   // 512
 
-// Dims of MFMA step s held by lane half g (the same map for A and B, so the
-// dot products are whatever order K is taken in): step s covers dims 16 s ..
-// 16 s + 15, so the two lanes of a pair read 32 adjacent bytes of a row and
+// Bytes of MFMA step s held by lane half g of a row (the same map for A and
+// B, so the dot products are unchanged whatever order K is taken in): step s
+// covers K values KSTEP s .. KSTEP s + KSTEP - 1 and lane half g the g-th
+// half of them, so the two lanes of a pair read adjacent bytes of a row and
 // one load instruction touches 32 rows' cache lines. (Giving each lane one
 // contiguous half of the row instead touches 64 lines per instruction:
-// 229 against 212 us for 256 sequences of 64K tokens.)
-#define KOFF(s, g) (16 * (s) + 8 * (g))
+// 229 against 212 us for 256 sequences of 64K tokens, BF16.)
+template <bool FP8>
+__device__ __forceinline__ int koff_bytes(int s, int g) {
+  return FP8 ? 64 * s + 32 * g : 32 * s + 16 * g;
+}
 
-template <int H, int D>
+template <int H, int D, bool FP8>
 __global__ __launch_bounds__(64 * kDecWaves) void decode_logits_kernel(DecodeLogitsArgs a) {
   constexpr int MT = H > 32 ? H / 32 : 1;          // 32-row tiles of heads
-  constexpr int NSTEP = D / 16;                    // MFMAs per 32 x 32 tile
+  constexpr int KSTEP = FP8 ? 64 : 16;             // K per MFMA
+  constexpr int NSTEP = D / KSTEP;                 // MFMAs per 32 x 32 tile
+  constexpr int ROWB = FP8 ? D : 2 * D;            // bytes per q or key row
+  constexpr int CH = FP8 ? 2 : 1;                  // 16-byte chunks per lane and step
+  using Frag = typename std::conditional<FP8, i32x8_t, bf16x8_t>::type;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int b = (int)blockIdx.x / a.pieces;
   const int piece = (int)blockIdx.x % a.pieces;
@@ -52,42 +62,68 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_logits_kernel(DecodeLog
   if (p_lo >= n_c) return;                         // nothing for this wave (no barrier below)
   const int n = lane & 31, g = lane >> 5;
   const int pool0 = a.pool_start[b];
+  const uint8_t* __restrict__ qb = reinterpret_cast<const uint8_t*>(a.q);
+  const uint8_t* __restrict__ kb = reinterpret_cast<const uint8_t*>(a.keys);
 
-  // A: head rows of q[b]; lane (n, g) holds row n of each tile at dims
-  // KOFF(s, g) .. + 7 for step s
-  bf16x8_t afrag[MT][NSTEP];
+  auto to_frag = [](const uint4 (&c)[CH]) -> Frag {
+    if constexpr (FP8) {
+      const i32x8_t f = {(int)c[0].x, (int)c[0].y, (int)c[0].z, (int)c[0].w,
+                         (int)c[CH - 1].x, (int)c[CH - 1].y, (int)c[CH - 1].z, (int)c[CH - 1].w};
+      return f;
+    } else {
+      return __builtin_bit_cast(bf16x8_t, c[0]);
+    }
+  };
+
+  // A: head rows of q[b]; lane (n, g) holds row n of each tile, the bytes
+  // koff_bytes(s, g) .. of step s
+  Frag afrag[MT][NSTEP];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int head = mt * 32 + n;
-    const uint16_t* qrow = a.q + ((size_t)b * H + (head < H ? head : 0)) * D;
+    const uint8_t* qrow = qb + ((size_t)b * H + (head < H ? head : 0)) * ROWB;
 #pragma unroll
     for (int s = 0; s < NSTEP; ++s) {
-      const uint4 v = head < H ? *reinterpret_cast<const uint4*>(qrow + KOFF(s, g)) : make_uint4(0, 0, 0, 0);
-      afrag[mt][s] = __builtin_bit_cast(bf16x8_t, v);
+      uint4 c[CH];
+#pragma unroll
+      for (int h = 0; h < CH; ++h)
+        c[h] = head < H ? *reinterpret_cast<const uint4*>(qrow + koff_bytes<FP8>(s, g) + 16 * h)
+                        : make_uint4(0, 0, 0, 0);
+      afrag[mt][s] = to_frag(c);
     }
   }
-  // w' of this lane's accumulator rows: element v of a 32 x 32 accumulator is
-  // row 8 (v / 4) + 4 g + (v mod 4)
+  // w' of this lane's accumulator rows (element v of a 32 x 32 accumulator is
+  // row 8 (v / 4) + 4 g + (v mod 4)); FP8: times the q row's scale
   float wq[MT][16];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int head = mt * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
-      wq[mt][v] = head < H ? a.w[(size_t)b * H + head] * a.scale : 0.f;
+      float wv = 0.f;
+      if (head < H) {
+        wv = a.w[(size_t)b * H + head] * a.scale;
+        if constexpr (FP8) wv *= a.q_scale[(size_t)b * H + head];
+      }
+      wq[mt][v] = wv;
     }
 
   // B of block i: key row p_lo + 32 kDecWaves i + n, clamped into the causal
   // range (clamped columns are never stored) and into the cache
-  auto load_b = [&](int i, uint4 (&bf)[NSTEP]) {
+  auto key_row = [&](int i) {
     const int p = min(p_lo + 32 * kDecWaves * i + n, n_c - 1);
-    const int row = clampi(pool0 + p, 0, a.pooled_rows - 1);
-    const uint16_t* krow = a.keys + (size_t)row * D;
+    return clampi(pool0 + p, 0, a.pooled_rows - 1);
+  };
+  auto load_b = [&](int i, uint4 (&bf)[NSTEP][CH]) {
+    const uint8_t* krow = kb + (size_t)key_row(i) * ROWB;
 #pragma unroll
-    for (int s = 0; s < NSTEP; ++s) bf[s] = *reinterpret_cast<const uint4*>(krow + KOFF(s, g));
+    for (int s = 0; s < NSTEP; ++s)
+#pragma unroll
+      for (int h = 0; h < CH; ++h)
+        bf[s][h] = *reinterpret_cast<const uint4*>(krow + koff_bytes<FP8>(s, g) + 16 * h);
   };
   float* __restrict__ out = a.out + (size_t)b * a.ld;
-  uint4 bfr[2][NSTEP];
+  uint4 bfr[2][NSTEP][CH];
   load_b(0, bfr[0]);
 #pragma unroll
   for (int i = 0; i < kDecBlocksPerWave; ++i) {
@@ -105,10 +141,15 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_logits_kernel(DecodeLog
       for (int v = 0; v < 16; ++v) acc[mt][v] = 0.f;
 #pragma unroll
     for (int s = 0; s < NSTEP; ++s) {
-      const bf16x8_t bf = __builtin_bit_cast(bf16x8_t, bfr[i & 1][s]);
+      const Frag bf = to_frag(bfr[i & 1][s]);
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afrag[mt][s], bf, acc[mt], 0, 0, 0);
+      for (int mt = 0; mt < MT; ++mt) {
+        if constexpr (FP8)
+          acc[mt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(afrag[mt][s], bf, acc[mt], 0, 0,
+                                                                    0, 0, 0, 0);
+        else
+          acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afrag[mt][s], bf, acc[mt], 0, 0, 0);
+      }
     }
     // w' * ReLU over this lane's head rows (ReLU as an integer max: FP32
     // values of either sign order like their bit patterns against +0)
@@ -121,34 +162,36 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_logits_kernel(DecodeLog
     // add the other half-wave's rows of the same column
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(sum), __float_as_uint(sum),
                                                      false, false);
-    const float score = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    float score = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    if constexpr (FP8) score *= a.k_scale[key_row(i)];     // the key's power-of-two scale
     if (g == 0 && c0 + n < n_c) out[c0 + n] = score;
   }
 }
 
-template <int H, int D>
+template <int H, int D, bool FP8>
 static void launch_hd(const DecodeLogitsArgs& a0, hipStream_t st) {
   DecodeLogitsArgs a = a0;
   a.pieces = (a.max_pools + kDecPoolsPerGroup - 1) / kDecPoolsPerGroup;
   if (a.pieces < 1) a.pieces = 1;
-  decode_logits_kernel<H, D><<<a.B * a.pieces, 64 * kDecWaves, 0, st>>>(a);
+  decode_logits_kernel<H, D, FP8><<<a.B * a.pieces, 64 * kDecWaves, 0, st>>>(a);
 }
 
-template <int D>
+template <int D, bool FP8>
 static void launch_d(const DecodeLogitsArgs& a, hipStream_t st) {
   switch (a.H) {
-    case 4: launch_hd<4, D>(a, st); break;
-    case 8: launch_hd<8, D>(a, st); break;
-    case 16: launch_hd<16, D>(a, st); break;
-    case 32: launch_hd<32, D>(a, st); break;
-    default: launch_hd<64, D>(a, st); break;
+    case 4: launch_hd<4, D, FP8>(a, st); break;
+    case 8: launch_hd<8, D, FP8>(a, st); break;
+    case 16: launch_hd<16, D, FP8>(a, st); break;
+    case 32: launch_hd<32, D, FP8>(a, st); break;
+    default: launch_hd<64, D, FP8>(a, st); break;
   }
 }
 
 void launch_decode_logits(const DecodeLogitsArgs& a, hipStream_t st) {
   if (a.B <= 0 || a.max_pools <= 0 || a.pooled_rows <= 0) return;
-  if (a.D == 128) launch_d<128>(a, st);
-  else launch_d<64>(a, st);
+  if (a.fp8) launch_d<128, true>(a, st);
+  else if (a.D == 128) launch_d<128, false>(a, st);
+  else launch_d<64, false>(a, st);
 }
 
 }  // namespace kpool

@@ -23,6 +23,7 @@
 
 #include "kpool_device.h"
 #include "kpool_internal.h"
+#include "fp8_row.h"
 
 #pragma clang fp contract(off)
 
@@ -58,58 +59,8 @@ __global__ __launch_bounds__(256) void fp8_quantize_kernel(
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = bf16_bits_to_f32((wv[e >> 1] >> (16 * (e & 1))) & 0xffffu);
 
-    // stages h = 1, 2, 4 inside the lane
-#pragma unroll
-    for (int h = 1; h < 8; h <<= 1) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        if ((e & h) == 0) {
-          const float a = v[e], b = v[e + h];
-          v[e] = a + b;
-          v[e + h] = a - b;
-        }
-      }
-    }
-    // stages h = 8, 16, 32, 64 across lanes l and l ^ (h / 8): the lower
-    // lane keeps v + other, the upper one other - v, both as one
-    // fma(+-1, v, other), which rounds exactly as the addition or
-    // subtraction does
-#pragma unroll
-    for (int s = 1; s < 16; s <<= 1) {
-      const float sgn = (l & s) != 0 ? -1.f : 1.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float other = xor_lane16(v[e], s);
-        v[e] = fmaf(sgn, v[e], other);
-      }
-    }
-    const float norm = 0.08838834764831845f;   // FP32(128^-1/2)
-    float amax = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      v[e] = (float)(__bf16)(v[e] * norm);      // v_cvt_pk_bf16_f32: round to nearest even
-      amax = fmaxf(amax, fabsf(v[e]));
-    }
-#pragma unroll
-    for (int s = 1; s < 16; s <<= 1) amax = fmaxf(amax, xor_lane16(amax, s));
-
-    int ex = 0;
-    if (amax > 0.f && amax <= 3.402823466e38f) {
-      int fe;
-      const float f = frexpf(amax, &fe);      // amax = f * 2^fe, f in [0.5, 1)
-      ex = fe - 9 + (f > 0.875f ? 1 : 0);
-    }
-    // v_cvt_pk_fp8_f32: OCP E4M3, round to nearest even, subnormals kept;
-    // |v 2^-ex| <= 448 by the choice of ex, so nothing saturates
     uint32_t packed[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      int w = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[4 * h], -ex), ldexpf(v[4 * h + 1], -ex), 0,
-                                              false);
-      w = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[4 * h + 2], -ex), ldexpf(v[4 * h + 3], -ex), w,
-                                          true);
-      packed[h] = (uint32_t)w;
-    }
+    const int ex = fp8_row_codes(v, l, packed);
     if (row < limit) {
       *reinterpret_cast<uint2*>(codes + (size_t)row * 128 + l * 8) = make_uint2(packed[0], packed[1]);
       if (l == 0) row_scale[row] = ldexpf(1.0f, ex);

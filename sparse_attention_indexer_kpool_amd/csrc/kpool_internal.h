@@ -54,10 +54,13 @@ void launch_expand(const int32_t* pool_ids, int q_begin, int q_end, const int32_
 // sequence's floor(seq_lens[b] / kpool) cached pools at pooled rows
 // pool_start[b] ...; scores to out [B, ld].
 struct DecodeLogitsArgs {
-  const uint16_t* q;           // BF16 [B, H, D]
+  const void* q;               // BF16 [B, H, D], or E4M3 codes [B, H, 128]
+  const float* q_scale;        // FP8: FP32 [B, H] row scales, else null
   const float* w;              // FP32 [B, H]
-  const uint16_t* keys;        // BF16 pooled rows [pooled_rows, D]
+  const void* keys;            // BF16 [pooled_rows, D], or E4M3 codes [pooled_rows, 128]
+  const float* k_scale;        // FP8: FP32 [pooled_rows] row scales, else null
   int pooled_rows;             // reads are clamped into this many rows
+  int fp8;
   const int32_t* pool_start;   // [B]
   const int32_t* seq_lens;     // [B]
   int B, H, D, kpool, max_pools;
@@ -78,10 +81,12 @@ void launch_select_decode(const float* scores, int64_t ld, int B, const int32_t*
 
 // Compression of N complete pools given their slot tokens: pool n is tokens
 // n kpool .. n kpool + kpool - 1 of k / gate, written to pooled row
-// dst_rows[n] (rows outside [0, dst_cap) are skipped).
+// dst_rows[n] (rows outside [0, dst_cap) are skipped). With row_scale (D =
+// 128), the rows are E4M3 codes of the FP8 input path instead (pooled viewed
+// as uint8 [dst_cap, 128]) and their scales go to row_scale.
 void launch_compress_pools(const uint16_t* k, const uint16_t* gate, const float* ape, int N,
                            int D, int kpool, const int32_t* dst_rows, int dst_cap,
-                           uint16_t* pooled, hipStream_t st);
+                           uint16_t* pooled, float* row_scale, hipStream_t st);
 
 // Largest max_pools the selection kernel handles (its LDS bitmap has one bit
 // per pool of a row).

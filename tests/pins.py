@@ -612,4 +612,35 @@ def pin_decode_is_last_token_row(o):
                 assert np.array_equal(dpid[b], np.where(pid >= 0, pid + starts[b], -1)), (kp, tail, b)
 
 
+def pin_decode_fp8_is_last_token_row(o):
+    """The FP8 decode row (q and cached keys through the FP8 input path)
+    equals the FP8 prefill row of the sequence's last token."""
+    H, D, kp, topk = 2, 128, 4, 16
+    lens = [0, 7, 40, 131]
+    q_rows, w_rows, cache, starts, per_doc = [], [], [], [], []
+    cursor = 0
+    for b, L in enumerate(lens):
+        q, k, gate, w, ape, cu = _tiny_case(970 + b, [max(L, 1)], H, D, kp)
+        pb, _ = o.compress(k[:L], gate[:L], ape, [0, L], kp)
+        starts.append(cursor)
+        cache.append(pb)
+        cursor += len(pb)
+        q_rows.append(q[max(L, 1) - 1])
+        w_rows.append(w[max(L, 1) - 1])
+        if L > 0:
+            tok, pid = o.indexer_topk(q[:L], w[:L], pb, [0, L], kp, topk, True, rows=[L - 1],
+                                      fp8=True)
+        else:
+            tok = np.full((1, topk + kp), -1, np.int32)
+            pid = np.full((1, topk // kp), -1, np.int32)
+        per_doc.append((tok[0], pid[0]))
+    pooled = np.concatenate(cache).astype(F32)
+    dtok, dpid = o.decode_topk(np.stack(q_rows), np.stack(w_rows), pooled, starts, lens, kp,
+                               topk, True, fp8=True)
+    for b in range(len(lens)):
+        tok, pid = per_doc[b]
+        assert np.array_equal(dtok[b], tok), b
+        assert np.array_equal(dpid[b], np.where(pid >= 0, pid + starts[b], -1)), b
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -133,7 +133,9 @@ def test_decode_workspace():
     p = P(num_docs=64, total_tokens=0, max_seqlen=65536)
     assert kp.kpool_decode_workspace_bytes(p) == 64 * 16384 * 4
     assert kp.kpool_decode_workspace_bytes(P(num_docs=3, max_seqlen=4100)) == 3 * 1088 * 4
-    assert kp.kpool_decode_workspace_bytes(P(use_fp8=1)) == 0
+    p8 = P(num_docs=64, total_tokens=0, max_seqlen=65536, use_fp8=1)
+    assert kp.kpool_decode_workspace_bytes(p8) == 64 * 16384 * 4 + 64 * 32 * 128 + 64 * 32 * 4
+    assert kp.kpool_decode_workspace_bytes(P(use_fp8=1, head_dim=64)) == 0
     assert kp.kpool_decode_workspace_bytes(P(num_docs=0)) == 0
     assert kp.kpool_decode_workspace_bytes(P(max_seqlen=262148)) == 0
 
@@ -142,22 +144,29 @@ def test_decode_workspace():
 def test_decode_argument_checks():
     p = P(num_docs=8, max_seqlen=65536)
     ws = kp.kpool_decode_workspace_bytes(p)
-    args = (FAKE, FAKE, FAKE, 100, FAKE, FAKE, None, FAKE, ws, FAKE, None, None)
-    assert raw("kpool_decode_topk", pref(P(use_fp8=1)), *args) == kp.KPOOL_E_UNSUPPORTED
-    assert "BF16" in kp.kpool_last_error()
+    args = (FAKE, FAKE, FAKE, 100, None, FAKE, FAKE, None, FAKE, ws, FAKE, None, None)
+    assert raw("kpool_decode_topk", pref(P(use_fp8=1, head_dim=64)), *args) == kp.KPOOL_E_UNSUPPORTED
+    assert "FP8" in kp.kpool_last_error()
+    p8 = P(num_docs=8, max_seqlen=65536, use_fp8=1)
+    ws8 = kp.kpool_decode_workspace_bytes(p8)
+    noscale = (FAKE, FAKE, FAKE, 100, None, FAKE, FAKE, None, FAKE, ws8, FAKE, None, None)
+    assert raw("kpool_decode_topk", pref(p8), *noscale) == kp.KPOOL_E_INVALID
+    assert "pooled_scale" in kp.kpool_last_error()
     assert raw("kpool_decode_topk", pref(P(num_heads=12)), *args) == kp.KPOOL_E_UNSUPPORTED
-    small = (FAKE, FAKE, FAKE, 100, FAKE, FAKE, None, FAKE, ws - 1, FAKE, None, None)
+    small = (FAKE, FAKE, FAKE, 100, None, FAKE, FAKE, None, FAKE, ws - 1, FAKE, None, None)
     assert raw("kpool_decode_topk", pref(p), *small) == kp.KPOOL_E_WORKSPACE
-    nolen = (FAKE, FAKE, FAKE, 100, FAKE, None, None, FAKE, ws, FAKE, None, None)
+    nolen = (FAKE, FAKE, FAKE, 100, None, FAKE, None, None, FAKE, ws, FAKE, None, None)
     assert raw("kpool_decode_topk", pref(p), *nolen) == kp.KPOOL_E_INVALID
     assert "seq_lens" in kp.kpool_last_error()
-    badbase = (FAKE, FAKE, FAKE, 100, FAKE, FAKE, FAKE + 2, FAKE, ws, FAKE, None, None)
+    badbase = (FAKE, FAKE, FAKE, 100, None, FAKE, FAKE, FAKE + 2, FAKE, ws, FAKE, None, None)
     assert raw("kpool_decode_topk", pref(p), *badbase) == kp.KPOOL_E_INVALID
-    negrows = (FAKE, FAKE, FAKE, -1, FAKE, FAKE, None, FAKE, ws, FAKE, None, None)
+    negrows = (FAKE, FAKE, FAKE, -1, None, FAKE, FAKE, None, FAKE, ws, FAKE, None, None)
     assert raw("kpool_decode_topk", pref(p), *negrows) == kp.KPOOL_E_INVALID
-    assert raw("kpool_compress_pools", pref(p), FAKE, FAKE, FAKE, -1, FAKE, 10, FAKE, None) == kp.KPOOL_E_INVALID
-    assert raw("kpool_compress_pools", pref(p), FAKE, FAKE, FAKE, 4, None, 10, FAKE, None) == kp.KPOOL_E_INVALID
-    assert raw("kpool_compress_pools", pref(P(kpool=65)), FAKE, FAKE, FAKE, 4, FAKE, 10, FAKE, None) == kp.KPOOL_E_UNSUPPORTED
+    assert raw("kpool_compress_pools", pref(p), FAKE, FAKE, FAKE, -1, FAKE, 10, FAKE, None, None) == kp.KPOOL_E_INVALID
+    assert raw("kpool_compress_pools", pref(p), FAKE, FAKE, FAKE, 4, None, 10, FAKE, None, None) == kp.KPOOL_E_INVALID
+    assert raw("kpool_compress_pools", pref(P(kpool=65)), FAKE, FAKE, FAKE, 4, FAKE, 10, FAKE, None, None) == kp.KPOOL_E_UNSUPPORTED
+    assert raw("kpool_compress_pools", pref(P(use_fp8=1)), FAKE, FAKE, FAKE, 4, FAKE, 10, FAKE, None, None) == kp.KPOOL_E_INVALID
+    assert raw("kpool_compress_pools", pref(P(use_fp8=1, head_dim=64)), FAKE, FAKE, FAKE, 4, FAKE, 10, FAKE, FAKE, None) == kp.KPOOL_E_UNSUPPORTED
 
 
 def test_status_strings():

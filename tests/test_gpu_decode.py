@@ -9,6 +9,10 @@ oracle on the same seeded inputs:
                   the k-th score; token rows equal the oracle's expansion of the
                   GPU's pool ids exactly; the last token of every document of a
                   packed batch gets the prefill indexer's row
+  FP8 cache       compress_pools codes and scales bit-identical to
+                  kpool_fp8_quantize of kpool_compress's rows; FP8 decode vs the
+                  oracle's FP8 decode (q and keys through the oracle's own FP8
+                  input path) and vs the FP8 prefill row of each last token
 """
 import numpy as np
 import pytest
@@ -29,24 +33,36 @@ def _gpu():
     kp.lib()
 
 
-def _dparams(lens, H, D, kpool, topk, tail=True):
+def _dparams(lens, H, D, kpool, topk, tail=True, fp8=False):
     return kp.Params(num_docs=len(lens), total_tokens=0, max_seqlen=max(max(lens), 0),
                      num_heads=H, head_dim=D, kpool=kpool, index_topk=topk,
-                     always_select_tail=int(tail))
+                     always_select_tail=int(tail), use_fp8=int(fp8))
 
 
-def _run_decode(p, di):
+def _fp8_cache(pooled_bf16_dev):
+    """E4M3 codes and scales of BF16 cache rows, by the library's quantiser
+    (its codes are checked bit for bit against the oracle elsewhere)."""
+    rows = pooled_bf16_dev.shape[0]
+    codes = torch.empty(rows, 128, dtype=torch.uint8, device=DEV)
+    scales = torch.empty(rows, dtype=torch.float32, device=DEV)
+    kp.kpool_fp8_quantize(pooled_bf16_dev.contiguous(), rows, codes, scales)
+    return codes, scales
+
+
+def _run_decode(p, di, pooled_dev=None, pooled_scale=None):
     ws = torch.empty(max(kp.kpool_decode_workspace_bytes(p), 256), dtype=torch.uint8, device=DEV)
     tok = torch.full((di.B, p.width), -12345, dtype=torch.int32, device=DEV)
     pid = torch.full((di.B, p.k_sel), -12345, dtype=torch.int32, device=DEV)
-    kp.kpool_decode_topk(p, di.q.to(DEV), di.w.to(DEV), di.pooled.to(DEV),
+    if pooled_dev is None:
+        pooled_dev = di.pooled.to(DEV)
+    kp.kpool_decode_topk(p, di.q.to(DEV), di.w.to(DEV), pooled_dev,
                          di.pool_start.to(DEV), di.seq_lens.to(DEV), ws, tok, pid,
-                         token_base=di.token_base.to(DEV))
+                         token_base=di.token_base.to(DEV), pooled_scale=pooled_scale)
     torch.cuda.synchronize()
     return tok.cpu().numpy(), pid.cpu().numpy()
 
 
-def _check_decode(p, di, tok, pid):
+def _check_decode(p, di, tok, pid, fp8=False):
     q = di.q.float().numpy()
     w = di.w.numpy()
     pooled = di.pooled.float().numpy()
@@ -60,7 +76,11 @@ def _check_decode(p, di, tok, pid):
             assert np.all(tok[b] == -1) and np.all(pid[b] == -1), b
             continue
         n_c = L // p.kpool
-        scores = oracle.row_scores(q[b], w[b], pooled[s0:s0 + n_c], sc)
+        keys, q_b = pooled[s0:s0 + n_c], q[b]
+        if fp8:
+            _, _, keys = oracle.fp8_quantize_rows(keys)
+            _, _, q_b = oracle.fp8_quantize_rows(q_b)
+        scores = oracle.row_scores(q_b, w[b], keys, sc)
         ref_local = oracle.select_pools(scores, p.k_sel)
         ref = np.full(p.k_sel, -1, np.int64)
         ref[:len(ref_local)] = ref_local + s0
@@ -167,3 +187,89 @@ def test_compress_pools_matches_compress(kpool, D):
             written.add(r)
     untouched = [r for r in range(cap) if r not in written]
     assert np.all(got[untouched] == 0x7F7F)
+
+
+@pytest.mark.parametrize("lens,H,kpool,topk", [
+    ([0, 1, 5, 2047, 2051, 9000, 65536], 32, 4, 2048),
+    ([3, 300, 4097], 4, 3, 300),
+    ([64, 65, 2000], 64, 1, 64),
+], ids=["h32_k4", "h4_k3", "h64_k1"])
+def test_decode_fp8_matches_oracle(lens, H, kpool, topk):
+    p = _dparams(lens, H, 128, kpool, topk, fp8=True)
+    di = wlm.make_decode_inputs(lens, H, 128, kpool, seed=17 + H)
+    codes, scales = _fp8_cache(di.pooled.to(DEV))
+    log(f"decode fp8 {len(lens)} sequences, H {H} kpool {kpool} topk {topk}")
+    tok, pid = _run_decode(p, di, codes, scales)
+    _check_decode(p, di, tok, pid, fp8=True)
+
+
+def test_decode_fp8_is_prefill_last_token_row():
+    """FP8 decode over the codes of the pooled keys kpool_compress wrote for
+    a packed batch gives each document's last token the FP8 prefill row (up
+    to near-ties)."""
+    wl = wlm.custom("fp8_docs", doc_lengths=[700, 1300, 2501], H=32, D=128, kpool=4,
+                    index_topk=512, fp8=True, heavy_frac=0.05)
+    d = Dev(wlm.make_inputs(wl))
+    d.compress()
+    tok_pf, pid_pf = d.indexer()
+    inp = d.inp
+    cu = inp.cu_seqlens.numpy().astype(np.int64)
+    cuP = d.cu_pools.cpu().numpy().astype(np.int64)
+    B = len(inp.doc_lengths)
+    last = [int(cu[b + 1]) - 1 for b in range(B)]
+    lens = list(inp.doc_lengths)
+    P = int(cuP[B])
+    codes, scales = _fp8_cache(d.pooled[:P])
+    di = wlm.DecodeInputs(q=inp.q[last].contiguous(), w=inp.w[last].contiguous(),
+                          pooled=d.pooled[:P].cpu(), pool_start=torch.tensor(cuP[:B], dtype=torch.int32),
+                          seq_lens=torch.tensor(lens, dtype=torch.int32),
+                          token_base=torch.tensor(cu[:B], dtype=torch.int32), kpool=4)
+    p = _dparams(lens, 32, 128, 4, 512, fp8=True)
+    tok, pid = _run_decode(p, di, codes, scales)
+    q, _, _, w, _, _ = oracle_inputs(inp)
+    _, _, keys_all = oracle.fp8_quantize_rows(d.pooled[:P].float().cpu().numpy())
+    sc = float(np.float32(1.0 / np.sqrt(128)))
+    for b, t in enumerate(last):
+        n_c = lens[b] // 4
+        _, _, q_t = oracle.fp8_quantize_rows(q[t])
+        scores = oracle.row_scores(q_t, w[t], keys_all[cuP[b]:cuP[b] + n_c], sc)
+        okk, why = sets_match_up_to_ties(pid[b], pid_pf[t], scores, int(cuP[b]), p.k_sel)
+        assert okk, f"document {b}: {why}"
+        if np.array_equal(pid[b], pid_pf[t]):
+            assert np.array_equal(tok[b], tok_pf[t]), f"document {b}"
+
+
+@pytest.mark.parametrize("kpool", [4, 3])
+def test_compress_pools_fp8_matches_quantised_compress(kpool):
+    wl = wlm.custom("pools8", T=1200, H=4, D=128, kpool=kpool, index_topk=64)
+    d = Dev(wlm.make_inputs(wl))
+    d.compress()
+    P = int(d.cu_pools[-1].item())
+    ref_codes, ref_scales = _fp8_cache(d.pooled[:P])
+    g = torch.Generator().manual_seed(kpool)
+    pick = torch.randperm(P, generator=g)[: P // 2]
+    N = len(pick)
+    cap = P + 7
+    dst = torch.randperm(cap, generator=g)[:N].to(torch.int32)
+    dst[1] = cap                               # skipped
+    tok_idx = (pick[:, None] * kpool + torch.arange(kpool)[None, :]).reshape(-1)
+    k_slots = d.inp.k[tok_idx].contiguous().to(DEV)
+    g_slots = d.inp.gate[tok_idx].contiguous().to(DEV)
+    codes = torch.full((cap, 128), 0xA5, dtype=torch.uint8, device=DEV)
+    scales = torch.full((cap,), -3.0, dtype=torch.float32, device=DEV)
+    p = kp.Params(num_docs=1, total_tokens=1200, max_seqlen=1200, num_heads=4, head_dim=128,
+                  kpool=kpool, index_topk=64, use_fp8=1)
+    kp.kpool_compress_pools(p, k_slots, g_slots, d.ape, N, dst.to(DEV), codes, pooled_scale=scales)
+    torch.cuda.synchronize()
+    got_c, got_s = codes.cpu().numpy(), scales.cpu().numpy()
+    rc, rs = ref_codes.cpu().numpy(), ref_scales.cpu().numpy()
+    written = set()
+    for n in range(N):
+        r = int(dst[n])
+        if 0 <= r < cap:
+            assert np.array_equal(got_c[r], rc[int(pick[n])]), n
+            assert got_s[r] == rs[int(pick[n])], n
+            written.add(r)
+    untouched = [r for r in range(cap) if r not in written]
+    assert np.all(got_c[untouched] == 0xA5) and np.all(got_s[untouched] == -3.0)
+
