@@ -215,30 +215,41 @@ def cpu_baseline(inp: wlm.Inputs, n_rows: int):
                       f"NumPy FP32 on {os.cpu_count()} host CPUs"}
 
 
-def decode_bench(reps: int, B: int = 64, L: int = 65536):
+def decode_bench(reps: int, B: int = 64, L: int = 65536, fp8: bool = False):
     """The serving step: kpool_decode_topk for B sequences of L tokens each
     (one query per sequence over L / 4 cached pooled keys), H = 32, D = 128,
-    kpool = 4, index_topk = 2048. Returns the JSON object of its line."""
+    kpool = 4, index_topk = 2048; with fp8 the cache holds E4M3 codes and
+    scales. Returns the JSON object of its line."""
     import sparse_attention_indexer_kpool_amd as kp
     H, D, KP, TOPK = 32, 128, 4, 2048
     di = wlm.make_decode_inputs([L] * B, H, D, KP, seed=7)
     p = kp.Params(num_docs=B, total_tokens=0, max_seqlen=L, num_heads=H, head_dim=D, kpool=KP,
-                  index_topk=TOPK, always_select_tail=1)
+                  index_topk=TOPK, always_select_tail=1, use_fp8=int(fp8))
     dev = "cuda:0"
     q, w, pooled = di.q.to(dev), di.w.to(dev), di.pooled.to(dev)
+    scales = None
+    if fp8:
+        rows = pooled.shape[0]
+        codes = torch.empty(rows, 128, dtype=torch.uint8, device=dev)
+        scales = torch.empty(rows, dtype=torch.float32, device=dev)
+        kp.kpool_fp8_quantize(pooled, rows, codes, scales)
+        pooled = codes
     ps, sl, tb = di.pool_start.to(dev), di.seq_lens.to(dev), di.token_base.to(dev)
     ws = torch.empty(kp.kpool_decode_workspace_bytes(p), dtype=torch.uint8, device=dev)
     tok = torch.empty(B, p.width, dtype=torch.int32, device=dev)
-    run = lambda: kp.kpool_decode_topk(p, q, w, pooled, ps, sl, ws, tok, token_base=tb)
+    run = lambda: kp.kpool_decode_topk(p, q, w, pooled, ps, sl, ws, tok, token_base=tb,
+                                       pooled_scale=scales)
     ms = time_region(run, reps, warm=2)
     n_c = L // KP
-    by = B * n_c * (2 * D + 4 + 4) + B * H * (2 * D + 4) + 4 * B * p.width
-    return {"workload": f"decode_B{B}_L{L}_H{H}_D{D}", "ms": round(ms, 4),
+    if fp8:   # key codes + scale; q read, its codes and scales written and read
+        by = B * n_c * (D + 4 + 4 + 4) + B * H * (2 * D + 4 + 2 * (D + 4)) + 4 * B * p.width
+    else:
+        by = B * n_c * (2 * D + 4 + 4) + B * H * (2 * D + 4) + 4 * B * p.width
+    return {"workload": f"decode{'_fp8' if fp8 else ''}_B{B}_L{L}_H{H}_D{D}", "ms": round(ms, 4),
             "queries_per_s": round(B / (ms * 1e-3), 1),
             "hbm": {"bytes": by, "GB/s": round(by / (ms * 1e-3) / 1e9, 1),
                     "frac": round(by / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
-            "note": "keys read once (2 D bytes per pool), scores written and read once, "
-                    "token rows written"}
+            "note": "keys read once, scores written and read once, token rows written"}
 
 
 def main():
@@ -354,6 +365,7 @@ def main():
     if not args.no_decode and wl.name == "long_T65536_H32_D128":
         log("decode step, 64 sequences of 64K tokens")
         out["decode"] = decode_bench(reps)
+        out["decode_fp8"] = decode_bench(reps, fp8=True)
     if rank == 0 and not args.no_cpu_baseline:
         log(f"cpu baseline on {args.cpu_rows} rows")
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_rows)
