@@ -12,15 +12,18 @@
 //
 //   score[b, j] = sum_h w[b, h] * ReLU(scale * q[b, h, :] . pooled[start_b + j, :])
 //
-// HBM-bound: every causal pooled key of every sequence is read once (2 D bytes
-// per pool); the arithmetic is 2 H D FLOP per pool, a few percent of what the
-// matrix cores could do in that time. Still a contraction, so it runs on
-// v_mfma_f32_32x32x16_bf16: the A operand is the sequence's H head rows of q
-// (zero rows up to a multiple of 32), held in registers; the B operand is a
-// block of 32 keys, each lane pair reading 32 adjacent bytes of a key row
-// per step. The epilogue multiplies each
-// lane's 16 head rows by w' = w * scale, clamps at 0, sums them and adds the
-// other half-wave's 16 rows.
+// HBM-bound: every causal pooled key of every sequence is read once (2 D
+// bytes per pool, or D bytes of E4M3 codes and a 4-byte scale); the
+// arithmetic is 2 H D FLOP per pool, a few percent of what the matrix cores
+// could do in that time. Still a contraction, so it runs on them:
+// v_mfma_f32_32x32x16_bf16 for a BF16 cache, v_mfma_f32_32x32x64_f8f6f4 on
+// E4M3 codes for an FP8 cache (the q rows quantised first; their scales fold
+// into w', and each key's scale multiplies its head sum, as in the prefill
+// kernel). The A operand is the sequence's H head rows of q (zero rows up to
+// a multiple of 32), held in registers; the B operand is a block of 32 keys,
+// each lane pair reading adjacent bytes of a key row per step. The epilogue
+// multiplies each lane's 16 head rows by w' = w * scale, clamps at 0, sums
+// them and adds the other half-wave's 16 rows.
 
 #include <type_traits>
 
