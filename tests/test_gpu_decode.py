@@ -100,7 +100,9 @@ def _check_decode(p, di, tok, pid, fp8=False):
     ([0, 2, 3, 300, 301, 902, 5000, 12345], 4, 64, 3, 300, False),
     ([1, 63, 64, 65, 1000, 4096], 64, 128, 1, 64, True),
     ([17, 130, 131, 1024, 3000], 8, 128, 2, 256, True),
-], ids=["h32_k4", "h4_d64_k3_notail", "h64_k1", "h8_k2"])
+    ([2044, 2048, 2055, 4096, 4100, 8191], 16, 64, 4, 512, True),
+    ([40, 4095, 4096, 4103], 32, 128, 8, 1024, True),
+], ids=["h32_k4", "h4_d64_k3_notail", "h64_k1", "h8_k2", "h16_d64_piece_edges", "k8"])
 def test_decode_matches_oracle(lens, H, D, kpool, topk, tail):
     p = _dparams(lens, H, D, kpool, topk, tail)
     di = wlm.make_decode_inputs(lens, H, D, kpool, seed=len(lens) + H + kpool)
