@@ -241,8 +241,8 @@ def decode_bench(reps: int, B: int = 64, L: int = 65536, fp8: bool = False):
                                        pooled_scale=scales)
     ms = time_region(run, reps, warm=2)
     n_c = L // KP
-    if fp8:   # key codes + scale; q read, its codes and scales written and read
-        by = B * n_c * (D + 4 + 4 + 4) + B * H * (2 * D + 4 + 2 * (D + 4)) + 4 * B * p.width
+    if fp8:   # key codes + scale, scores written and read; q (quantised in the kernel) and w
+        by = B * n_c * (D + 4 + 4 + 4) + B * H * (2 * D + 4) + 4 * B * p.width
     else:
         by = B * n_c * (2 * D + 4 + 4) + B * H * (2 * D + 4) + 4 * B * p.width
     return {"workload": f"decode{'_fp8' if fp8 else ''}_B{B}_L{L}_H{H}_D{D}", "ms": round(ms, 4),

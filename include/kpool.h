@@ -220,8 +220,7 @@ kpool_status kpool_compress_pools(const kpool_params* p, const void* k, const vo
                                   void* stream);
 
 /* Bytes of workspace kpool_decode_topk needs (0 for invalid parameters):
- * the scores of every sequence, B rows of kpool_logits_ld floats, and with
- * use_fp8 the codes and scales of the B H query rows. */
+ * the scores of every sequence, B rows of kpool_logits_ld floats. */
 size_t kpool_decode_workspace_bytes(const kpool_params* p);
 
 /* Steps 2-4 for B = num_docs sequences, one query each. Sequence b has
@@ -244,9 +243,9 @@ size_t kpool_decode_workspace_bytes(const kpool_params* p);
  *   workspace   at least kpool_decode_workspace_bytes(p) bytes, 256-byte aligned
  *   out_token_idx  out int32 [B, W];  out_pool_idx  out int32 [B, K_sel]
  *               (may be NULL): pool_start[b] + j, ascending, -1 pad
- * With use_fp8 the q rows (b, h) go through the FP8 input path (into the
- * workspace) and are scored from their codes against the cached key codes,
- * as kpool_indexer_topk's FP8 path scores them.
+ * With use_fp8 the q rows (b, h) go through the FP8 input path (inside the
+ * scoring kernel) and are scored from their codes against the cached key
+ * codes, as kpool_indexer_topk's FP8 path scores them.
  * Uses params: num_docs (= B), max_seqlen (a bound on every L_b), num_heads,
  * head_dim, kpool, index_topk, always_select_tail, use_fp8 (head_dim 128),
  * scale; total_tokens and query_chunk are not used.

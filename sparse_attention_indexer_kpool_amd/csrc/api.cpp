@@ -160,7 +160,7 @@ struct DecodeDerived {
   int B, H, D, kpool, k_sel, width, max_pools, tail, fp8;
   int64_t ld;
   float scale;
-  size_t off_qc, off_qs, total;    // workspace: scores, then (FP8) q codes and scales
+  size_t total;                    // workspace: the scores
 };
 
 kpool_status derive_decode(const kpool_params* p, DecodeDerived* d) {
@@ -197,15 +197,7 @@ kpool_status derive_decode(const kpool_params* p, DecodeDerived* d) {
                 d->max_pools, kpool::kMaxSelectPools);
   d->ld = (int64_t)round_up((size_t)std::max(d->max_pools, 1), 64);
   d->scale = p->scale > 0.f ? p->scale : 1.0f / sqrtf((float)d->D);
-  size_t off = round_up((size_t)d->B * d->ld * 4, 256);
-  d->off_qc = d->off_qs = off;
-  if (d->fp8) {
-    d->off_qc = off;
-    off = round_up(off + (size_t)d->B * d->H * 128, 256);
-    d->off_qs = off;
-    off = round_up(off + (size_t)d->B * d->H * 4, 256);
-  }
-  d->total = off;
+  d->total = round_up((size_t)d->B * d->ld * 4, 256);
   return KPOOL_OK;
 }
 
@@ -413,19 +405,10 @@ kpool_status kpool_decode_topk(const kpool_params* p, const void* q, const float
     return fail(KPOOL_E_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, d.total);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   float* scores = reinterpret_cast<float*>(workspace);
-  uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
   (void)hipGetLastError();
   kpool::DecodeLogitsArgs a{};
-  if (d.fp8) {
-    // the FP8 input path on the B H query rows; the cache already holds codes
-    kpool::launch_fp8_quantize(reinterpret_cast<const uint16_t*>(q), d.B * d.H, nullptr,
-                               ws + d.off_qc, reinterpret_cast<float*>(ws + d.off_qs), st);
-    a.q = ws + d.off_qc;
-    a.q_scale = reinterpret_cast<const float*>(ws + d.off_qs);
-    a.k_scale = pooled_scale;
-  } else {
-    a.q = q;
-  }
+  a.q = q;                       // BF16; the FP8 kernel quantises its rows itself
+  if (d.fp8) a.k_scale = pooled_scale;
   a.fp8 = d.fp8;
   a.w = w;
   a.keys = pooled;

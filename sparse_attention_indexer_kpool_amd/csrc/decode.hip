@@ -17,9 +17,9 @@
 // arithmetic is 2 H D FLOP per pool, a few percent of what the matrix cores
 // could do in that time. Still a contraction, so it runs on them:
 // v_mfma_f32_32x32x16_bf16 for a BF16 cache, v_mfma_f32_32x32x64_f8f6f4 on
-// E4M3 codes for an FP8 cache (the q rows quantised first; their scales fold
-// into w', and each key's scale multiplies its head sum, as in the prefill
-// kernel). The A operand is the sequence's H head rows of q (zero rows up to
+// E4M3 codes for an FP8 cache (the q rows quantised first, inside the
+// kernel; their scales fold into w', and each key's scale multiplies its
+// head sum, as in the prefill kernel). The A operand is the sequence's H head rows of q (zero rows up to
 // a multiple of 32), held in registers; the B operand is a block of 32 keys,
 // each lane pair reading adjacent bytes of a key row per step. The epilogue
 // multiplies each lane's 16 head rows by w' = w * scale, clamps at 0, sums
@@ -27,6 +27,7 @@
 
 #include <type_traits>
 
+#include "fp8_row.h"
 #include "kpool_device.h"
 #include "kpool_internal.h"
 
@@ -61,12 +62,37 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_logits_kernel(DecodeLog
   const int piece = (int)blockIdx.x % a.pieces;
   const int L = max(a.seq_lens[b], 0);
   const int n_c = min(L / a.kpool, a.max_pools);
+  if (piece * kDecPoolsPerGroup >= n_c) return;   // the whole workgroup: nothing to score
   const int p_lo = piece * kDecPoolsPerGroup + 32 * wid;   // this wave's first pool
-  if (p_lo >= n_c) return;                         // nothing for this wave (no barrier below)
   const int n = lane & 31, g = lane >> 5;
   const int pool0 = a.pool_start[b];
-  const uint8_t* __restrict__ qb = reinterpret_cast<const uint8_t*>(a.q);
   const uint8_t* __restrict__ kb = reinterpret_cast<const uint8_t*>(a.keys);
+
+  // FP8: the workgroup first takes the sequence's H BF16 q rows through the
+  // FP8 input path (16 lanes per row, the quantiser's layout and arithmetic)
+  // into LDS; the A fragments and row scales are read from there. Every
+  // workgroup of the sequence repeats this (H rows, a few hundred VALU
+  // operations per lane) instead of a separate launch writing the codes.
+  __shared__ __attribute__((aligned(16))) uint8_t q_codes[FP8 ? H * 128 : 16];
+  __shared__ float q_scales[FP8 ? H : 1];
+  if constexpr (FP8) {
+    const int grp = threadIdx.x >> 4, l = threadIdx.x & 15;
+    const uint16_t* __restrict__ qsrc = reinterpret_cast<const uint16_t*>(a.q);
+    for (int r = grp; r < H; r += 64 * kDecWaves / 16) {   // uniform per 16-lane group
+      const uint4 in = *reinterpret_cast<const uint4*>(qsrc + ((size_t)b * H + r) * 128 + l * 8);
+      const uint32_t wv[4] = {in.x, in.y, in.z, in.w};
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = bf16_bits_to_f32((wv[e >> 1] >> (16 * (e & 1))) & 0xffffu);
+      uint32_t packed[2];
+      const int ex = fp8_row_codes(v, l, packed);
+      *reinterpret_cast<uint2*>(q_codes + r * 128 + l * 8) = make_uint2(packed[0], packed[1]);
+      if (l == 0) q_scales[r] = ldexpf(1.0f, ex);
+    }
+    __syncthreads();
+  }
+  if (p_lo >= n_c) return;                         // nothing for this wave (no barrier below)
+  const uint8_t* __restrict__ qb = FP8 ? q_codes : reinterpret_cast<const uint8_t*>(a.q);
 
   auto to_frag = [](const uint4 (&c)[CH]) -> Frag {
     if constexpr (FP8) {
@@ -84,7 +110,8 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_logits_kernel(DecodeLog
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int head = mt * 32 + n;
-    const uint8_t* qrow = qb + ((size_t)b * H + (head < H ? head : 0)) * ROWB;
+    const uint8_t* qrow = FP8 ? qb + (head < H ? head : 0) * ROWB
+                              : qb + ((size_t)b * H + (head < H ? head : 0)) * ROWB;
 #pragma unroll
     for (int s = 0; s < NSTEP; ++s) {
       uint4 c[CH];
@@ -106,7 +133,7 @@ __global__ __launch_bounds__(64 * kDecWaves) void decode_logits_kernel(DecodeLog
       float wv = 0.f;
       if (head < H) {
         wv = a.w[(size_t)b * H + head] * a.scale;
-        if constexpr (FP8) wv *= a.q_scale[(size_t)b * H + head];
+        if constexpr (FP8) wv *= q_scales[head];
       }
       wq[mt][v] = wv;
     }

@@ -54,8 +54,7 @@ void launch_expand(const int32_t* pool_ids, int q_begin, int q_end, const int32_
 // sequence's floor(seq_lens[b] / kpool) cached pools at pooled rows
 // pool_start[b] ...; scores to out [B, ld].
 struct DecodeLogitsArgs {
-  const void* q;               // BF16 [B, H, D], or E4M3 codes [B, H, 128]
-  const float* q_scale;        // FP8: FP32 [B, H] row scales, else null
+  const void* q;               // BF16 [B, H, D] (the FP8 kernel quantises the rows)
   const float* w;              // FP32 [B, H]
   const void* keys;            // BF16 [pooled_rows, D], or E4M3 codes [pooled_rows, 128]
   const float* k_scale;        // FP8: FP32 [pooled_rows] row scales, else null

@@ -134,7 +134,7 @@ def test_decode_workspace():
     assert kp.kpool_decode_workspace_bytes(p) == 64 * 16384 * 4
     assert kp.kpool_decode_workspace_bytes(P(num_docs=3, max_seqlen=4100)) == 3 * 1088 * 4
     p8 = P(num_docs=64, total_tokens=0, max_seqlen=65536, use_fp8=1)
-    assert kp.kpool_decode_workspace_bytes(p8) == 64 * 16384 * 4 + 64 * 32 * 128 + 64 * 32 * 4
+    assert kp.kpool_decode_workspace_bytes(p8) == 64 * 16384 * 4
     assert kp.kpool_decode_workspace_bytes(P(use_fp8=1, head_dim=64)) == 0
     assert kp.kpool_decode_workspace_bytes(P(num_docs=0)) == 0
     assert kp.kpool_decode_workspace_bytes(P(max_seqlen=262148)) == 0
