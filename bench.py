@@ -35,6 +35,18 @@ PEAK_FP8_TFLOPS = 5000.0
 PEAK_HBM_GBS = 8000.0
 
 
+def logits_source_digest() -> str:
+    """SHA-256 of what the logits kernel is built from: logits.hip, the
+    shared device helpers and its argument struct (the rest of the launcher
+    header declares other kernels)."""
+    import re
+    csrc = os.path.join(ROOT, "sparse_attention_indexer_kpool_amd", "csrc")
+    read = lambda f: open(os.path.join(csrc, f), "rb").read()
+    args = re.search(rb"struct LogitsArgs \{.*?\};", read("kpool_internal.h"), re.S)
+    return hashlib.sha256(read("logits.hip") + read("kpool_device.h") +
+                          (args.group(0) if args else b"")).hexdigest()
+
+
 def logits_traffic(wl_name: str):
     """HBM bytes per logits launch from the committed rocprofv3 FETCH_SIZE /
     WRITE_SIZE passes (profiles/logits_kernel_traffic_<workload>.txt), scaled
@@ -48,10 +60,7 @@ def logits_traffic(wl_name: str):
         if ":" in line:
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    csrc = os.path.join(ROOT, "sparse_attention_indexer_kpool_amd", "csrc")
-    src = b"".join(open(os.path.join(csrc, f), "rb").read()
-                   for f in ("logits.hip", "kpool_device.h", "kpool_internal.h"))
-    if hashlib.sha256(src).hexdigest() != kv.get("source_sha256"):
+    if logits_source_digest() != kv.get("source_sha256"):
         return None
     return int(float(kv["hbm_bytes_per_launch"]))
 
