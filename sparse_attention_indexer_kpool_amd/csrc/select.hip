@@ -48,7 +48,16 @@
 namespace kpool {
 
 constexpr int kBins = 1024;         // value-linear bins
-constexpr int kListPerLane = 8;     // list entries per lane of a wave segment
+// List entries per lane of a wave segment. The 256-thread shapes take six:
+// those of up to 10 groups, whose registers allow eight workgroups per CU,
+// then also fit eight in the CU's 160 KB of LDS (19.6 KB each instead of
+// 23.7 KB), and the longer ones lose nothing (64K step, selection 0.711 ->
+// 0.676 ms). The wider shapes keep eight: a wave's segment holds its share
+// of the sampled level's margin, and a segment that overflows sends the row
+// to the slow general path.
+__host__ __device__ constexpr int list_per_lane(int nt) {
+  return nt == 256 ? 6 : 8;
+}
 constexpr int kLogKeyBins = 10;     // key-space bins of the general path
 constexpr int kKeyBins = 1 << kLogKeyBins;
 
@@ -150,6 +159,7 @@ template <int NT, int G, bool VEC4>
 __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
   constexpr int NW = NT / 64;
   constexpr int E = 4 * G;                       // values per thread
+  constexpr int LPL = list_per_lane(NT);
   using Sh = SelectShared<NT, G>;
   __shared__ Sh sh;
   extern __shared__ __attribute__((aligned(16))) uint8_t dyn[];
@@ -316,7 +326,7 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
     // prefix, the running count stays scalar, and a (value, index) pair is one
     // 8-byte LDS write. A wave that overflows its segment keeps writing into
     // the segment's last slot; its count records the overflow.
-    const int seg_cap = list_cap / NW;                 // at most 64 * kListPerLane
+    const int seg_cap = list_cap / NW;                 // at most 64 * LPL
     uint2* seg = list + wid * seg_cap;
     int running = 0;
     forget(v);
@@ -355,10 +365,10 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
       // ---- 4. exact threshold on the list. Each wave takes its own segment
       // into registers once (lane l holds entries l, l + 64, ...); min / max,
       // histogram, candidate gather and marking all work from there.
-      float ev[kListPerLane];
-      int ei[kListPerLane];
+      float ev[LPL];
+      int ei[LPL];
 #pragma unroll
-      for (int i = 0; i < kListPerLane; ++i) {
+      for (int i = 0; i < LPL; ++i) {
         const int j = lane + 64 * i;
         const uint2 e = seg[j < running ? j : 0];
         ev[i] = j < running ? __uint_as_float(e.x) : NAN;   // list values are never NaN
@@ -374,7 +384,7 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
       } else {
         const float linv = (float)kBins / lrange;
 #pragma unroll
-        for (int i = 0; i < kListPerLane; ++i)
+        for (int i = 0; i < LPL; ++i)
           if (ev[i] == ev[i]) atomicAdd(&sh.hist[vbin(ev[i], lmn, linv)], 1u);
         __syncthreads();
         find_bin<NT, G, kBins>(sh, k_sel);
@@ -385,7 +395,7 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
           fast = false;                                // crowded bin: general path
         } else {
 #pragma unroll
-          for (int i = 0; i < kListPerLane; ++i) {
+          for (int i = 0; i < LPL; ++i) {
             if (ev[i] == ev[i] && vbin(ev[i], lmn, linv) == bstar) {
               const int slot = atomicAdd(&sh.cand_cnt, 1);
               sh.cand_key[slot] = f32_order_key(ev[i]);
@@ -422,7 +432,7 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
           }
           // ---- 5a. chosen list entries set their bitmap bits
 #pragma unroll
-          for (int i = 0; i < kListPerLane; ++i) {
+          for (int i = 0; i < LPL; ++i) {
             if (ev[i] == ev[i]) {
               const uint32_t kx = f32_order_key(ev[i]);
               if (kx > tk || (kx == tk && ei[i] <= ti)) atomicOr(&sh.bitmap[ei[i] >> 5], 1u << (ei[i] & 31));
@@ -571,13 +581,14 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
   write_tail();
 }
 
-// LDS list capacity: one segment of 64 * kListPerLane entries per wave. The
+// LDS list capacity: one segment of 64 * list_per_lane entries per wave. The
 // sampled level keeps about 1.25 K_sel plus a few sample standard deviations
 // in all, spread evenly over the waves; rows whose share overflows a segment
 // take the general path.
 // A wave of a G-group row holds at most 4 G values, so short rows need less.
 static int list_capacity(int nt, int g) {
-  return (nt / 64) * 64 * (4 * g < kListPerLane ? 4 * g : kListPerLane);
+  const int lpl = list_per_lane(nt);
+  return (nt / 64) * 64 * (4 * g < lpl ? 4 * g : lpl);
 }
 
 template <int NT, int G>
