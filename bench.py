@@ -30,8 +30,10 @@ import torch  # noqa: E402
 import workloads as wlm  # noqa: E402
 
 METRIC = "KPool indexer queries/s at 64K ctx; logits TFLOP/s as % of MFMA peak"
-PEAK_BF16_TFLOPS = 2500.0
-PEAK_FP8_TFLOPS = 5000.0
+# MI355X dense peaks: 256 CUs at 2.4 GHz, 4096 BF16 (8192 FP8) MFMA FLOP per
+# CU per clock (published as 2.5 and 5.0 PFLOP/s); HBM3E 8 TB/s.
+PEAK_BF16_TFLOPS = 256 * 2.4e9 * 4096 / 1e12      # 2516.6
+PEAK_FP8_TFLOPS = 2 * PEAK_BF16_TFLOPS            # 5033.2
 PEAK_HBM_GBS = 8000.0
 
 
@@ -106,7 +108,7 @@ class Path:
         self.ws = torch.empty(max(kp.kpool_workspace_bytes(self.p), 256), dtype=torch.uint8,
                               device=dev)
         self.tok = torch.empty(T, self.p.width, dtype=torch.int32, device=dev)
-        self.qc = self.p.query_chunk if self.p.query_chunk > 0 else 4096
+        self.qc = kp.kpool_query_chunk_rows(self.p)
         self.ld = kp.kpool_logits_ld(self.p)
 
     def step(self):
@@ -261,45 +263,28 @@ def decode_bench(reps: int, B: int = 64, L: int = 65536, fp8: bool = False):
             "note": "keys read once, scores written and read once, token rows written"}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="long_T65536_H32_D128")
-    ap.add_argument("--cpu-rows", type=int, default=12288)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-decode", action="store_true",
-                    help="skip the serving-step measurement (kpool_decode_topk)")
-    ap.add_argument("--copy-mib", type=int, default=0,
-                    help="after the bench, run 3 device copies of this many MiB (a kernel of "
-                         "known traffic that calibrates the HBM byte counters of a profiler)")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the indexer here runs "
-              "on a single device and has no multi-GPU path.", file=sys.stderr)
-        sys.exit(2)
-    rank = int(os.environ.get("RANK", "0"))
-
-    wl = wlm.workload(int(args.workload)) if args.workload.isdigit() else wlm.workload(args.workload)
+def measure_workload(wl, steps: int, warmup: int):
+    """One workload: the whole step timed over `steps` steps after `warmup`
+    untimed ones, then each phase alone with the same launches. Returns
+    (inputs, ms per step, the line's figures for this workload)."""
     log(f"inputs {wl.name}")
     inp = wlm.make_inputs(wl)
     path = Path(inp)
     T = inp.T
     tot_nc, need_nc, need_rows = causal_counts(inp.doc_lengths, wl.kpool, wl.k_sel)
 
-    log(f"warmup {args.warmup}")
-    for _ in range(args.warmup):
+    log(f"{wl.name}: warmup {warmup}")
+    for _ in range(warmup):
         path.step()
     torch.cuda.synchronize()
-    log(f"timing {args.steps} steps")
-    ms = time_region(path.step, args.steps, warm=0)
-    log(f"{ms:.3f} ms/step")
+    log(f"{wl.name}: timing {steps} steps")
+    ms = time_region(path.step, steps, warm=0)
+    log(f"{wl.name}: {ms:.4f} ms/step")
 
     # phases, each timed live on the launch stream with the same launches
     logits = torch.empty(path.qc, path.ld, dtype=torch.float32, device="cuda:0")
     ids = torch.empty(T, wl.k_sel, dtype=torch.int32, device="cuda:0")
-    reps = max(3, min(args.steps, 10))
+    reps = max(3, min(steps, 10))
     path.phase_logits(logits)      # also leaves the pooled keys / fp8 buffers in place
     ms_compress = path.time_compress_cold()
     ms_logits = time_region(lambda: path.phase_logits(logits), reps)
@@ -315,6 +300,7 @@ def main():
                 torch.empty(max(P, 1), 128, dtype=torch.uint8, device="cuda:0"),
                 torch.empty(max(P, 1), dtype=torch.float32, device="cuda:0"), P)
         ms_fp8 = time_region(lambda: path.phase_fp8_quant(bufs), reps)
+    del logits, ids
     n_chunks = (T + path.qc - 1) // path.qc
 
     flops = 2.0 * wl.H * wl.D * need_nc
@@ -326,8 +312,62 @@ def main():
     by_expand = 4 * T * (wl.k_sel + wl.width)
     by_fp8 = (T * wl.H + P) * (256 + 128 + 4)
 
-    def gbs(b, m):
-        return round(b / (m * 1e-3) / 1e9, 1)
+    def hbm(b, m):
+        return {"bytes": b, "GB/s": round(b / (m * 1e-3) / 1e9, 1),
+                "frac": round(b / (m * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+
+    fig = {
+        "config": {"workload": wl.name, "T": T, "H": wl.H, "D": wl.D, "kpool": wl.kpool,
+                   "index_topk": wl.index_topk, "always_select_tail": wl.tail,
+                   "query_chunk": path.qc, "docs": len(inp.doc_lengths), "fp8": wl.fp8},
+        "ms_per_step": round(ms, 4),
+        "queries_per_s": round(T / (ms * 1e-3), 1),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak, 1),
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": logits_traffic(wl.name),
+                     "kernel": "logits_kernel", "launches_per_step": n_chunks,
+                     "algorithmic_flops_per_step": flops},
+        "phases_ms": {"compress": round(ms_compress, 4), "logits": round(ms_logits, 4),
+                      "select_expand": round(ms_select_expand, 4),
+                      "select": round(ms_select, 4), "expand": round(ms_expand, 4)},
+        "phases_hbm": {"compress": hbm(by_compress, ms_compress),
+                       "select_expand": hbm(by_select_expand, ms_select_expand),
+                       "select": hbm(by_select, ms_select),
+                       "expand": hbm(by_expand, ms_expand)},
+    }
+    if ms_fp8 is not None:
+        fig["phases_ms"]["fp8_quant"] = round(ms_fp8, 4)
+        fig["phases_hbm"]["fp8_quant"] = hbm(by_fp8, ms_fp8)
+    del path
+    torch.cuda.empty_cache()
+    return inp, ms, fig
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="long_T65536_H32_D128")
+    ap.add_argument("--cpu-rows", type=int, default=12288)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip the serving-step measurement (kpool_decode_topk)")
+    ap.add_argument("--no-others", action="store_true",
+                    help="skip the other workloads (FP8 and the short ones) on the line")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="after the bench, run 3 device copies of this many MiB (a kernel of "
+                         "known traffic that calibrates the HBM byte counters of a profiler)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the indexer here runs "
+              "on a single device and has no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+    rank = int(os.environ.get("RANK", "0"))
+
+    wl = wlm.workload(int(args.workload)) if args.workload.isdigit() else wlm.workload(args.workload)
+    inp, ms, fig = measure_workload(wl, args.steps, args.warmup)
+    T = inp.T
 
     out = {
         "metric": METRIC,
@@ -342,39 +382,23 @@ def main():
         "vs_baseline": None,
         "dtype": "fp8" if wl.fp8 else "bf16",
         "data": "synthetic",
-        "config": {"workload": wl.name, "T": T, "H": wl.H, "D": wl.D, "kpool": wl.kpool,
-                   "index_topk": wl.index_topk, "always_select_tail": wl.tail,
-                   "query_chunk": path.qc, "docs": len(inp.doc_lengths), "fp8": wl.fp8},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
-                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "traffic": logits_traffic(wl.name),
-                     "kernel": "logits_kernel", "launches_per_step": n_chunks,
-                     "algorithmic_flops_per_step": flops},
-        "phases_ms": {"compress": round(ms_compress, 4), "logits": round(ms_logits, 4),
-                      "select_expand": round(ms_select_expand, 4),
-                      "select": round(ms_select, 4), "expand": round(ms_expand, 4)},
-        "phases_hbm": {
-            "compress": {"bytes": by_compress, "GB/s": gbs(by_compress, ms_compress),
-                         "frac": round(by_compress / (ms_compress * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
-            "select_expand": {"bytes": by_select_expand,
-                              "GB/s": gbs(by_select_expand, ms_select_expand),
-                              "frac": round(by_select_expand / (ms_select_expand * 1e-3) / 1e9
-                                            / PEAK_HBM_GBS, 4)},
-            "select": {"bytes": by_select, "GB/s": gbs(by_select, ms_select),
-                       "frac": round(by_select / (ms_select * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
-            "expand": {"bytes": by_expand, "GB/s": gbs(by_expand, ms_expand),
-                       "frac": round(by_expand / (ms_expand * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
-        },
+        "config": fig["config"],
+        "roofline": fig["roofline"],
+        "phases_ms": fig["phases_ms"],
+        "phases_hbm": fig["phases_hbm"],
     }
-    if ms_fp8 is not None:
-        out["phases_ms"]["fp8_quant"] = round(ms_fp8, 4)
-        out["phases_hbm"]["fp8_quant"] = {
-            "bytes": by_fp8, "GB/s": gbs(by_fp8, ms_fp8),
-            "frac": round(by_fp8 / (ms_fp8 * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
     if not args.no_decode and wl.name == "long_T65536_H32_D128":
+        reps = max(3, min(args.steps, 10))
         log("decode step, 64 sequences of 64K tokens")
         out["decode"] = decode_bench(reps)
         out["decode_fp8"] = decode_bench(reps, fp8=True)
+    if not args.no_others and wl.name == "long_T65536_H32_D128":
+        # the FP8 input path and the short workloads, each timed the same way
+        for key, other in (("fp8", "fp8_T32768_H32_D128"), ("tiny", "tiny_T256_H4_D64"),
+                           ("single_4k", "single_T4096_H32_D128"),
+                           ("packed8", "packed8_H32_D128")):
+            _, _, f2 = measure_workload(wlm.workload(other), args.steps, args.warmup)
+            out[key] = f2
     if rank == 0 and not args.no_cpu_baseline:
         log(f"cpu baseline on {args.cpu_rows} rows")
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_rows)

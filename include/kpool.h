@@ -31,9 +31,11 @@
  * on failure it enqueues nothing, leaves the outputs untouched and returns a
  * status, with a description in kpool_last_error() (per calling thread). A
  * launch failure reported by the HIP runtime returns KPOOL_E_LAUNCH.
- * Pointers must be 16-byte aligned (cu_seqlens, cu_pools, w, ape and
- * row_scale: 4-byte aligned). The contents of cu_seqlens are a precondition
- * that the host cannot see: for contents that break it, outputs are
+ * Pointers must be 16-byte aligned, except the int32 and FP32 arrays
+ * cu_seqlens, cu_pools, w, row_scale, pooled_scale, dst_rows, pool_start,
+ * seq_lens, token_base and out_pool_idx, which need 4-byte alignment (ape,
+ * read 16 bytes at a time, needs 16). The contents of cu_seqlens are a
+ * precondition that the host cannot see: for contents that break it, outputs are
  * unspecified, but every kernel keeps its reads and writes inside the
  * documented extents of the buffers.
  */
@@ -67,7 +69,8 @@ typedef struct {
   int32_t index_topk;         /* >= kpool                                          */
   int32_t always_select_tail; /* 0 / 1                                             */
   int32_t use_fp8;            /* 0 / 1: FP8 input path                             */
-  int32_t query_chunk;        /* query rows per logits tile; 0 = default 4096      */
+  int32_t query_chunk;        /* query rows per logits tile; 0 = as many as fit a  */
+                              /* 256 MiB tile (kpool_query_chunk_rows)             */
   float   scale;              /* score scale inside the ReLU; 0 = head_dim^-1/2    */
 } kpool_params;
 
@@ -83,6 +86,11 @@ size_t kpool_workspace_bytes(const kpool_params* p);
 /* Row stride, in floats, of the logits tiles of kpool_logits / kpool_select:
  * max_pools rounded up to a multiple of 64. */
 int64_t kpool_logits_ld(const kpool_params* p);
+
+/* Query rows per logits tile that kpool_indexer_topk uses: query_chunk when
+ * it is set, else floor(256 MiB / (4 * kpool_logits_ld(p))), capped at T
+ * (0 when T == 0 or the parameters are invalid). */
+int32_t kpool_query_chunk_rows(const kpool_params* p);
 
 /* Step 1, key compression ([MLM] section 3; [SKY] k-pool commit). For each
  * document b, pool p < P_b and dimension d, with slot tokens

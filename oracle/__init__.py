@@ -19,5 +19,4 @@ from .kpool_oracle import (  # noqa: F401
     pow2_row_exponent,
     row_scores,
     select_pools,
-    tail_len,
 )

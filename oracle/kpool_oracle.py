@@ -175,11 +175,6 @@ def causal_pools(i: int, kpool: int) -> int:
     return (i + 1) // kpool
 
 
-def tail_len(i: int, kpool: int, tail_on: bool) -> int:
-    """Tokens of the query's incomplete causal pool (0 .. kpool - 1)."""
-    return (i + 1) % kpool if tail_on else 0
-
-
 # ---------------------------------------------------------------------------
 # Step 1: key compression ([MLM] section 3; [SKY] k-pool commit)
 # ---------------------------------------------------------------------------

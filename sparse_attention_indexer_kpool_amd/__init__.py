@@ -92,6 +92,8 @@ def lib() -> ctypes.CDLL:
         L.kpool_workspace_bytes.argtypes = [P]
         L.kpool_logits_ld.restype = ctypes.c_int64
         L.kpool_logits_ld.argtypes = [P]
+        L.kpool_query_chunk_rows.restype = ctypes.c_int32
+        L.kpool_query_chunk_rows.argtypes = [P]
         L.kpool_compress.restype = ctypes.c_int
         L.kpool_compress.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
         L.kpool_indexer_topk.restype = ctypes.c_int
@@ -120,7 +122,8 @@ def lib() -> ctypes.CDLL:
     return _lib
 
 
-EXPORTS = ["kpool_abi_version", "kpool_workspace_bytes", "kpool_logits_ld", "kpool_compress",
+EXPORTS = ["kpool_abi_version", "kpool_workspace_bytes", "kpool_logits_ld",
+           "kpool_query_chunk_rows", "kpool_compress",
            "kpool_indexer_topk", "kpool_logits", "kpool_select", "kpool_select_expand",
            "kpool_expand",
            "kpool_fp8_quantize", "kpool_compress_pools", "kpool_decode_workspace_bytes",
@@ -160,6 +163,10 @@ def kpool_workspace_bytes(p: Params) -> int:
 
 def kpool_logits_ld(p: Params) -> int:
     return int(lib().kpool_logits_ld(ctypes.byref(p.c())))
+
+
+def kpool_query_chunk_rows(p: Params) -> int:
+    return int(lib().kpool_query_chunk_rows(ctypes.byref(p.c())))
 
 
 def kpool_compress(p: Params, k, gate, ape, cu_seqlens, cu_pools, pooled, stream=None) -> None:

@@ -35,7 +35,9 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-constexpr int kDefaultQueryChunk = 4096;
+// Default query chunk: as many rows as fit a logits tile of this many bytes
+// (4096 rows of 16384 pools at a 64K context; the whole batch for short ones).
+constexpr size_t kDefaultTileBytes = size_t(256) << 20;
 
 struct Derived {
   int B, T, H, D, kpool, topk, k_sel, width, max_pools, qc, tail, fp8;
@@ -86,8 +88,10 @@ kpool_status derive(const kpool_params* p, Derived* d, bool need_heads) {
                 d->max_pools, kpool::kMaxSelectPools);
   d->ld = (int64_t)round_up((size_t)std::max(d->max_pools, 1), 64);
   d->scale = p->scale > 0.f ? p->scale : 1.0f / sqrtf((float)d->D);
-  int qc = p->query_chunk > 0 ? p->query_chunk : kDefaultQueryChunk;
-  d->qc = std::max(1, std::min(qc, std::max(d->T, 1)));
+  const int64_t qc = p->query_chunk > 0
+                       ? (int64_t)p->query_chunk
+                       : (int64_t)(kDefaultTileBytes / ((size_t)d->ld * sizeof(float)));
+  d->qc = (int)std::max<int64_t>(1, std::min<int64_t>(qc, std::max(d->T, 1)));
   // workspace layout (256-byte aligned pieces)
   size_t off = 0;
   d->off_logits = off;
@@ -217,6 +221,12 @@ int64_t kpool_logits_ld(const kpool_params* p) {
   Derived d;
   if (derive(p, &d, true) != KPOOL_OK) return 0;
   return d.ld;
+}
+
+int32_t kpool_query_chunk_rows(const kpool_params* p) {
+  Derived d;
+  if (derive(p, &d, true) != KPOOL_OK) return 0;
+  return d.T > 0 ? d.qc : 0;
 }
 
 kpool_status kpool_compress(const kpool_params* p, const void* k, const void* gate,

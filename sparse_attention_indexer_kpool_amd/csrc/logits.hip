@@ -33,24 +33,12 @@
 
 namespace kpool {
 
-// FP8 MFMA K: 64 uses v_mfma_f32_32x32x64_f8f6f4, 16 uses
-// v_mfma_f32_32x32x16_fp8_fp8.
-#ifndef KPOOL_FP8_MFMA_K
-#define KPOOL_FP8_MFMA_K 64
-#endif
-constexpr int kFp8K = KPOOL_FP8_MFMA_K;
-static_assert(kFp8K == 64 || kFp8K == 16, "FP8 MFMA K");
+// FP8 MFMA K: v_mfma_f32_32x32x64_f8f6f4 takes 64 K values per instruction.
+constexpr int kFp8K = 64;
 
 constexpr int kLogitsWaves = 8;
-#ifndef KPOOL_POOL_TILE
-#define KPOOL_POOL_TILE 64
-#endif
-#ifndef KPOOL_EPI_CHAINS
-#define KPOOL_EPI_CHAINS 1
-#endif
-constexpr int kPoolTile = KPOOL_POOL_TILE;   // pools per LDS stage (32-wide MFMA units)
+constexpr int kPoolTile = 64;                 // pools per LDS stage (two 32-wide MFMA units)
 constexpr int kUnits = kPoolTile / 32;
-constexpr int kEpiChains = KPOOL_EPI_CHAINS;
 
 template <int H, int D, bool FP8>
 struct LogitsCfg {
@@ -316,8 +304,7 @@ __global__ __launch_bounds__(64 * kLogitsWaves) void logits_kernel(LogitsArgs a)
   // ---- A operand: this wave's (query, head) rows, held for the whole launch.
   // Row m of tile mt is flat row mt * 32 + m of the wave: query flat / H,
   // head flat % H. Lane (n, g) holds row n, K slice [g D/2, (g + 1) D/2).
-  using Frag = typename std::conditional<FP8, typename std::conditional<kFp8K == 64, i32x8_t, long>::type,
-                                         bf16x8_t>::type;
+  using Frag = typename std::conditional<FP8, i32x8_t, bf16x8_t>::type;
   Frag afrag[MT][C::NSTEP];
   float wq[MT][16];          // w' of the 16 accumulator rows this lane holds
   // the q rows, head weights (and the first key tile) have arrived in LDS
@@ -346,16 +333,13 @@ __global__ __launch_bounds__(64 * kLogitsWaves) void logits_kernel(LogitsArgs a)
     const uint8_t* blk = tile1 + wid * C::A_BYTES + mt * 32 * C::ROWB;
 #pragma unroll
     for (int s = 0; s < C::NSTEP; ++s) {
-      if constexpr (FP8 && kFp8K == 64) {
+      if constexpr (FP8) {
         uint4 lo4 = *reinterpret_cast<const uint4*>(blk + boff[2 * s]);
         uint4 hi4 = *reinterpret_cast<const uint4*>(blk + boff[2 * s + 1]);
         if (!ok) lo4 = hi4 = make_uint4(0, 0, 0, 0);
         i32x8_t f = {(int)lo4.x, (int)lo4.y, (int)lo4.z, (int)lo4.w,
                      (int)hi4.x, (int)hi4.y, (int)hi4.z, (int)hi4.w};
         afrag[mt][s] = f;
-      } else if constexpr (FP8) {
-        const long v = *reinterpret_cast<const long*>(blk + boff[s >> 1] + (s & 1) * 8);
-        afrag[mt][s] = ok ? v : 0l;
       } else {
         uint4 v = *reinterpret_cast<const uint4*>(blk + boff[s]);
         if (!ok) v = make_uint4(0, 0, 0, 0);
@@ -425,16 +409,9 @@ __global__ __launch_bounds__(64 * kLogitsWaves) void logits_kernel(LogitsArgs a)
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
           for (int qq = 0; qq < QPT; ++qq) {
-            constexpr int NC = kEpiChains < RPQ ? kEpiChains : RPQ;
-            float cs[NC];
+            float s = wq[mt][qq * RPQ] * relu(acc[mt][qq * RPQ]);
 #pragma unroll
-            for (int c = 0; c < NC; ++c) cs[c] = wq[mt][qq * RPQ + c] * relu(acc[mt][qq * RPQ + c]);
-#pragma unroll
-            for (int j = qq * RPQ + NC; j < (qq + 1) * RPQ; ++j)
-              cs[j % NC] += wq[mt][j] * relu(acc[mt][j]);
-            float s = cs[0];
-#pragma unroll
-            for (int c = 1; c < NC; ++c) s += cs[c];
+            for (int j = qq * RPQ + 1; j < (qq + 1) * RPQ; ++j) s += wq[mt][j] * relu(acc[mt][j]);
             tot[mt * QPT + qq] = s;
           }
         // pair queries 2i and 2i+1: after the swap the low half-wave holds
@@ -463,12 +440,7 @@ __global__ __launch_bounds__(64 * kLogitsWaves) void logits_kernel(LogitsArgs a)
       const uint8_t* unit = tb + np * 32 * C::ROWB;     // constant: folds into the offset
 #pragma unroll
       for (int s = 0; s < C::NSTEP; ++s) {
-        if constexpr (FP8 && kFp8K == 16) {
-          const long bf = *reinterpret_cast<const long*>(unit + boff[s >> 1] + (s & 1) * 8);
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt)
-            acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(afrag[mt][s], bf, acc[mt], 0, 0, 0);
-        } else if constexpr (FP8) {
+        if constexpr (FP8) {
           const uint4 lo4 = *reinterpret_cast<const uint4*>(unit + boff[2 * s]);
           const uint4 hi4 = *reinterpret_cast<const uint4*>(unit + boff[2 * s + 1]);
           i32x8_t bf = {(int)lo4.x, (int)lo4.y, (int)lo4.z, (int)lo4.w,
@@ -552,10 +524,6 @@ __global__ void fill_kernel(float* __restrict__ out, size_t count, float v) {
   for (; i < count; i += stride) out[i] = v;
 }
 
-#ifndef KPOOL_LOGITS_PIECES
-#define KPOOL_LOGITS_PIECES 0
-#endif
-
 template <int H, int D, bool FP8>
 static void launch_hdf(LogitsArgs a, hipStream_t st) {
   constexpr int QPB = LogitsCfg<H, D, FP8>::QPB;
@@ -569,7 +537,7 @@ static void launch_hdf(LogitsArgs a, hipStream_t st) {
   // context (16384 pools, BF16) it gains about 1 %, and it loses at 8192
   // pools on the FP8 path, whose sweep is half as long per pool.
   const long sweep = (long)a.max_pools * (FP8 ? 1 : 2);
-  a.pieces = KPOOL_LOGITS_PIECES > 0 ? KPOOL_LOGITS_PIECES : (sweep >= 32768 ? 2 : 1);
+  a.pieces = sweep >= 32768 ? 2 : 1;
   const int groups = ((rows + QPB - 1) / QPB + 7) / 8;
   logits_kernel<H, D, FP8><<<groups * 8 * a.pieces, 64 * kLogitsWaves, 0, st>>>(a);
 }

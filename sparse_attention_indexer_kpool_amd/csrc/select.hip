@@ -665,12 +665,9 @@ void launch_select_decode(const float* scores, int64_t ld, int B, const int32_t*
   a.dec_len = seq_lens;
   a.dec_pool0 = pool_start;
   a.dec_base = token_base;
-#ifndef KPOOL_DECODE_WIDE_ROWS
-#define KPOOL_DECODE_WIDE_ROWS 512
-#endif
   // A decode batch can have fewer rows than the GPU has CUs; then the time is
   // one row's latency, which 1024 threads per row shorten
-  if (B <= KPOOL_DECODE_WIDE_ROWS) {
+  if (B <= 512) {
     const int mp = a.max_pools;
     if (mp <= 4096) launch_sel<1024, 1>(a, st);
     else if (mp <= 8192) launch_sel<1024, 2>(a, st);

@@ -48,6 +48,15 @@ def test_workspace_and_ld():
     assert kp.kpool_logits_ld(P(max_seqlen=4097, total_tokens=5000)) == 1024
     assert kp.kpool_logits_ld(P(max_seqlen=4100, total_tokens=5000)) == 1088
     assert kp.kpool_workspace_bytes(P(total_tokens=0, max_seqlen=0)) == 0
+    # rows per logits tile: query_chunk when set, else what fits 256 MiB
+    assert kp.kpool_query_chunk_rows(P()) == 4096
+    assert kp.kpool_query_chunk_rows(P(query_chunk=0)) == 4096          # 16384 pools
+    assert kp.kpool_query_chunk_rows(P(query_chunk=0, total_tokens=32768, max_seqlen=32768)) == 8192
+    assert kp.kpool_query_chunk_rows(P(query_chunk=0, total_tokens=19679, max_seqlen=3789)) == 19679
+    assert kp.kpool_query_chunk_rows(P(query_chunk=333)) == 333
+    assert kp.kpool_query_chunk_rows(P(query_chunk=10 ** 6)) == 65536   # capped at T
+    assert kp.kpool_query_chunk_rows(P(total_tokens=0, max_seqlen=0)) == 0
+    assert kp.kpool_workspace_bytes(P(query_chunk=0, total_tokens=19679, max_seqlen=3789)) >= 19679 * 960 * 4
     # unsupported or invalid parameters size to 0
     assert kp.kpool_workspace_bytes(P(num_heads=12)) == 0
     assert kp.kpool_workspace_bytes(P(max_seqlen=70000)) == 0
@@ -125,6 +134,35 @@ def test_pointer_checks():
     assert raw("kpool_fp8_quantize", FAKE, 4, None, FAKE, None) == kp.KPOOL_E_INVALID
     # null params
     assert raw("kpool_indexer_topk", None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, FAKE, None, None) == kp.KPOOL_E_INVALID
+
+
+@raw_calls
+def test_alignment_rule_of_the_header():
+    """The header's alignment rule: ape needs 16 bytes (it is read as 16-byte
+    vectors), the int32 / FP32 arrays 4 bytes; a 4-byte-aligned array passes
+    its own check and validation fails later, on the next argument."""
+    p = P()
+    # kpool_compress(p, k, gate, ape, cu_seqlens, cu_pools, pooled, stream)
+    assert raw("kpool_compress", pref(p), FAKE, FAKE, FAKE + 4, FAKE, FAKE, FAKE, None) == kp.KPOOL_E_INVALID
+    assert "ape is not 16-byte aligned" in kp.kpool_last_error()
+    assert raw("kpool_compress", pref(p), FAKE, FAKE, FAKE + 8, FAKE, FAKE, FAKE, None) == kp.KPOOL_E_INVALID
+    assert "ape" in kp.kpool_last_error()
+    # cu_seqlens / cu_pools at 4-byte offsets pass; the misaligned pooled fails next
+    assert raw("kpool_compress", pref(p), FAKE, FAKE, FAKE, FAKE + 4, FAKE + 4, FAKE + 4, None) == kp.KPOOL_E_INVALID
+    assert "pooled is not 16-byte aligned" in kp.kpool_last_error()
+    assert raw("kpool_compress", pref(p), FAKE, FAKE, FAKE, FAKE + 2, FAKE, FAKE, None) == kp.KPOOL_E_INVALID
+    assert "cu_seqlens is not 4-byte aligned" in kp.kpool_last_error()
+    # compress_pools: ape 16, dst_rows 4
+    assert raw("kpool_compress_pools", pref(p), FAKE, FAKE, FAKE + 4, 4, FAKE, 10, FAKE, None, None) == kp.KPOOL_E_INVALID
+    assert "ape is not 16-byte aligned" in kp.kpool_last_error()
+    assert raw("kpool_compress_pools", pref(p), FAKE, FAKE, FAKE, 4, FAKE + 4, 10, FAKE + 4, None, None) == kp.KPOOL_E_INVALID
+    assert "pooled is not 16-byte aligned" in kp.kpool_last_error()
+    # the indexer: w at a 4-byte offset passes; a misaligned q fails
+    ws = kp.kpool_workspace_bytes(p)
+    assert raw("kpool_indexer_topk", pref(p), FAKE + 4, FAKE, FAKE, FAKE, FAKE, FAKE, ws, FAKE, None, None) == kp.KPOOL_E_INVALID
+    assert "q is not 16-byte aligned" in kp.kpool_last_error()
+    assert raw("kpool_indexer_topk", pref(p), FAKE, FAKE + 4, FAKE, FAKE + 4, FAKE + 4, FAKE, ws, FAKE + 8, None, None) == kp.KPOOL_E_INVALID
+    assert "out_token_idx is not 16-byte aligned" in kp.kpool_last_error()
 
 
 def test_decode_workspace():

@@ -1,16 +1,20 @@
 """GPU parity of the serving entry points, through the C ABI, against the CPU
 oracle on the same seeded inputs:
   compress_pools  pooled rows of pools given by their slot tokens, written to
-                  scattered cache rows: bit-identical to the rows
-                  kpool_compress writes for the same tokens (and within the
-                  oracle's 1 BF16 ulp); rows outside the cache are skipped
+                  scattered cache rows: within 1 BF16 ulp (plus the FP32
+                  cancellation floor) of oracle.compress of the same slot
+                  tokens, and bit-identical to the rows kpool_compress writes
+                  for them; rows outside the cache are skipped
   decode_topk     pool sets vs the oracle's decode rows (oracle scores from the
                   same cached keys): equal except pools within 1e-3 relative of
                   the k-th score; token rows equal the oracle's expansion of the
                   GPU's pool ids exactly; the last token of every document of a
                   packed batch gets the prefill indexer's row
-  FP8 cache       compress_pools codes and scales bit-identical to
-                  kpool_fp8_quantize of kpool_compress's rows; FP8 decode vs the
+  FP8 cache       compress_pools codes and scales bit-identical to the
+                  oracle's FP8 input path (oracle.fp8_quantize_rows) applied to
+                  the BF16 pooled rows of the same pools, and, on every pool
+                  whose BF16 row equals the oracle's, to the oracle's whole chain
+                  (oracle.compress, then oracle.fp8_quantize_rows); FP8 decode vs the
                   oracle's FP8 decode (q and keys through the oracle's own FP8
                   input path) and vs the FP8 prefill row of each last token
 """
@@ -19,6 +23,7 @@ import pytest
 import torch
 
 import oracle
+import pins
 import workloads as wlm
 from gpu_common import DEV, Dev, log, oracle_inputs, sets_match_up_to_ties
 
@@ -181,12 +186,20 @@ def test_compress_pools_matches_compress(kpool, D):
     torch.cuda.synchronize()
     got = cache.view(torch.int16).cpu().numpy()
     ref_bits = d.pooled.view(torch.int16).cpu().numpy()
+    # the oracle on the same slot tokens: one document of N * kpool tokens
+    ks_np, gs_np = d.inp.k[tok_idx].float().numpy(), d.inp.gate[tok_idx].float().numpy()
+    ape_np = d.inp.ape.numpy()
+    cu1 = np.array([0, N * kpool], np.int64)
+    ref_orc, _ = oracle.compress(ks_np, gs_np, ape_np, cu1, kpool)
+    floor = pins.pooled_fp32_floor(ks_np, gs_np, ape_np, cu1, kpool)
+    ok_rows = [n for n in range(N) if 0 <= int(dst[n]) < cap]
+    got_rows = cache[dst[ok_rows].long().to(DEV)].float().cpu().numpy()
+    pins.assert_within_bf16_ulps(got_rows, ref_orc[ok_rows], 1, floor[ok_rows])
     written = set()
-    for n in range(N):
+    for n in ok_rows:
         r = int(dst[n])
-        if 0 <= r < cap:
-            assert np.array_equal(got[r], ref_bits[int(pick[n])]), n
-            written.add(r)
+        assert np.array_equal(got[r], ref_bits[int(pick[n])]), n
+        written.add(r)
     untouched = [r for r in range(cap) if r not in written]
     assert np.all(got[untouched] == 0x7F7F)
 
@@ -262,16 +275,38 @@ def test_compress_pools_fp8_matches_quantised_compress(kpool):
     p = kp.Params(num_docs=1, total_tokens=1200, max_seqlen=1200, num_heads=4, head_dim=128,
                   kpool=kpool, index_topk=64, use_fp8=1)
     kp.kpool_compress_pools(p, k_slots, g_slots, d.ape, N, dst.to(DEV), codes, pooled_scale=scales)
+    # the same pools in BF16, through the same entry point
+    bf_p = kp.Params(num_docs=1, total_tokens=1200, max_seqlen=1200, num_heads=4, head_dim=128,
+                     kpool=kpool, index_topk=64, use_fp8=0)
+    bf_cache = torch.zeros((cap, 128), dtype=torch.bfloat16, device=DEV)
+    kp.kpool_compress_pools(bf_p, k_slots, g_slots, d.ape, N, dst.to(DEV), bf_cache)
     torch.cuda.synchronize()
     got_c, got_s = codes.cpu().numpy(), scales.cpu().numpy()
     rc, rs = ref_codes.cpu().numpy(), ref_scales.cpu().numpy()
+    ok_rows = [n for n in range(N) if 0 <= int(dst[n]) < cap]
+    rows_ok = dst[ok_rows].long()
+    # (1) the oracle's FP8 input path on the BF16 pooled rows of the same pools
+    gpu_bf = bf_cache[rows_ok.to(DEV)].float().cpu().numpy()
+    o_codes, o_exps, _ = oracle.fp8_quantize_rows(gpu_bf)
+    assert np.array_equal(got_c[rows_ok.numpy()], o_codes)
+    assert np.array_equal(got_s[rows_ok.numpy()], np.ldexp(1.0, o_exps).astype(np.float32))
+    # (2) the oracle's whole chain (compress, then the FP8 input path) on
+    # every pool whose BF16 row equals the oracle's
+    ks_np, gs_np = d.inp.k[tok_idx].float().numpy(), d.inp.gate[tok_idx].float().numpy()
+    orc_bf, _ = oracle.compress(ks_np, gs_np, d.inp.ape.numpy(), np.array([0, N * kpool]), kpool)
+    orc_bf = orc_bf[ok_rows]
+    same = np.all(orc_bf == gpu_bf, axis=1)
+    c2, e2, _ = oracle.fp8_quantize_rows(orc_bf[same])
+    assert np.array_equal(got_c[rows_ok.numpy()[same]], c2)
+    assert np.array_equal(got_s[rows_ok.numpy()[same]], np.ldexp(1.0, e2).astype(np.float32))
+    log(f"  FP8 cache rows: {int(same.sum())}/{len(ok_rows)} pools through the oracle's whole chain")
+    assert same.mean() > 0.5
     written = set()
-    for n in range(N):
+    for n in ok_rows:
         r = int(dst[n])
-        if 0 <= r < cap:
-            assert np.array_equal(got_c[r], rc[int(pick[n])]), n
-            assert got_s[r] == rs[int(pick[n])], n
-            written.add(r)
+        assert np.array_equal(got_c[r], rc[int(pick[n])]), n
+        assert got_s[r] == rs[int(pick[n])], n
+        written.add(r)
     untouched = [r for r in range(cap) if r not in written]
     assert np.all(got_c[untouched] == 0xA5) and np.all(got_s[untouched] == -3.0)
 

@@ -6,8 +6,7 @@ pooled key cannot move a near-tie downstream:
   compress   GPU pooled vs oracle pooled            <= 1 BF16 ulp; cu_pools exact
   fp8 codes  GPU quantiser vs oracle on the same BF16 rows     bit-exact
   logits     GPU scores vs oracle scores from the GPU's pooled keys
-             |g - o| <= 2e-3 * max(|o|, 0.01 * max_row |o|)
-                        + 2 D 2^-24 sum_h |w_h| scale sum_d |q_hd k_jd|
+             |g - o| <= 2e-3 * |o| + 2 D 2^-24 sum_h |w_h| scale sum_d |q_hd k_jd|
              (the last term is the FP32 dot-product rounding bound on each
              side; it only matters where heads cancel); -inf past n_c
   select     GPU selection of the GPU's logits vs oracle selection of the same
@@ -16,6 +15,9 @@ pooled key cannot move a near-tie downstream:
   end to end GPU pool sets vs oracle sets from oracle scores: equal except
              pools within 1e-3 relative of the k-th score; token rows equal the
              oracle's expansion of the GPU's pool ids exactly.
+  all-oracle the oracle from the raw inputs alone (its own pooled keys) vs the
+             GPU path: the fraction of sampled rows that agree up to ties,
+             logged and held above a floor (an informational figure).
 """
 import numpy as np
 import pytest
@@ -499,6 +501,48 @@ def test_end_to_end_full_size_sampled(wl, n):
     rows = [r for r in rows if r < d.inp.T]
     log(f"end to end {d.inp.wl.name}: {len(rows)} sampled rows, query_chunk {d.p.query_chunk}")
     _end_to_end(d, rows, fp8=bool(d.inp.wl.fp8))
+
+
+@pytest.mark.parametrize("wl,n", [(1, 192), (2, 192), (3, 96), (4, 64)])
+def test_end_to_end_full_oracle_informational(wl, n):
+    """The oracle run from the raw inputs alone (its own pooled keys, scores,
+    selection and expansion) against the GPU path, on the sampled rows of
+    the full-size workloads. The staged tests above isolate each step; here a
+    legitimate 1-ulp difference in a pooled key may move a near-tie, so the
+    figure is the fraction of rows whose pool set agrees with the all-oracle
+    set up to the 1e-3 tie rule (the oracle's own scores decide), and whose
+    token row then equals the all-oracle row wherever the sets are equal. The
+    floor of 0.95 is far below what an FP64 evaluation of the pooling agrees
+    with the oracle on these rows (every row): the pooled keys differ in about
+    1e-4 of their elements, by 1 ulp."""
+    d = dev_for(wl)
+    tok, pid = d.indexer()
+    q, k, gate, w, ape, cu = oracle_inputs(d.inp)
+    p = d.p
+    orc_pooled, cuP = oracle.compress(k, gate, ape, cu, p.kpool)
+    rows = wlm.strided_rows(d.inp.T, n)
+    rows = sorted(set(rows) | {max(c - 1, 0) for c in cu[1:].tolist()} | set(cu[:-1].tolist()))
+    rows = [r for r in rows if r < d.inp.T]
+    otok, opid, osc = oracle.indexer_topk(q, w, orc_pooled, cu, p.kpool, p.index_topk,
+                                          bool(p.always_select_tail), rows=rows,
+                                          fp8=bool(d.inp.wl.fp8), return_scores=True)
+    agree = exact = 0
+    worst = ""
+    for r, t in enumerate(rows):
+        b = oracle.doc_of(t, cu)
+        okk, why = sets_match_up_to_ties(pid[t], opid[r], osc[r], int(cuP[b]), p.k_sel)
+        agree += int(okk)
+        if not okk:
+            worst = f"row {t}: {why}"
+        if np.array_equal(pid[t], opid[r]):
+            exact += 1
+            assert np.array_equal(tok[t], otok[r]), f"row {t}"
+    frac = agree / len(rows)
+    diff = float(np.mean(d.pooled[:int(cuP[-1])].float().cpu().numpy() != orc_pooled))
+    log(f"  all-oracle end to end {d.inp.wl.name}: {agree}/{len(rows)} rows agree up to ties "
+        f"({frac:.4f}), {exact} identical; pooled elements differing from the oracle's: "
+        f"{diff:.2e} {worst}")
+    assert frac >= 0.95, worst
 
 
 def test_end_to_end_max_pools():
