@@ -266,6 +266,27 @@ kpool_status kpool_decode_topk(const kpool_params* p, const void* q, const float
                                void* workspace, size_t workspace_bytes,
                                int32_t* out_token_idx, int32_t* out_pool_idx, void* stream);
 
+/* ---- For callers that cannot allocate ----------------------------------
+ * For code that must not call hipMalloc (work captured in a HIP graph, tight
+ * serving loops, hosts that forbid allocation): kpool_decode_topk with its
+ * scores kept in a scratch array built into the library instead of a caller
+ * workspace. The array holds kpool_decode_noalloc_max_bytes() bytes (32 MiB)
+ * on each device the library runs on, from load until the process ends; a
+ * call needs num_docs * kpool_logits_ld * 4 bytes of it (for example 512
+ * sequences of up to 64K tokens at kpool 4) and fails with
+ * KPOOL_E_WORKSPACE, enqueuing nothing, when that is more. The call
+ * allocates no memory. Every call on one device uses the same array: calls
+ * that overlap on one device (on different streams, or from several host
+ * threads) race and their outputs are unspecified; calls ordered on one
+ * stream are safe. Arguments and outputs are those of kpool_decode_topk. */
+size_t kpool_decode_noalloc_max_bytes(void);
+kpool_status kpool_decode_topk_noalloc(const kpool_params* p, const void* q, const float* w,
+                                       const void* pooled, int32_t pooled_rows,
+                                       const float* pooled_scale, const int32_t* pool_start,
+                                       const int32_t* seq_lens, const int32_t* token_base,
+                                       int32_t* out_token_idx, int32_t* out_pool_idx,
+                                       void* stream);
+
 /* Static description of a status code. */
 const char* kpool_status_string(kpool_status s);
 

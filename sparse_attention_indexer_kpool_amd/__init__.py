@@ -114,6 +114,10 @@ def lib() -> ctypes.CDLL:
         L.kpool_decode_workspace_bytes.argtypes = [P]
         L.kpool_decode_topk.restype = ctypes.c_int
         L.kpool_decode_topk.argtypes = [P, vp, vp, vp, i32, vp, vp, vp, vp, vp, sz, vp, vp, vp]
+        L.kpool_decode_noalloc_max_bytes.restype = sz
+        L.kpool_decode_noalloc_max_bytes.argtypes = []
+        L.kpool_decode_topk_noalloc.restype = ctypes.c_int
+        L.kpool_decode_topk_noalloc.argtypes = [P, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp]
         L.kpool_status_string.restype = ctypes.c_char_p
         L.kpool_status_string.argtypes = [ctypes.c_int]
         L.kpool_last_error.restype = ctypes.c_char_p
@@ -127,7 +131,8 @@ EXPORTS = ["kpool_abi_version", "kpool_workspace_bytes", "kpool_logits_ld",
            "kpool_indexer_topk", "kpool_logits", "kpool_select", "kpool_select_expand",
            "kpool_expand",
            "kpool_fp8_quantize", "kpool_compress_pools", "kpool_decode_workspace_bytes",
-           "kpool_decode_topk", "kpool_status_string", "kpool_last_error"]
+           "kpool_decode_topk", "kpool_decode_noalloc_max_bytes", "kpool_decode_topk_noalloc",
+           "kpool_status_string", "kpool_last_error"]
 
 
 def _check(status: int) -> None:
@@ -239,6 +244,20 @@ def kpool_decode_topk(p: Params, q, w, pooled, pool_start, seq_lens, workspace, 
                                    int(pooled.shape[0]), _ptr(pooled_scale), _ptr(pool_start), _ptr(seq_lens), _ptr(token_base),
                                    _ptr(workspace), ws_bytes, _ptr(out_token_idx),
                                    _ptr(out_pool_idx), _stream(stream)))
+
+
+def kpool_decode_noalloc_max_bytes() -> int:
+    return int(lib().kpool_decode_noalloc_max_bytes())
+
+
+def kpool_decode_topk_noalloc(p: Params, q, w, pooled, pool_start, seq_lens, out_token_idx,
+                              out_pool_idx=None, token_base=None, pooled_scale=None,
+                              stream=None) -> None:
+    _check(lib().kpool_decode_topk_noalloc(ctypes.byref(p.c()), _ptr(q), _ptr(w), _ptr(pooled),
+                                           int(pooled.shape[0]), _ptr(pooled_scale),
+                                           _ptr(pool_start), _ptr(seq_lens), _ptr(token_base),
+                                           _ptr(out_token_idx), _ptr(out_pool_idx),
+                                           _stream(stream)))
 
 
 def kpool_status_string(status: int) -> str:

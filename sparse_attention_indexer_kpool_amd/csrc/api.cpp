@@ -7,6 +7,7 @@
 #include <algorithm>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "kpool.h"
@@ -390,14 +391,16 @@ size_t kpool_decode_workspace_bytes(const kpool_params* p) {
   return d.total;
 }
 
-kpool_status kpool_decode_topk(const kpool_params* p, const void* q, const float* w,
+}  // extern "C"
+
+namespace {
+
+// Argument checks of the decode entry points, workspace aside.
+kpool_status check_decode_args(const DecodeDerived& d, const void* q, const float* w,
                                const void* pooled, int32_t pooled_rows,
                                const float* pooled_scale, const int32_t* pool_start,
                                const int32_t* seq_lens, const int32_t* token_base,
-                               void* workspace, size_t workspace_bytes,
-                               int32_t* out_token_idx, int32_t* out_pool_idx, void* stream) {
-  DecodeDerived d;
-  CHECK(derive_decode(p, &d));
+                               const int32_t* out_token_idx, const int32_t* out_pool_idx) {
   CHECK(check_ptr(q, 16, "q"));
   CHECK(check_ptr(w, 4, "w"));
   CHECK(check_ptr(pool_start, 4, "pool_start"));
@@ -410,11 +413,16 @@ kpool_status kpool_decode_topk(const kpool_params* p, const void* q, const float
     CHECK(check_ptr(pooled, 16, "pooled"));
     if (d.fp8) CHECK(check_ptr(pooled_scale, 4, "pooled_scale"));
   }
-  CHECK(check_ptr(workspace, 256, "workspace"));
-  if (workspace_bytes < d.total)
-    return fail(KPOOL_E_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, d.total);
+  return KPOOL_OK;
+}
+
+// The two launches of a decode step; `scores` holds B rows of d.ld floats.
+kpool_status run_decode(const DecodeDerived& d, const void* q, const float* w,
+                        const void* pooled, int32_t pooled_rows, const float* pooled_scale,
+                        const int32_t* pool_start, const int32_t* seq_lens,
+                        const int32_t* token_base, float* scores, int32_t* out_token_idx,
+                        int32_t* out_pool_idx, void* stream) {
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  float* scores = reinterpret_cast<float*>(workspace);
   (void)hipGetLastError();
   kpool::DecodeLogitsArgs a{};
   a.q = q;                       // BF16; the FP8 kernel quantises its rows itself
@@ -434,6 +442,84 @@ kpool_status kpool_decode_topk(const kpool_params* p, const void* q, const float
                               d.k_sel, d.width, d.tail, d.max_pools, out_pool_idx, out_token_idx,
                               st);
   return after_launch();
+}
+
+// Scratch of kpool_decode_topk_noalloc: the scores of one decode step live in
+// this array, so that entry point allocates nothing. Each device holds its
+// own copy, from the library's load until the process ends; its address on a
+// device comes from hipGetSymbolAddress with that device current (the
+// array's name in host code is only a stand-in and is never used as an
+// address).
+constexpr size_t kScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (looked up once per
+// device); null with a message on failure.
+kpool_status scratch_on_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(KPOOL_E_LAUNCH, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(KPOOL_E_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(KPOOL_E_LAUNCH, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return KPOOL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kpool_status kpool_decode_topk(const kpool_params* p, const void* q, const float* w,
+                               const void* pooled, int32_t pooled_rows,
+                               const float* pooled_scale, const int32_t* pool_start,
+                               const int32_t* seq_lens, const int32_t* token_base,
+                               void* workspace, size_t workspace_bytes,
+                               int32_t* out_token_idx, int32_t* out_pool_idx, void* stream) {
+  DecodeDerived d;
+  CHECK(derive_decode(p, &d));
+  CHECK(check_decode_args(d, q, w, pooled, pooled_rows, pooled_scale, pool_start, seq_lens,
+                          token_base, out_token_idx, out_pool_idx));
+  CHECK(check_ptr(workspace, 256, "workspace"));
+  if (workspace_bytes < d.total)
+    return fail(KPOOL_E_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, d.total);
+  return run_decode(d, q, w, pooled, pooled_rows, pooled_scale, pool_start, seq_lens, token_base,
+                    reinterpret_cast<float*>(workspace), out_token_idx, out_pool_idx, stream);
+}
+
+size_t kpool_decode_noalloc_max_bytes(void) { return kScratchBytes; }
+
+kpool_status kpool_decode_topk_noalloc(const kpool_params* p, const void* q, const float* w,
+                                       const void* pooled, int32_t pooled_rows,
+                                       const float* pooled_scale, const int32_t* pool_start,
+                                       const int32_t* seq_lens, const int32_t* token_base,
+                                       int32_t* out_token_idx, int32_t* out_pool_idx,
+                                       void* stream) {
+  DecodeDerived d;
+  CHECK(derive_decode(p, &d));
+  if (d.total > kScratchBytes)
+    return fail(KPOOL_E_WORKSPACE,
+                "the scores of %d sequences of up to %d pools need %zu bytes; the built-in "
+                "scratch holds %zu (num_docs * kpool_logits_ld * 4)",
+                d.B, d.max_pools, d.total, kScratchBytes);
+  CHECK(check_decode_args(d, q, w, pooled, pooled_rows, pooled_scale, pool_start, seq_lens,
+                          token_base, out_token_idx, out_pool_idx));
+  void* ws = nullptr;
+  CHECK(scratch_on_current_device(&ws));
+  return run_decode(d, q, w, pooled, pooled_rows, pooled_scale, pool_start, seq_lens, token_base,
+                    reinterpret_cast<float*>(ws), out_token_idx, out_pool_idx, stream);
 }
 
 kpool_status kpool_compress_pools(const kpool_params* p, const void* k, const void* gate,
