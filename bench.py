@@ -117,6 +117,17 @@ class Path:
         kp.kpool_indexer_topk(self.p, self.q, self.w, self.pooled, self.cu, self.cu_pools,
                               self.ws, self.tok, None)
 
+    def fused_indexer(self):
+        """kpool_indexer_topk_fused: scoring, selection and expansion in one
+        kernel per query chunk (plus the FP8 quantiser on the FP8 path)."""
+        self.kp.kpool_indexer_topk_fused(self.p, self.q, self.w, self.pooled, self.cu,
+                                         self.cu_pools, self.ws, self.tok, None)
+
+    def fused_step(self):
+        kp = self.kp
+        kp.kpool_compress(self.p, self.k, self.gate, self.ape, self.cu, self.cu_pools, self.pooled)
+        self.fused_indexer()
+
     # --- phases timed on their own (same launches as inside a step) --------
     def time_compress_cold(self, n_copies=16, replays=10):
         """Device time (ms) of one kpool_compress launch on inputs that no
@@ -302,6 +313,13 @@ def measure_workload(wl, steps: int, warmup: int):
         ms_fp8 = time_region(lambda: path.phase_fp8_quant(bufs), reps)
     del logits, ids
     n_chunks = (T + path.qc - 1) // path.qc
+    fused = None
+    if wl.k_sel <= path.kp.kpool_fused_max_ksel(path.p):
+        path.fused_step()
+        ms_fused_step = time_region(path.fused_step, steps, warm=1)
+        ms_fused_idx = time_region(path.fused_indexer, reps)
+        fused = (ms_fused_step, ms_fused_idx)
+        log(f"{wl.name}: fused step {ms_fused_step:.4f} ms")
 
     flops = 2.0 * wl.H * wl.D * need_nc
     peak = PEAK_FP8_TFLOPS if wl.fp8 else PEAK_BF16_TFLOPS
@@ -338,6 +356,20 @@ def measure_workload(wl, steps: int, warmup: int):
     if ms_fp8 is not None:
         fig["phases_ms"]["fp8_quant"] = round(ms_fp8, 4)
         fig["phases_hbm"]["fp8_quant"] = hbm(by_fp8, ms_fp8)
+    if fused is not None:
+        # the fused entry point, timed the same way; its kernel does the
+        # same FLOPs as the scoring kernel (the quantiser's time, on the FP8
+        # path, is taken off with the phase measured above)
+        ms_fk = fused[1] - (ms_fp8 or 0.0)
+        fig["fused"] = {
+            "entry": "kpool_indexer_topk_fused", "ms_per_step": round(fused[0], 4),
+            "queries_per_s": round(T / (fused[0] * 1e-3), 1),
+            "vs_two_kernel_step": round(ms / fused[0], 4),
+            "indexer_ms": round(fused[1], 4),
+            "kernel_roofline": {"bound": "mfma", "achieved": round(flops / (ms_fk * 1e-3) / 1e12, 2),
+                                "peak": round(peak, 1), "unit": "TFLOP/s",
+                                "frac": round(flops / (ms_fk * 1e-3) / 1e12 / peak, 4)},
+            "note": "scores never leave the chip; token rows written directly"}
     del path
     torch.cuda.empty_cache()
     return inp, ms, fig
@@ -387,6 +419,8 @@ def main():
         "phases_ms": fig["phases_ms"],
         "phases_hbm": fig["phases_hbm"],
     }
+    if "fused" in fig:
+        out["fused"] = fig["fused"]
     if not args.no_decode and wl.name == "long_T65536_H32_D128":
         reps = max(3, min(args.steps, 10))
         log("decode step, 64 sequences of 64K tokens")

@@ -78,16 +78,17 @@ typedef struct {
 int kpool_abi_version(void);
 
 /* Bytes of device workspace kpool_indexer_topk and kpool_logits need for
- * these parameters (0 when T == 0). The workspace holds the FP32 logits tile
- * (query_chunk x kpool_logits_ld floats) and, with use_fp8, the E4M3 codes
- * and row scales of q and of the pooled keys. */
+ * these parameters (0 when T == 0). The workspace holds, with use_fp8, the
+ * E4M3 codes and row scales of q and of the pooled keys, then the FP32
+ * logits tile of kpool_query_chunk_rows x kpool_logits_ld floats. It is
+ * also enough for kpool_indexer_topk_fused. */
 size_t kpool_workspace_bytes(const kpool_params* p);
 
 /* Row stride, in floats, of the logits tiles of kpool_logits / kpool_select:
  * max_pools rounded up to a multiple of 64. */
 int64_t kpool_logits_ld(const kpool_params* p);
 
-/* Query rows per logits tile that kpool_indexer_topk uses: query_chunk when
+/* Query rows per logits tile of kpool_indexer_topk: query_chunk when
  * it is set, else floor(256 MiB / (4 * kpool_logits_ld(p))), capped at T
  * (0 when T == 0 or the parameters are invalid). */
 int32_t kpool_query_chunk_rows(const kpool_params* p);
@@ -115,8 +116,10 @@ kpool_status kpool_compress(const kpool_params* p, const void* k, const void* ga
  * over the causal pools p = cuP[b] .. cuP[b] + n_c(t) - 1 of t's document;
  * the min(K_sel, n_c(t)) best pools (ties to the lower pool id) are expanded,
  * in ascending pool order, to their kpool tokens, followed by the tail(t)
- * tokens cu[b] + n_c(t)*kpool .. t, then -1 up to width W. Query rows are
- * processed query_chunk at a time through a logits tile in the workspace.
+ * tokens cu[b] + n_c(t)*kpool .. t, then -1 up to width W. Query rows go
+ * kpool_query_chunk_rows at a time through a logits tile in the workspace:
+ * the scoring kernel of kpool_logits, then the selection + expansion kernel
+ * of kpool_select_expand on each chunk.
  * With use_fp8 the q rows (t, h) and the pooled rows first go through the FP8
  * input path of kpool_fp8_quantize and are scored from their E4M3 codes and
  * power-of-two scales.
@@ -133,6 +136,27 @@ kpool_status kpool_indexer_topk(const kpool_params* p, const void* q, const floa
                                 const int32_t* cu_pools, void* workspace,
                                 size_t workspace_bytes, int32_t* out_token_idx,
                                 int32_t* out_pool_idx, void* stream);
+
+/* Steps 2-4 in one kernel per query chunk, with the same arguments and the
+ * same output as kpool_indexer_topk, bit for bit ([MLM] section 3 names a
+ * fused scoring + top-k + expansion op). Each workgroup keeps a running top
+ * K_sel of each of its queries' scores in LDS while the pools stream past
+ * (exact selection when a candidate list fills, then a higher entry
+ * threshold), so no score is written to memory. Needs K_sel to fit the
+ * per-query candidate list: K_sel <= kpool_fused_max_ksel(p) (1184 at
+ * H = 32, D = 128; 1344 with use_fp8; fewer with fewer heads, whose
+ * workgroups hold more queries). Otherwise it returns KPOOL_E_UNSUPPORTED
+ * and enqueues nothing. The
+ * workspace holds only the FP8 codes and scales:
+ * kpool_fused_workspace_bytes(p) bytes (0 without use_fp8, and 0 when the
+ * shape is unsupported; the pointer may then be NULL). */
+int32_t kpool_fused_max_ksel(const kpool_params* p);      /* uses H, D, use_fp8 */
+size_t kpool_fused_workspace_bytes(const kpool_params* p);
+kpool_status kpool_indexer_topk_fused(const kpool_params* p, const void* q, const float* w,
+                                      const void* pooled, const int32_t* cu_seqlens,
+                                      const int32_t* cu_pools, void* workspace,
+                                      size_t workspace_bytes, int32_t* out_token_idx,
+                                      int32_t* out_pool_idx, void* stream);
 
 /* Step 2 alone, for query rows q_begin .. q_end-1 (0 <= q_begin <= q_end <= T):
  *   out[r, j] = score of row t = q_begin + r against doc-local pool j of t's

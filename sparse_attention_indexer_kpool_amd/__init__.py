@@ -98,6 +98,12 @@ def lib() -> ctypes.CDLL:
         L.kpool_compress.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
         L.kpool_indexer_topk.restype = ctypes.c_int
         L.kpool_indexer_topk.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp]
+        L.kpool_fused_max_ksel.restype = ctypes.c_int32
+        L.kpool_fused_max_ksel.argtypes = [P]
+        L.kpool_fused_workspace_bytes.restype = sz
+        L.kpool_fused_workspace_bytes.argtypes = [P]
+        L.kpool_indexer_topk_fused.restype = ctypes.c_int
+        L.kpool_indexer_topk_fused.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp]
         L.kpool_logits.restype = ctypes.c_int
         L.kpool_logits.argtypes = [P, vp, vp, vp, vp, vp, i32, i32, vp, sz, vp, i32, vp]
         L.kpool_select.restype = ctypes.c_int
@@ -128,7 +134,9 @@ def lib() -> ctypes.CDLL:
 
 EXPORTS = ["kpool_abi_version", "kpool_workspace_bytes", "kpool_logits_ld",
            "kpool_query_chunk_rows", "kpool_compress",
-           "kpool_indexer_topk", "kpool_logits", "kpool_select", "kpool_select_expand",
+           "kpool_indexer_topk", "kpool_fused_max_ksel", "kpool_fused_workspace_bytes",
+           "kpool_indexer_topk_fused",
+           "kpool_logits", "kpool_select", "kpool_select_expand",
            "kpool_expand",
            "kpool_fp8_quantize", "kpool_compress_pools", "kpool_decode_workspace_bytes",
            "kpool_decode_topk", "kpool_decode_noalloc_max_bytes", "kpool_decode_topk_noalloc",
@@ -185,6 +193,23 @@ def kpool_indexer_topk(p: Params, q, w, pooled, cu_seqlens, cu_pools, workspace,
     _check(lib().kpool_indexer_topk(ctypes.byref(p.c()), _ptr(q), _ptr(w), _ptr(pooled),
                                     _ptr(cu_seqlens), _ptr(cu_pools), _ptr(workspace), ws_bytes,
                                     _ptr(out_token_idx), _ptr(out_pool_idx), _stream(stream)))
+
+
+def kpool_fused_max_ksel(p: Params) -> int:
+    return int(lib().kpool_fused_max_ksel(ctypes.byref(p.c())))
+
+
+def kpool_fused_workspace_bytes(p: Params) -> int:
+    return int(lib().kpool_fused_workspace_bytes(ctypes.byref(p.c())))
+
+
+def kpool_indexer_topk_fused(p: Params, q, w, pooled, cu_seqlens, cu_pools, workspace,
+                             out_token_idx, out_pool_idx=None, stream=None) -> None:
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().kpool_indexer_topk_fused(ctypes.byref(p.c()), _ptr(q), _ptr(w), _ptr(pooled),
+                                          _ptr(cu_seqlens), _ptr(cu_pools), _ptr(workspace),
+                                          ws_bytes, _ptr(out_token_idx), _ptr(out_pool_idx),
+                                          _stream(stream)))
 
 
 KPOOL_LOGITS_FILL_MASKED = 1

@@ -42,6 +42,7 @@ constexpr size_t kDefaultTileBytes = size_t(256) << 20;
 
 struct Derived {
   int B, T, H, D, kpool, topk, k_sel, width, max_pools, qc, tail, fp8;
+  bool fused;                      // the indexer scores and selects in one kernel
   int64_t ld;
   float scale;
   size_t off_logits, off_qc, off_qs, off_kc, off_ks, total;
@@ -93,10 +94,10 @@ kpool_status derive(const kpool_params* p, Derived* d, bool need_heads) {
                        ? (int64_t)p->query_chunk
                        : (int64_t)(kDefaultTileBytes / ((size_t)d->ld * sizeof(float)));
   d->qc = (int)std::max<int64_t>(1, std::min<int64_t>(qc, std::max(d->T, 1)));
-  // workspace layout (256-byte aligned pieces)
+  d->fused = need_heads && kpool::logits_select_supported(d->H, d->D, d->fp8, d->k_sel);
+  // workspace layout (256-byte aligned pieces): the FP8 codes and scales of
+  // q and of the pooled keys, then the logits tile of the two-kernel path
   size_t off = 0;
-  d->off_logits = off;
-  off = round_up(off + (size_t)d->qc * d->ld * 4, 256);
   d->off_qc = d->off_qs = d->off_kc = d->off_ks = off;
   if (d->fp8) {
     const size_t qrows = (size_t)d->T * d->H, krows = (size_t)(d->T / d->kpool);
@@ -109,6 +110,8 @@ kpool_status derive(const kpool_params* p, Derived* d, bool need_heads) {
     d->off_ks = off;
     off = round_up(off + krows * 4, 256);
   }
+  d->off_logits = off;
+  off = round_up(off + (size_t)d->qc * d->ld * 4, 256);
   d->total = d->T > 0 ? off : 0;
   return KPOOL_OK;
 }
@@ -206,6 +209,28 @@ kpool_status derive_decode(const kpool_params* p, DecodeDerived* d) {
   return KPOOL_OK;
 }
 
+// Checks shared by the two indexer entry points; `need` is the workspace
+// the entry point uses.
+kpool_status check_indexer_args(const Derived& d, const void* q, const float* w,
+                                const void* pooled, const int32_t* cu_seqlens,
+                                const int32_t* cu_pools, const void* workspace,
+                                size_t workspace_bytes, size_t need,
+                                const int32_t* out_token_idx, const int32_t* out_pool_idx) {
+  CHECK(check_ptr(q, 16, "q"));
+  CHECK(check_ptr(w, 4, "w"));
+  CHECK(check_ptr(cu_seqlens, 4, "cu_seqlens"));
+  CHECK(check_ptr(cu_pools, 4, "cu_pools"));
+  CHECK(check_ptr(out_token_idx, 16, "out_token_idx"));
+  if (out_pool_idx) CHECK(check_ptr(out_pool_idx, 4, "out_pool_idx"));
+  if (d.T / d.kpool > 0) CHECK(check_ptr(pooled, 16, "pooled"));
+  if (need > 0) {
+    CHECK(check_ptr(workspace, 256, "workspace"));
+    if (workspace_bytes < need)
+      return fail(KPOOL_E_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+  }
+  return KPOOL_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -259,16 +284,8 @@ kpool_status kpool_indexer_topk(const kpool_params* p, const void* q, const floa
   Derived d;
   CHECK(derive(p, &d, true));
   if (d.T == 0) return ok();
-  CHECK(check_ptr(q, 16, "q"));
-  CHECK(check_ptr(w, 4, "w"));
-  CHECK(check_ptr(cu_seqlens, 4, "cu_seqlens"));
-  CHECK(check_ptr(cu_pools, 4, "cu_pools"));
-  CHECK(check_ptr(out_token_idx, 16, "out_token_idx"));
-  if (out_pool_idx) CHECK(check_ptr(out_pool_idx, 4, "out_pool_idx"));
-  if (d.T / d.kpool > 0) CHECK(check_ptr(pooled, 16, "pooled"));
-  CHECK(check_ptr(workspace, 256, "workspace"));
-  if (workspace_bytes < d.total)
-    return fail(KPOOL_E_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, d.total);
+  CHECK(check_indexer_args(d, q, w, pooled, cu_seqlens, cu_pools, workspace, workspace_bytes,
+                           d.total, out_token_idx, out_pool_idx));
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
   (void)hipGetLastError();
@@ -285,6 +302,56 @@ kpool_status kpool_indexer_topk(const kpool_params* p, const void* q, const floa
                          d.width, d.tail, d.max_pools,
                          out_pool_idx ? out_pool_idx + (size_t)c0 * d.k_sel : nullptr,
                          out_token_idx + (size_t)c0 * d.width, st);
+  }
+  return after_launch();
+}
+
+int32_t kpool_fused_max_ksel(const kpool_params* p) {
+  if (!p) return 0;
+  const int H = p->num_heads, D = p->head_dim, fp8 = p->use_fp8;
+  if (H != 4 && H != 8 && H != 16 && H != 32 && H != 64) return 0;
+  if ((D != 64 && D != 128) || (fp8 != 0 && fp8 != 1) || (fp8 && D != 128)) return 0;
+  return kpool::logits_select_max_ksel(H, D, fp8);
+}
+
+size_t kpool_fused_workspace_bytes(const kpool_params* p) {
+  Derived d;
+  if (derive(p, &d, true) != KPOOL_OK || !d.fused || d.T == 0) return 0;
+  return d.off_logits;             // the FP8 codes and scales; no tile
+}
+
+kpool_status kpool_indexer_topk_fused(const kpool_params* p, const void* q, const float* w,
+                                      const void* pooled, const int32_t* cu_seqlens,
+                                      const int32_t* cu_pools, void* workspace,
+                                      size_t workspace_bytes, int32_t* out_token_idx,
+                                      int32_t* out_pool_idx, void* stream) {
+  Derived d;
+  CHECK(derive(p, &d, true));
+  if (!d.fused)
+    return fail(KPOOL_E_UNSUPPORTED,
+                "K_sel = %d does not fit the fused kernel's per-query candidate list at H = %d, "
+                "D = %d%s (kpool_indexer_topk takes any K_sel)",
+                d.k_sel, d.H, d.D, d.fp8 ? ", FP8" : "");
+  if (d.T == 0) return ok();
+  CHECK(check_indexer_args(d, q, w, pooled, cu_seqlens, cu_pools, workspace, workspace_bytes,
+                           d.off_logits, out_token_idx, out_pool_idx));
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
+  (void)hipGetLastError();
+  if (d.fp8) quantize_inputs(d, q, pooled, cu_pools, 0, d.T, ws, st);
+  kpool::LogitsArgs a = logits_args(d, q, w, pooled, cu_seqlens, cu_pools, ws);
+  a.skip_select_all = 1;
+  a.width = d.width;
+  a.tail_on = d.tail;
+  // one launch per query chunk, as the two-kernel path; nothing but the
+  // token rows (and pool ids) is written
+  for (int c0 = 0; c0 < d.T; c0 += d.qc) {
+    const int c1 = std::min(d.T, c0 + d.qc);
+    a.q_begin = c0;
+    a.q_end = c1;
+    a.out_tok = out_token_idx + (size_t)c0 * d.width;
+    a.out_ids = out_pool_idx ? out_pool_idx + (size_t)c0 * d.k_sel : nullptr;
+    kpool::launch_logits_select(a, st);
   }
   return after_launch();
 }
@@ -308,10 +375,11 @@ kpool_status kpool_logits(const kpool_params* p, const void* q, const float* w,
   CHECK(check_ptr(cu_pools, 4, "cu_pools"));
   CHECK(check_ptr(out, 16, "out"));
   if (d.T / d.kpool > 0) CHECK(check_ptr(pooled, 16, "pooled"));
-  if (d.fp8) {
+  if (d.fp8) {                     // the codes and scales; no tile
     CHECK(check_ptr(workspace, 256, "workspace"));
-    if (workspace_bytes < d.total)
-      return fail(KPOOL_E_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, d.total);
+    if (workspace_bytes < d.off_logits)
+      return fail(KPOOL_E_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes,
+                  d.off_logits);
   }
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);

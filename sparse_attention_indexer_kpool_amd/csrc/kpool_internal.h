@@ -35,8 +35,22 @@ struct LogitsArgs {
   int skip_select_all;      // 1: leave rows with n_c <= k_sel unwritten
   int fp8;
   int pieces;               // set by the launcher: workgroups per query block
+  // fused selection (launch_logits_select): every row's chosen pools go
+  // straight to its token row; no logits tile
+  int32_t* out_tok;         // [q_end - q_begin, width]
+  int32_t* out_ids;         // [q_end - q_begin, k_sel] global pool ids, or null
+  int width, tail_on;
 };
 void launch_logits(const LogitsArgs& a, hipStream_t st);
+
+// Scoring, pool top-k, expansion and tail of rows q_begin .. q_end-1 in one
+// kernel: each workgroup keeps a running top-k_sel of every query's scores
+// in LDS while it sweeps the pools, so no score leaves the chip. Returns
+// false (and launches nothing) for shapes whose per-query LDS list cannot
+// hold k_sel entries with room to spare; the caller then takes the tile path.
+bool logits_select_supported(int H, int D, int fp8, int k_sel);
+int logits_select_max_ksel(int H, int D, int fp8);
+void launch_logits_select(const LogitsArgs& a, hipStream_t st);
 
 // Pool top-k of rows q_begin .. q_end-1 from a logits tile; writes the pool
 // ids (out_ids, may be null) and/or the expanded token rows with the tail

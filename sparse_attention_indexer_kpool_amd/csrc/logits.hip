@@ -103,11 +103,22 @@ __device__ __forceinline__ void dma4(const float* src, float* block) {
 
 // Issue this wave's share of a key tile straight into LDS. Rows past the
 // causal range read the last causal row instead: their scores are never
-// stored.
+// stored. On the FP8 path wave 0 also copies the tile's 64 key scales, so
+// the epilogue reads them from LDS: a global load there would make the
+// compiler's wait for it also wait for the next tile's copy, which was issued
+// before it (vector-memory operations complete in order).
 template <int H, int D, bool FP8>
 __device__ __forceinline__ void load_key_tile(const uint8_t* __restrict__ keys, int pool0, int j0,
-                                              int maxnc, uint8_t* lds, int wid, int lane) {
+                                              int maxnc, uint8_t* lds, int wid, int lane,
+                                              const float* __restrict__ kscale = nullptr,
+                                              float* sbuf = nullptr) {
   using C = LogitsCfg<H, D, FP8>;
+  if constexpr (FP8) {
+    if (wid == 0) {
+      const int jr = j0 + lane < maxnc ? j0 + lane : maxnc - 1;
+      dma4(kscale + pool0 + jr, sbuf);
+    }
+  }
 #pragma unroll
   for (int i = 0; i < C::LPW; ++i) {
     const int L = (wid * C::LPW + i) * 64 + lane;     // LDS chunk index
@@ -174,10 +185,133 @@ struct OutSlots {
   }
 };
 
+// Fused selection: LDS left for the per-query candidate lists once the two
+// key tiles and the small per-query arrays are placed, and the entries each
+// list holds (6 bytes each: the score's bits and a 16-bit pool index).
 template <int H, int D, bool FP8>
+struct SelCfg {
+  using C = LogitsCfg<H, D, FP8>;
+  static constexpr int SMALL = C::QPB * 4 * 8 + 1280 + 32 * 6 + (FP8 ? 512 : 0);
+  static constexpr int BUDGET = 160 * 1024 - 2 * C::TILE_BYTES - SMALL;
+  // at most 24 entries per lane while a list is ranked (its keys stay in
+  // registers beside the operands the sweep holds)
+  static constexpr int CAP_LDS = (BUDGET / (C::QPB * 6)) & ~7;
+  static constexpr int CAP = CAP_LDS < 1536 ? CAP_LDS : 1536;
+  // a wave asks for a shrink once one of its lists has passed TRIGGER. From
+  // the last check a list passed (count <= TRIGGER), or from a shrink (count
+  // <= k_sel + slack), to the next shrink two step starts after a failed
+  // check, a list takes at most two steps of two 32-pool units and its run's
+  // last unit: 160 entries; a unit's stores reach 31 positions past its count.
+  // So TRIGGER + 160 <= CAP and k_sel + slack + 160 <= CAP.
+  static constexpr int TRIGGER = CAP - 160;
+};
+
+__device__ __forceinline__ float key_to_f32(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+// Top-k shrink of one candidate list of cnt > k entries, whole wave.
+// Entries are in ascending pool order (the sweep appends them in that
+// order), so "equal scores to the lower pool" is "equal scores to the
+// earlier entry". A threshold key theta with at least k keys >= theta is
+// found by bisection over the bits where the list's smallest and largest
+// keys differ; counts come from ballots (scalar popcounts), so each step is
+// one vector compare per slot. The bisection stops once k to k + slack keys
+// reach the candidate; with slack 0 (the final selection) it ends either
+// there or at the k-th largest key. The list is compacted in place, order
+// kept: every entry above theta, and entries equal to theta up to a total
+// of k + slack when they fit, else only the first k - #(above) of them. So
+// the kept entries include the exact top k. Returns theta (a later entry, of
+// a higher pool, can belong to the top k only if its key exceeds theta) and
+// the number kept.
+template <int CAP>
+__device__ __forceinline__ uint32_t list_select(uint32_t* __restrict__ lval,
+                                                uint16_t* __restrict__ lidx, int cnt, int k,
+                                                int slack, int lane, int& kept_out) {
+  constexpr int SL = (CAP + 63) / 64;
+  static_assert(SL <= 64, "list slots per lane");
+  uint32_t kv[SL];
+  uint64_t vmask = 0u;
+  uint32_t kmin = 0xffffffffu, kmax = 0u;
+#pragma unroll
+  for (int s = 0; s < SL; ++s) {
+    const int e = s * 64 + lane;
+    const bool valid = e < cnt;
+    const uint32_t key = valid ? f32_order_key(__uint_as_float(lval[valid ? e : 0])) : 0u;
+    kv[s] = key;                                      // invalid slots hold 0 (below every key)
+    vmask |= valid ? (1ull << s) : 0ull;
+    kmin = valid && key < kmin ? key : kmin;
+    kmax = valid && key > kmax ? key : kmax;
+  }
+  kmin = wave_min(kmin);
+  kmax = wave_max(kmax);
+  // #(keys >= c) over the list, wave-uniform (for c >= 1 invalid slots never count)
+  auto count_ge = [&](uint32_t c) {
+    int n = 0;
+#pragma unroll
+    for (int s = 0; s < SL; ++s) n += __popcll(__ballot(kv[s] >= c));
+    return n;
+  };
+  // theta lies in [kmin, kmax], so it shares their common leading bits
+  const int free_bits = kmin == kmax ? 0 : 32 - __clz(kmin ^ kmax);
+  uint32_t th = free_bits >= 32 ? 0u : (kmin >> free_bits) << free_bits;
+  int n_ge = cnt;                                     // #(keys >= th)
+  for (int b = free_bits - 1; b >= 0; --b) {
+    const uint32_t cand = th | (1u << b);
+    const int c = count_ge(cand);
+    if (c >= k) {
+      th = cand;
+      n_ge = c;
+      if (c <= k + slack) break;
+    }
+  }
+  int above = 0;
+#pragma unroll
+  for (int s = 0; s < SL; ++s) above += __popcll(__ballot(((vmask >> s) & 1u) && kv[s] > th));
+  const int keep_eq = (n_ge <= k + slack ? n_ge : k) - above;
+  // compaction: slot s writes only positions below 64 (s + 1), so the pool
+  // indices of a later batch of slots can be read before this batch writes
+  int eq_seen = 0, kept = 0;
+  constexpr int BATCH = 8;
+#pragma unroll
+  for (int s0 = 0; s0 < SL; s0 += BATCH) {
+    uint32_t ix[BATCH];
+#pragma unroll
+    for (int j = 0; j < BATCH; ++j) {
+      const int s = s0 + j;
+      if (s < SL) {
+        const int e = s * 64 + lane;
+        ix[j] = lidx[((vmask >> s) & 1u) ? e : 0];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < BATCH; ++j) {
+      const int s = s0 + j;
+      if (s < SL) {
+        const bool valid = (vmask >> s) & 1u;
+        const bool eq = valid && kv[s] == th;
+        const uint64_t mq = __ballot(eq);
+        const bool keep = valid && (kv[s] > th || (eq && eq_seen + popc_lt(mq) < keep_eq));
+        eq_seen += __popcll(mq);
+        const uint64_t mk = __ballot(keep);
+        if (keep) {
+          const int pos = kept + popc_lt(mk);
+          lval[pos] = __float_as_uint(key_to_f32(kv[s]));
+          lidx[pos] = (uint16_t)ix[j];
+        }
+        kept += __popcll(mk);
+      }
+    }
+  }
+  kept_out = kept;
+  return th;
+}
+
+template <int H, int D, bool FP8, bool SEL>
 __global__ __launch_bounds__(64 * kLogitsWaves) void logits_kernel(LogitsArgs a) {
   using C = LogitsCfg<H, D, FP8>;
   using S = OutSlots<H>;
+  using SC = SelCfg<H, D, FP8>;
   constexpr int MT = C::MT, QPB = C::QPB;
   constexpr int QPW = QPB / kLogitsWaves;
   static_assert(H >= 4 && H <= 64 && (H & (H - 1)) == 0, "H in {4, 8, 16, 32, 64}");
@@ -190,14 +324,35 @@ __global__ __launch_bounds__(64 * kLogitsWaves) void logits_kernel(LogitsArgs a)
   constexpr int W_OFF = kLogitsWaves * C::A_BYTES;
   constexpr int QS_OFF = W_OFF + kLogitsWaves * 256;
   constexpr int STAGE_USED = QS_OFF + (FP8 ? kLogitsWaves * 256 : 0);
-  constexpr int STAGE = C::TILE_BYTES > STAGE_USED ? C::TILE_BYTES : STAGE_USED;
-  static_assert(C::TILE_BYTES + STAGE + 1024 <= 160 * 1024, "LDS budget");
+  // fused selection: after tile1, one candidate list per query, scores
+  // (FP32 bits) [QPB][CAP] then pool indices (uint16) [QPB][CAP]; the q
+  // staging overlaps them (it is read into registers before any entry is
+  // written)
+  constexpr int CAP = SEL ? SC::CAP : 0;
+  constexpr int LIST_OFF = 2 * C::TILE_BYTES;
+  // (plus 32 entries that take the stores of half-waves holding no query:
+  // the second half at 64 heads)
+  constexpr int LIST_ENTRIES = QPB * CAP + 32;
+  constexpr int LIST_BYTES = LIST_ENTRIES * 6;
+  constexpr int TILES_USED = SEL ? 2 * C::TILE_BYTES + LIST_BYTES : 2 * C::TILE_BYTES;
+  constexpr int STAGE_END = C::TILE_BYTES + STAGE_USED;
+  constexpr int LDS_BYTES = TILES_USED > STAGE_END ? TILES_USED : STAGE_END;
+  static_assert(LDS_BYTES + 1024 <= 160 * 1024, "LDS budget");
+  static_assert(!SEL || CAP >= 64, "candidate list capacity");
   // one LDS object with tile0 first, so every tile0 read and most tile1
   // reads fold their address into the 16-bit instruction offset
-  __shared__ __attribute__((aligned(1024))) uint8_t lds_tiles[C::TILE_BYTES + STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_tiles[LDS_BYTES];
   uint8_t* const tile0 = lds_tiles;
   uint8_t* const tile1 = lds_tiles + C::TILE_BYTES;
+  uint32_t* const lval = reinterpret_cast<uint32_t*>(lds_tiles + LIST_OFF);
+  uint16_t* const lidx = reinterpret_cast<uint16_t*>(lds_tiles + LIST_OFF + LIST_ENTRIES * 4);
   __shared__ int q_doc[QPB], q_nc[QPB];
+  __shared__ int q_start[SEL ? QPB : 1], q_pool0[SEL ? QPB : 1];
+  __shared__ __attribute__((aligned(256))) float kscale_lds[2][FP8 ? 64 : 1];   // per tile buffer
+  // step at which every wave shrinks its lists, by the step's parity: a
+  // request for step s + 1 is written during step s, while step s's own
+  // slot is still being read
+  __shared__ int s_req[2];
   __shared__ int run_doc[QPB], run_nc[QPB], run_pool0[QPB];
   constexpr int QW = (QPB + 63) / 64;                // waves holding one query per lane
   __shared__ int run_cnt[QW];
@@ -221,7 +376,7 @@ __global__ __launch_bounds__(64 * kLogitsWaves) void logits_kernel(LogitsArgs a)
 
   // document, causal range and pool offset of each query: a few dependent
   // loads, done before the q rows are requested so they do not queue behind
-  int my_doc = -1, my_nc = 0, my_pool0 = 0;
+  int my_doc = -1, my_nc = 0, my_pool0 = 0, my_start = 0;
   if (tid < QPB) {
     const int t = t0 + tid;
     if (t < a.q_end) {
@@ -229,10 +384,16 @@ __global__ __launch_bounds__(64 * kLogitsWaves) void logits_kernel(LogitsArgs a)
       my_doc = qi.doc;
       my_nc = qi.n_c;
       my_pool0 = qi.pool0;
+      my_start = qi.start;
     }
     q_doc[tid] = my_doc;
     q_nc[tid] = my_nc;
+    if constexpr (SEL) {
+      q_start[tid] = my_start;
+      q_pool0[tid] = my_pool0;
+    }
   }
+  if (tid == 0) s_req[0] = s_req[1] = -1;
   __syncthreads();
   // Runs of queries in one document. Queries are in token order, so each
   // document's queries are consecutive and the last one of a run has the
@@ -271,11 +432,77 @@ __global__ __launch_bounds__(64 * kLogitsWaves) void logits_kernel(LogitsArgs a)
     const DocWork d = run_work(r);
     if (d.jt_lo < d.jt_hi) { r_first = r; break; }
   }
-  if (r_first == n_runs) return;             // nothing to score (uniform)
+  const bool any_work = r_first < n_runs;    // (uniform)
+  if (!SEL && !any_work) return;             // nothing to score
+
+  // fused selection, per output slot k of this lane (query S::query(k, g) of
+  // the wave): entries in the list, the threshold a new score must exceed
+  // (open: no threshold yet, every score enters), the list's first entry
+  int cnt_r[S::N];
+  float thr_r[S::N];
+  bool open_r[S::N];
+  int lbase[S::N];
+#pragma unroll
+  for (int k = 0; k < S::N; ++k) {
+    cnt_r[k] = 0;
+    thr_r[k] = 0.f;
+    open_r[k] = true;
+    lbase[k] = (H == 64 && g == 1) ? QPB * CAP : (wid * QPW + S::query(k, g)) * CAP;
+  }
+  int stepno = 0;
+  // a shrink may keep up to k_sel + slack entries (when the bisection finds
+  // such a threshold first): at most CAP - 160, the bound the trigger
+  // assumes for a list just shrunk
+  const int slack = min(64, CAP - 160 - a.k_sel);
+  int pending = -1;                         // the step at which a shrink was asked for
+  const int gneg = g ? -1 : 0;
+  // every list of the wave above k_sel entries -> its exact top k_sel
+  auto shrink_wave = [&]() {
+#pragma unroll 1
+    for (int qq = 0; qq < QPW; ++qq) {
+      const int kq = qq >> 1, gq = qq & 1;     // the slot and half-wave holding query qq
+      int c = cnt_r[0];
+#pragma unroll
+      for (int k = 1; k < S::N; ++k) c = k == kq ? cnt_r[k] : c;
+      c = __builtin_amdgcn_readlane(c, gq * 32);
+      // a list that a shrink could not cut below k_sel + slack is left as it
+      // is (its threshold must not drop)
+      if (c <= a.k_sel + slack) continue;
+      const int base = (wid * QPW + qq) * CAP;
+      int kept;
+      const uint32_t th = list_select<(SEL ? CAP : 64)>(lval + base, lidx + base, c, a.k_sel,
+                                                        slack, lane, kept);
+      const float tf = key_to_f32(th);
+#pragma unroll
+      for (int k = 0; k < S::N; ++k) {
+        if (k == kq && g == gq) {
+          cnt_r[k] = kept;
+          thr_r[k] = tf;
+          open_r[k] = false;
+        }
+      }
+    }
+  };
+  // at the end of step s, a wave with a list past the trigger asks every
+  // wave to shrink at the start of step s + 2: the request is read at the
+  // start of step s + 1, after the barrier that orders it, and acted on one
+  // step later, so no wave waits for that read
+  auto request_check = [&]() {
+    bool over = false;
+#pragma unroll
+    for (int k = 0; k < S::N; ++k) over |= cnt_r[k] > SC::TRIGGER;
+    // (none when the next step shrinks already: that covers every list)
+    if (__ballot(over) && pending != stepno + 1) {
+      if (lane == 0) s_req[(stepno + 1) & 1] = stepno + 2;
+    }
+  };
+
+  if (any_work) {
   {
     // the first key tile and the q rows are in flight together
     const DocWork d = run_work(r_first);
-    load_key_tile<H, D, FP8>(keys, d.pool0, d.jt_lo * kPoolTile, d.maxnc, tile0, wid, lane);
+    load_key_tile<H, D, FP8>(keys, d.pool0, d.jt_lo * kPoolTile, d.maxnc, tile0, wid, lane,
+                             a.k_scale, kscale_lds[0]);
   }
   {
     const size_t row0 = (size_t)(t0 + wid * QPW) * H, row_last = (size_t)a.q_end * H - 1;
@@ -373,10 +600,8 @@ __global__ __launch_bounds__(64 * kLogitsWaves) void logits_kernel(LogitsArgs a)
 
     // epilogue of one 32-pool unit whose first column is cbase (negative:
     // nothing to store): w' * ReLU, sum over heads, causal mask, store
-    auto epilogue = [&](const f32x16_t (&acc)[MT], int cbase) {
+    auto epilogue = [&](const f32x16_t (&acc)[MT], int cbase, float kscale) {
       const int col = cbase + n;
-      float kscale = 1.f;
-      if constexpr (FP8) kscale = a.k_scale[pool0 + clampi(col, 0, maxnc - 1)];
       // the lane's rows of one query form one multiply-add chain (one VALU
       // op per row after the ReLU; the chain's latency hides behind MFMAs)
       float outv[S::N];
@@ -426,8 +651,31 @@ __global__ __launch_bounds__(64 * kLogitsWaves) void logits_kernel(LogitsArgs a)
 #pragma unroll
       for (int k = 0; k < S::N; ++k) {
         const bool ok = (uint32_t)col < lim[k];
-        const uint32_t off = ok ? roff[k] + (uint32_t)col * 4u : nrec;
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(outv[k] * kscale), orsrc, (int)off, 0, 0);
+        const float sv = outv[k] * kscale;
+        if constexpr (SEL) {
+          // the score enters the query's list when it exceeds the threshold
+          // (NaN never does once there is one). The lanes of one slot's
+          // query are one half-wave: the a entering scores take list
+          // positions cnt .. cnt + a - 1 in lane order, and the other lanes
+          // of the half write into cnt + a .. cnt + 31, past the list's end
+          // (room the shrink protocol keeps free), so every lane stores and
+          // the epilogue stays one branch-free block beside the MFMAs
+          const bool app = ok & (open_r[k] | (sv > thr_r[k]));
+          const uint64_t m = __ballot(app);
+          const uint32_t lo = (uint32_t)m, hi = (uint32_t)(m >> 32);
+          const int lo_cnt = __popc(lo), hi_cnt = __popc(hi);
+          // entering lanes below this one in its half, and in its half
+          const int below =
+              (int)__builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, 0u)) - (lo_cnt & gneg);
+          const int a_cnt = lo_cnt + ((hi_cnt - lo_cnt) & gneg);
+          const int pos = cnt_r[k] + (app ? below : a_cnt + (n - below));
+          lval[lbase[k] + pos] = __float_as_uint(sv);
+          lidx[lbase[k] + pos] = (uint16_t)col;
+          cnt_r[k] += a_cnt;
+        } else {
+          const uint32_t off = ok ? roff[k] + (uint32_t)col * 4u : nrec;
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sv), orsrc, (int)off, 0, 0);
+        }
       }
     };
 
@@ -482,10 +730,12 @@ __global__ __launch_bounds__(64 * kLogitsWaves) void logits_kernel(LogitsArgs a)
     // negative, so every lane's store is masked)
     constexpr int kNoUnit = -(1 << 30);
     int prev = kNoUnit;
+    float ks_prev = 1.f;   // FP8: key scale of this lane's column in accB's unit
 
     if (r != r_first) {  // (the first run's first tile is already on its way)
       __syncthreads();   // both LDS buffers are free
-      load_key_tile<H, D, FP8>(keys, pool0, jt_lo * kPoolTile, maxnc, tile0, wid, lane);
+      load_key_tile<H, D, FP8>(keys, pool0, jt_lo * kPoolTile, maxnc, tile0, wid, lane,
+                               a.k_scale, kscale_lds[0]);
     }
 
     // Tiles alternate between tile0 and tile1; the body is instantiated once
@@ -493,28 +743,112 @@ __global__ __launch_bounds__(64 * kLogitsWaves) void logits_kernel(LogitsArgs a)
     // The DMA of tile jt was issued at the start of the previous step, before
     // that step's kUnits * S::N output stores: waiting until only those
     // stores are outstanding covers the DMA without waiting for the stores.
-    auto step = [&](const int jt, const uint8_t* __restrict__ tb, uint8_t* __restrict__ nb) {
-      if (jt == jt_lo) wait_vmem_all();
+    // The fused selection issues no stores in a step, so it waits for
+    // everything (the DMA).
+    static_assert(kUnits == 2, "one pair of 32-pool units per tile");
+    auto step = [&](const int jt, const uint8_t* __restrict__ tb, uint8_t* __restrict__ nb,
+                    const int buf) {
+      if (SEL || jt == jt_lo) wait_vmem_all();
       else wait_vmem_leave<kUnits * S::N>();
       __syncthreads();   // tile jt is in LDS; tile jt - 1 is no longer read
+      // FP8: this tile's key scales of the lane's two columns, read before
+      // the next copy may overwrite the other buffer's
+      float ks0 = 1.f, ks1 = 1.f;
+      if constexpr (FP8) {
+        ks0 = kscale_lds[buf][n];
+        ks1 = kscale_lds[buf][32 + n];
+      }
       const int j0 = jt * kPoolTile;
-      if (jt + 1 < jt_hi) load_key_tile<H, D, FP8>(keys, pool0, j0 + kPoolTile, maxnc, nb, wid, lane);
-#pragma unroll
-      for (int u = 0; u < kUnits; u += 2) {
-        mma(accA, tb, u);
-        epilogue(accB, prev);
-        interleave();
-        mma(accB, tb, u + 1);
-        epilogue(accA, j0 + 32 * u);
-        interleave();
-        prev = j0 + 32 * u + 32;
+      if (jt + 1 < jt_hi)
+        load_key_tile<H, D, FP8>(keys, pool0, j0 + kPoolTile, maxnc, nb, wid, lane, a.k_scale,
+                                 kscale_lds[buf ^ 1]);
+      if constexpr (SEL) {
+        if (pending == stepno) shrink_wave();         // every wave at the same step
+        pending = s_req[stepno & 1];
+      }
+      mma(accA, tb, 0);
+      epilogue(accB, prev, ks_prev);
+      interleave();
+      mma(accB, tb, 1);
+      epilogue(accA, j0, ks0);
+      interleave();
+      prev = j0 + 32;
+      ks_prev = ks1;
+      if constexpr (SEL) {
+        request_check();
+        ++stepno;
       }
     };
     for (int jt = jt_lo; jt < jt_hi; jt += 2) {
-      step(jt, tile0, tile1);
-      if (jt + 1 < jt_hi) step(jt + 1, tile1, tile0);
+      step(jt, tile0, tile1, 0);
+      if (jt + 1 < jt_hi) step(jt + 1, tile1, tile0, 1);
     }
-    epilogue(accB, prev);
+    epilogue(accB, prev, ks_prev);
+    if constexpr (SEL) request_check();
+  }
+  }  // any_work
+
+  if constexpr (SEL) {
+    // ---- token rows of the wave's queries: the exact top k_sel of each
+    // list (ascending pools), or every causal pool when n_c <= k_sel; then
+    // the tail tokens and -1 padding
+    const bool vec4 = a.kpool == 4 && (a.width & 3) == 0;
+#pragma unroll 1
+    for (int qq = 0; qq < QPW; ++qq) {
+      const int qb = wid * QPW + qq;
+      const int t = t0 + qb;
+      if (t >= a.q_end) break;
+      const int n_c = q_nc[qb];
+      const int start = q_start[qb];
+      const int n_sel = n_c < a.k_sel ? n_c : a.k_sel;
+      const int base = qb * CAP;
+      if (n_c > a.k_sel) {
+        const int kq = qq >> 1, gq = qq & 1;
+        int c = cnt_r[0];
+#pragma unroll
+        for (int k = 1; k < S::N; ++k) c = k == kq ? cnt_r[k] : c;
+        c = __builtin_amdgcn_readlane(c, gq * 32);
+        int kept;
+        if (c > a.k_sel)
+          list_select<(SEL ? CAP : 64)>(lval + base, lidx + base, c, a.k_sel, 0, lane, kept);
+      }
+      const int tail = a.tail_on ? (t - start + 1) % a.kpool : 0;
+      const int row = t - a.q_begin;
+      int32_t* otok = a.out_tok + (size_t)row * a.width;
+      if (a.out_ids) {
+        int32_t* oid = a.out_ids + (size_t)row * a.k_sel;
+        const int pool0 = q_pool0[qb];
+        for (int j = lane; j < a.k_sel; j += 64)
+          oid[j] = j < n_sel ? pool0 + (n_c > a.k_sel ? (int)lidx[base + j] : j) : -1;
+      }
+      const int from = n_sel * a.kpool;              // tail and padding start here
+      const int tail_base = start + n_c * a.kpool;
+      if (vec4) {
+        for (int j = lane; j < n_sel; j += 64) {
+          const int pb = start + 4 * (n_c > a.k_sel ? (int)lidx[base + j] : j);
+          *reinterpret_cast<int4*>(otok + 4 * j) = make_int4(pb, pb + 1, pb + 2, pb + 3);
+        }
+        for (int gi = (from >> 2) + lane; gi < (a.width >> 2); gi += 64) {
+          int e[4];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const int jj = gi * 4 + c - from;
+            e[c] = jj < tail ? tail_base + jj : -1;
+          }
+          *reinterpret_cast<int4*>(otok + gi * 4) = make_int4(e[0], e[1], e[2], e[3]);
+        }
+      } else {
+        for (int j = lane; j < from; j += 64) {
+          const int e = j / a.kpool;
+          const int p = n_c > a.k_sel ? (int)lidx[base + e] : e;
+          otok[j] = start + p * a.kpool + (j - e * a.kpool);
+        }
+        for (int j = from + lane; j < a.width; j += 64) {
+          const int jj = j - from;
+          otok[j] = jj < tail ? tail_base + jj : -1;
+        }
+      }
+    }
   }
 }
 
@@ -524,7 +858,7 @@ __global__ void fill_kernel(float* __restrict__ out, size_t count, float v) {
   for (; i < count; i += stride) out[i] = v;
 }
 
-template <int H, int D, bool FP8>
+template <int H, int D, bool FP8, bool SEL>
 static void launch_hdf(LogitsArgs a, hipStream_t st) {
   constexpr int QPB = LogitsCfg<H, D, FP8>::QPB;
   const int rows = a.q_end - a.q_begin;
@@ -535,21 +869,23 @@ static void launch_hdf(LogitsArgs a, hipStream_t st) {
   // frees first. Each piece pays the start-up again (about 8 us to bring in
   // its q rows), so this pays only for long sweeps: measured on the 64K
   // context (16384 pools, BF16) it gains about 1 %, and it loses at 8192
-  // pools on the FP8 path, whose sweep is half as long per pool.
+  // pools on the FP8 path, whose sweep is half as long per pool. The fused
+  // selection keeps each query's candidates in its workgroup, so it takes
+  // whole blocks.
   const long sweep = (long)a.max_pools * (FP8 ? 1 : 2);
-  a.pieces = sweep >= 32768 ? 2 : 1;
+  a.pieces = (!SEL && sweep >= 32768) ? 2 : 1;
   const int groups = ((rows + QPB - 1) / QPB + 7) / 8;
-  logits_kernel<H, D, FP8><<<groups * 8 * a.pieces, 64 * kLogitsWaves, 0, st>>>(a);
+  logits_kernel<H, D, FP8, SEL><<<groups * 8 * a.pieces, 64 * kLogitsWaves, 0, st>>>(a);
 }
 
-template <int D, bool FP8>
+template <int D, bool FP8, bool SEL>
 static void launch_df(const LogitsArgs& a, hipStream_t st) {
   switch (a.H) {
-    case 4: launch_hdf<4, D, FP8>(a, st); break;
-    case 8: launch_hdf<8, D, FP8>(a, st); break;
-    case 16: launch_hdf<16, D, FP8>(a, st); break;
-    case 32: launch_hdf<32, D, FP8>(a, st); break;
-    default: launch_hdf<64, D, FP8>(a, st); break;
+    case 4: launch_hdf<4, D, FP8, SEL>(a, st); break;
+    case 8: launch_hdf<8, D, FP8, SEL>(a, st); break;
+    case 16: launch_hdf<16, D, FP8, SEL>(a, st); break;
+    case 32: launch_hdf<32, D, FP8, SEL>(a, st); break;
+    default: launch_hdf<64, D, FP8, SEL>(a, st); break;
   }
 }
 
@@ -561,9 +897,39 @@ void launch_logits(const LogitsArgs& a, hipStream_t st) {
     const int blocks = (int)std::min<size_t>((count + 255) / 256, 8192);
     fill_kernel<<<blocks, 256, 0, st>>>(a.out, count, -INFINITY);
   }
-  if (a.fp8) launch_df<128, true>(a, st);
-  else if (a.D == 128) launch_df<128, false>(a, st);
-  else launch_df<64, false>(a, st);
+  if (a.fp8) launch_df<128, true, false>(a, st);
+  else if (a.D == 128) launch_df<128, false, false>(a, st);
+  else launch_df<64, false, false>(a, st);
+}
+
+template <int D, bool FP8>
+static int sel_capacity(int H) {
+  switch (H) {
+    case 4: return SelCfg<4, D, FP8>::CAP;
+    case 8: return SelCfg<8, D, FP8>::CAP;
+    case 16: return SelCfg<16, D, FP8>::CAP;
+    case 32: return SelCfg<32, D, FP8>::CAP;
+    default: return SelCfg<64, D, FP8>::CAP;
+  }
+}
+
+int logits_select_max_ksel(int H, int D, int fp8) {
+  const int cap = fp8 ? sel_capacity<128, true>(H)
+                      : (D == 128 ? sel_capacity<128, false>(H) : sel_capacity<64, false>(H));
+  // a list just shrunk holds at least k_sel entries and takes up to 160 more
+  // before the next shrink
+  return cap - 160 > 0 ? cap - 160 : 0;
+}
+
+bool logits_select_supported(int H, int D, int fp8, int k_sel) {
+  return k_sel >= 1 && k_sel <= logits_select_max_ksel(H, D, fp8);
+}
+
+void launch_logits_select(const LogitsArgs& a, hipStream_t st) {
+  if (a.q_end <= a.q_begin) return;
+  if (a.fp8) launch_df<128, true, true>(a, st);
+  else if (a.D == 128) launch_df<128, false, true>(a, st);
+  else launch_df<64, false, true>(a, st);
 }
 
 }  // namespace kpool

@@ -34,8 +34,12 @@ int main(void) {
 
   CHECK(kpool_abi_version() == KPOOL_ABI_VERSION);
   CHECK(kpool_logits_ld(&p) == 16384);
+  CHECK(kpool_query_chunk_rows(&p) == 4096);
   ws = kpool_workspace_bytes(&p);
   CHECK(ws >= (size_t)4096 * 16384 * 4);
+  CHECK(kpool_fused_max_ksel(&p) == 1184);
+  CHECK(kpool_fused_workspace_bytes(&p) == 0); /* no logits tile */
+  CHECK(kpool_decode_noalloc_max_bytes() == ((size_t)32 << 20));
   CHECK(strcmp(kpool_status_string(KPOOL_OK), "ok") == 0);
   CHECK(strcmp(kpool_status_string(KPOOL_E_WORKSPACE), "workspace too small") == 0);
 

@@ -45,6 +45,14 @@ def test_workspace_and_ld():
     p8 = P(use_fp8=1, total_tokens=32768, max_seqlen=32768)
     ws8 = kp.kpool_workspace_bytes(p8)
     assert ws8 >= 4096 * 8192 * 4 + 32768 * 32 * (128 + 4) + 8192 * 132
+    # the fused entry point: no tile; FP8 codes and scales only
+    assert kp.kpool_fused_max_ksel(p) == 1184
+    assert kp.kpool_fused_max_ksel(p8) == 1344
+    assert kp.kpool_fused_max_ksel(P(num_heads=4, head_dim=128)) == 0
+    assert kp.kpool_fused_max_ksel(P(num_heads=12)) == 0
+    assert kp.kpool_fused_workspace_bytes(p) == 0
+    assert kp.kpool_fused_workspace_bytes(p8) == 32768 * 32 * (128 + 4) + 8192 * 132
+    assert kp.kpool_fused_workspace_bytes(P(index_topk=4 * 1185)) == 0
     assert kp.kpool_logits_ld(P(max_seqlen=4097, total_tokens=5000)) == 1024
     assert kp.kpool_logits_ld(P(max_seqlen=4100, total_tokens=5000)) == 1088
     assert kp.kpool_workspace_bytes(P(total_tokens=0, max_seqlen=0)) == 0
@@ -56,7 +64,8 @@ def test_workspace_and_ld():
     assert kp.kpool_query_chunk_rows(P(query_chunk=333)) == 333
     assert kp.kpool_query_chunk_rows(P(query_chunk=10 ** 6)) == 65536   # capped at T
     assert kp.kpool_query_chunk_rows(P(total_tokens=0, max_seqlen=0)) == 0
-    assert kp.kpool_workspace_bytes(P(query_chunk=0, total_tokens=19679, max_seqlen=3789)) >= 19679 * 960 * 4
+    assert kp.kpool_workspace_bytes(P(num_heads=4, query_chunk=0, total_tokens=19679,
+                                      max_seqlen=3789)) >= 19679 * 960 * 4
     # unsupported or invalid parameters size to 0
     assert kp.kpool_workspace_bytes(P(num_heads=12)) == 0
     assert kp.kpool_workspace_bytes(P(max_seqlen=70000)) == 0
@@ -116,10 +125,19 @@ def test_pointer_checks():
     # misaligned output
     assert raw("kpool_indexer_topk", pref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, FAKE + 4, None, None) == kp.KPOOL_E_INVALID
     assert "out_token_idx" in kp.kpool_last_error()
-    # workspace too small
+    # workspace too small / misaligned / null
     assert raw("kpool_indexer_topk", pref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws - 1, FAKE, None, None) == kp.KPOOL_E_WORKSPACE
-    # misaligned workspace
     assert raw("kpool_indexer_topk", pref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 16, ws, FAKE, None, None) == kp.KPOOL_E_INVALID
+    assert raw("kpool_indexer_topk", pref(p), FAKE, FAKE, FAKE, FAKE, FAKE, None, ws, FAKE, None, None) == kp.KPOOL_E_INVALID
+    assert "workspace is null" in kp.kpool_last_error()
+    # the fused entry point: a K_sel beyond its list is refused first
+    pbig = P(index_topk=4 * 1185)
+    assert raw("kpool_indexer_topk_fused", pref(pbig), FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, FAKE, None, None) == kp.KPOOL_E_UNSUPPORTED
+    assert "fused" in kp.kpool_last_error()
+    p8 = P(use_fp8=1, total_tokens=32768, max_seqlen=32768)
+    ws8 = kp.kpool_fused_workspace_bytes(p8)
+    assert raw("kpool_indexer_topk_fused", pref(p8), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws8 - 1, FAKE, None, None) == kp.KPOOL_E_WORKSPACE
+    assert raw("kpool_indexer_topk_fused", pref(p), None, FAKE, FAKE, FAKE, FAKE, None, 0, FAKE, None, None) == kp.KPOOL_E_INVALID
     # compress: null keys
     assert raw("kpool_compress", pref(p), None, FAKE, FAKE, FAKE, FAKE, FAKE, None) == kp.KPOOL_E_INVALID
     # logits: rows out of range
