@@ -53,7 +53,8 @@ def build(verbose: bool = True, out: str = LIB, defines=()) -> str:
         objs = list(ex.map(lambda src: _compile(src, build_dir, tuple(defines)), SOURCES))
     LIBOUT = out
     tmp = LIBOUT + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs,
+           "-L/opt/rocm/lib", "-Wl,-rpath,/opt/rocm/lib", "-lrocprofiler-sdk-roctx", "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

@@ -7,13 +7,27 @@
 #include <algorithm>
 #include <cstdarg>
 #include <cstdio>
+#include <cstring>
 #include <mutex>
 #include <string>
+
+#include <rocprofiler-sdk-roctx/roctx.h>
 
 #include "kpool.h"
 #include "kpool_internal.h"
 
 namespace {
+
+// A roctx range around the host side of one phase (its validation and
+// launches), so a profiler's marker trace shows compress, each chunk's
+// scoring and selection, and the serving calls by name. Without a profiler
+// attached the calls return at once.
+struct Range {
+  explicit Range(const char* name) { roctxRangePushA(name); }
+  ~Range() { roctxRangePop(); }
+  Range(const Range&) = delete;
+  Range& operator=(const Range&) = delete;
+};
 
 thread_local std::string g_last_error;
 
@@ -258,6 +272,7 @@ int32_t kpool_query_chunk_rows(const kpool_params* p) {
 kpool_status kpool_compress(const kpool_params* p, const void* k, const void* gate,
                             const float* ape, const int32_t* cu_seqlens, int32_t* cu_pools,
                             void* pooled, void* stream) {
+  Range range("kpool_compress");
   Derived d;
   CHECK(derive(p, &d, false));
   CHECK(check_ptr(cu_seqlens, 4, "cu_seqlens"));
@@ -281,6 +296,7 @@ kpool_status kpool_indexer_topk(const kpool_params* p, const void* q, const floa
                                 const int32_t* cu_pools, void* workspace,
                                 size_t workspace_bytes, int32_t* out_token_idx,
                                 int32_t* out_pool_idx, void* stream) {
+  Range range("kpool_indexer_topk");
   Derived d;
   CHECK(derive(p, &d, true));
   if (d.T == 0) return ok();
@@ -289,7 +305,10 @@ kpool_status kpool_indexer_topk(const kpool_params* p, const void* q, const floa
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
   (void)hipGetLastError();
-  if (d.fp8) quantize_inputs(d, q, pooled, cu_pools, 0, d.T, ws, st);
+  if (d.fp8) {
+    Range r("kpool.fp8_quantize");
+    quantize_inputs(d, q, pooled, cu_pools, 0, d.T, ws, st);
+  }
   kpool::LogitsArgs a = logits_args(d, q, w, pooled, cu_seqlens, cu_pools, ws);
   a.out = reinterpret_cast<float*>(ws + d.off_logits);
   a.skip_select_all = 1;
@@ -297,7 +316,11 @@ kpool_status kpool_indexer_topk(const kpool_params* p, const void* q, const floa
     const int c1 = std::min(d.T, c0 + d.qc);
     a.q_begin = c0;
     a.q_end = c1;
-    kpool::launch_logits(a, st);
+    {
+      Range r("kpool.logits");
+      kpool::launch_logits(a, st);
+    }
+    Range r("kpool.select_expand");
     kpool::launch_select(a.out, d.ld, c0, c1, cu_seqlens, cu_pools, d.B, d.T, d.kpool, d.k_sel,
                          d.width, d.tail, d.max_pools,
                          out_pool_idx ? out_pool_idx + (size_t)c0 * d.k_sel : nullptr,
@@ -325,6 +348,7 @@ kpool_status kpool_indexer_topk_fused(const kpool_params* p, const void* q, cons
                                       const int32_t* cu_pools, void* workspace,
                                       size_t workspace_bytes, int32_t* out_token_idx,
                                       int32_t* out_pool_idx, void* stream) {
+  Range range("kpool_indexer_topk_fused");
   Derived d;
   CHECK(derive(p, &d, true));
   if (!d.fused)
@@ -556,6 +580,7 @@ kpool_status kpool_decode_topk(const kpool_params* p, const void* q, const float
                                const int32_t* seq_lens, const int32_t* token_base,
                                void* workspace, size_t workspace_bytes,
                                int32_t* out_token_idx, int32_t* out_pool_idx, void* stream) {
+  Range range("kpool_decode_topk");
   DecodeDerived d;
   CHECK(derive_decode(p, &d));
   CHECK(check_decode_args(d, q, w, pooled, pooled_rows, pooled_scale, pool_start, seq_lens,
@@ -575,6 +600,7 @@ kpool_status kpool_decode_topk_noalloc(const kpool_params* p, const void* q, con
                                        const int32_t* seq_lens, const int32_t* token_base,
                                        int32_t* out_token_idx, int32_t* out_pool_idx,
                                        void* stream) {
+  Range range("kpool_decode_topk_noalloc");
   DecodeDerived d;
   CHECK(derive_decode(p, &d));
   if (d.total > kScratchBytes)
@@ -594,6 +620,7 @@ kpool_status kpool_compress_pools(const kpool_params* p, const void* k, const vo
                                   const float* ape, int32_t num_pools, const int32_t* dst_rows,
                                   int32_t pooled_rows, void* pooled, float* pooled_scale,
                                   void* stream) {
+  Range range("kpool_compress_pools");
   if (!p) return fail(KPOOL_E_INVALID, "params is null");
   const int D = p->head_dim, kp = p->kpool;
   if (p->use_fp8 != 0 && p->use_fp8 != 1) return fail(KPOOL_E_INVALID, "use_fp8 must be 0 or 1");
@@ -635,7 +662,11 @@ kpool_status kpool_fp8_quantize(const void* x, int32_t rows, uint8_t* codes, flo
 }
 
 const char* kpool_status_string(kpool_status s) {
-  switch (s) {
+  // a C caller may pass any int: read it as one (an out-of-range value
+  // loaded as the enum type would be undefined in C++)
+  int v;
+  std::memcpy(&v, &s, sizeof v);
+  switch (v) {
     case KPOOL_OK: return "ok";
     case KPOOL_E_INVALID: return "invalid argument";
     case KPOOL_E_UNSUPPORTED: return "unsupported shape";

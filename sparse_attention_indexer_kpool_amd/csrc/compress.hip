@@ -96,21 +96,27 @@ __global__ __launch_bounds__(256) void compress_kernel(
     for (int e = 0; e < 8; ++e) { z[e] = 0.f; acc[e] = 0.f; m[e] = -INFINITY; }
     if constexpr (KP > 0) {
       // all slot slices of the pool in registers: one read of gate and k.
-      // The memory clobber and the scheduling barrier keep every load issued
+      // The gate slices and the position bias are requested first and the
+      // key slices last, so the softmax weights (which need only the gate)
+      // are computed while the key slices are still on their way: the
+      // compiler's wait for the last gate load leaves the key loads
+      // outstanding (vector-memory loads complete in issue order). The
+      // memory clobber and the scheduling barrier keep every load issued
       // before the first use; left alone, the scheduler sinks the k loads to
       // their uses and each then waits a full memory round trip of its own.
       uint4 g4[KP], k4[KP];
       float4 ap[KP][2];
 #pragma unroll
-      for (int s = 0; s < KP; ++s) {
+      for (int s = 0; s < KP; ++s)
         g4[s] = *reinterpret_cast<const uint4*>(gate + (size_t)(t0 + s) * D + d0);
-        k4[s] = *reinterpret_cast<const uint4*>(k + (size_t)(t0 + s) * D + d0);
-      }
 #pragma unroll
       for (int s = 0; s < KP; ++s) {
         ap[s][0] = *reinterpret_cast<const float4*>(ape + s * D + d0);
         ap[s][1] = *reinterpret_cast<const float4*>(ape + s * D + d0 + 4);
       }
+#pragma unroll
+      for (int s = 0; s < KP; ++s)
+        k4[s] = *reinterpret_cast<const uint4*>(k + (size_t)(t0 + s) * D + d0);
       asm volatile("" ::: "memory");
       __builtin_amdgcn_sched_barrier(0);
       float a[KP][8];
@@ -126,17 +132,23 @@ __global__ __launch_bounds__(256) void compress_kernel(
           m[e] = fmaxf(m[e], a[s][e]);
         }
       }
+      // the weights, before any key slice is touched
 #pragma unroll
       for (int s = 0; s < KP; ++s) {
-        const uint32_t kw[4] = {k4[s].x, k4[s].y, k4[s].z, k4[s].w};
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           // hardware exp2 of the argument times log2(e): a few FP32 ulps
           // from the exact exponential, far inside the BF16 result's ulp
-          const float ex = __expf(a[s][e] - m[e]);
-          z[e] += ex;
-          acc[e] += ex * lo_hi(kw[e >> 1], e & 1);
+          a[s][e] = __expf(a[s][e] - m[e]);
+          z[e] += a[s][e];
         }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int s = 0; s < KP; ++s) {
+        const uint32_t kw[4] = {k4[s].x, k4[s].y, k4[s].z, k4[s].w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] += a[s][e] * lo_hi(kw[e >> 1], e & 1);
       }
     } else {
       // runtime kpool: pass 1 finds the per-dimension maximum, pass 2 the
