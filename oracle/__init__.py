@@ -15,7 +15,10 @@ from .kpool_oracle import (  # noqa: F401
     expand_row,
     fp8_quantize_rows,
     fwht128,
+    indexer_projections,
     indexer_topk,
+    layer_norm,
+    linear_bf16,
     pow2_row_exponent,
     row_scores,
     select_pools,

@@ -374,3 +374,51 @@ def decode_topk(q, w, pooled, pool_start, seq_lens, kpool: int, index_topk: int,
         tok[b] = np.where(row >= 0, row + base, -1)
     return tok, pid
 
+
+
+# ---------------------------------------------------------------------------
+# The indexer projections feeding the path ([MLM] section 4, the DSA indexer
+# precision split and its forward fragment: q from linear_wq_b of the query
+# latent, k = k_norm(linear_wk(x)), the head weights from linear_weights_proj
+# kept in FP32; [MLM] section 3: the per-token compression gate). Readings:
+# the compression gate is a linear map of the same input x to D gate logits
+# per token (BF16, like linear_wk); a linear layer's BF16 output is its FP32
+# product rounded to BF16, and k_norm is a LayerNorm over the D values of a
+# row, evaluated in FP32 on the BF16 output of linear_wk. No rotary embedding
+# (the NoPE indexer) and no activation rotation.
+# ---------------------------------------------------------------------------
+
+def linear_bf16(a, w):
+    """A BF16 linear layer: a [T, K] @ w[N, K]^T with FP32 products and sums,
+    rounded to BF16 (returned as FP32 holding BF16 values)."""
+    a = np.asarray(a, dtype=F32)
+    w = np.asarray(w, dtype=F32)
+    return bf16_round((a @ w.T).astype(F32))
+
+
+def layer_norm(v, gamma, beta, eps: float):
+    """LayerNorm of each row of v over its last axis, in FP32: (v - mean) /
+    sqrt(var + eps) * gamma + beta, var the mean squared deviation."""
+    v = np.asarray(v, dtype=F32)
+    mean = (v.sum(axis=1, dtype=F32) / F32(v.shape[1])).astype(F32)
+    dev = (v - mean[:, None]).astype(F32)
+    var = ((dev * dev).sum(axis=1, dtype=F32) / F32(v.shape[1])).astype(F32)
+    inv = (F32(1.0) / np.sqrt(var + F32(eps))).astype(F32)
+    return (dev * inv[:, None] * np.asarray(gamma, F32)[None, :]
+            + np.asarray(beta, F32)[None, :]).astype(F32)
+
+
+def indexer_projections(x, qr, wq_b, wk, k_norm_weight, k_norm_bias, wg, ww,
+                        num_heads: int, head_dim: int, eps: float = 1e-6):
+    """The four inputs of the indexer for T tokens.
+      x   [T, hidden] (BF16 values), qr [T, q_lora_rank] (BF16 values)
+      wq_b [H*D, q_lora_rank], wk [D, hidden], wg [D, hidden] (BF16 values)
+      k_norm_weight, k_norm_bias [D] (FP32); ww [H, hidden] (FP32)
+    Returns q [T, H, D] (BF16 values), k [T, D] (BF16 values), gate [T, D]
+    (BF16 values) and w [T, H] (FP32)."""
+    T = np.asarray(x).shape[0]
+    q = linear_bf16(qr, wq_b).reshape(T, num_heads, head_dim)
+    k = bf16_round(layer_norm(linear_bf16(x, wk), k_norm_weight, k_norm_bias, eps))
+    gate = linear_bf16(x, wg)
+    w = (np.asarray(x, dtype=F32) @ np.asarray(ww, dtype=F32).T).astype(F32)
+    return q, k, gate, w

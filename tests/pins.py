@@ -643,4 +643,101 @@ def pin_decode_fp8_is_last_token_row(o):
         assert np.array_equal(dpid[b], np.where(pid >= 0, pid + starts[b], -1)), b
 
 
+# ---------------------------------------------------------------------------
+# the indexer projections
+# ---------------------------------------------------------------------------
+
+def _proj_case(seed, T=24, hidden=192, qlr=96, H=4, D=32):
+    g = torch.Generator().manual_seed(seed)
+    bf = lambda *sh, s=1.0: (s * torch.randn(*sh, generator=g)).to(torch.bfloat16).float().numpy()
+    x, qr = bf(T, hidden), bf(T, qlr)
+    wq_b, wk, wg = bf(H * D, qlr, s=qlr ** -0.5), bf(D, hidden, s=hidden ** -0.5), bf(D, hidden, s=hidden ** -0.5)
+    gamma = (1.0 + 0.1 * torch.randn(D, generator=g)).numpy().astype(np.float32)
+    beta = (0.1 * torch.randn(D, generator=g)).numpy().astype(np.float32)
+    ww = (hidden ** -0.5 * torch.randn(H, hidden, generator=g)).numpy().astype(np.float32)
+    return x, qr, wq_b, wk, gamma, beta, wg, ww, H, D
+
+
+def pin_linear_bf16_matches_library(o):
+    """A BF16 linear layer: the FP64 product rounded to BF16 by torch, within
+    one BF16 ulp (FP32 accumulation can cross a rounding boundary) plus the
+    FP32 dot-product bound; most elements equal."""
+    x, qr, wq_b, wk, gamma, beta, wg, ww, H, D = _proj_case(1)
+    got = o.linear_bf16(x, wk)
+    exact = torch.from_numpy(x).double() @ torch.from_numpy(wk).double().T
+    ref = exact.to(torch.bfloat16).double().numpy()
+    bound = 2 * x.shape[1] * 2.0 ** -24 * (np.abs(x) @ np.abs(wk).T)
+    assert_within_bf16_ulps(got, ref, 1, bound)
+    assert np.mean(got == ref) > 0.97
+
+
+def pin_layer_norm_matches_library(o):
+    """LayerNorm vs torch's layer_norm in FP64 (weight and bias), within FP32
+    rounding; with weight 1 and bias 0 each row has mean 0 and variance
+    var / (var + eps)."""
+    g = torch.Generator().manual_seed(2)
+    v = (3.0 * torch.randn(40, 64, generator=g) + 1.5).numpy().astype(np.float32)
+    gamma = (1.0 + 0.2 * torch.randn(64, generator=g)).numpy().astype(np.float32)
+    beta = (0.3 * torch.randn(64, generator=g)).numpy().astype(np.float32)
+    got = o.layer_norm(v, gamma, beta, 1e-6)
+    ref = torch.nn.functional.layer_norm(torch.from_numpy(v).double(), (64,),
+                                         torch.from_numpy(gamma).double(),
+                                         torch.from_numpy(beta).double(), 1e-6).numpy()
+    assert np.allclose(got, ref, rtol=1e-5, atol=1e-5)
+    plain = o.layer_norm(v, np.ones(64, np.float32), np.zeros(64, np.float32), 1e-2)
+    var = v.astype(np.float64).var(axis=1)
+    assert np.allclose(plain.mean(axis=1), 0.0, atol=1e-5)
+    assert np.allclose(plain.astype(np.float64).var(axis=1), var / (var + 1e-2), rtol=1e-4)
+    # a constant row normalises to the bias exactly (the deviation is 0)
+    const = o.layer_norm(np.full((1, 64), 7.25, np.float32), gamma, beta, 1e-6)
+    assert np.array_equal(const[0], beta)
+
+
+def pin_projections_onehot(o):
+    """x = e_i: the gate is column i of wg, the head weights column i of ww
+    (FP32, exact), k the LayerNorm of column i of wk (FP64 closed form, then
+    BF16); q = e_j of the query latent gives column j of wq_b per head."""
+    x, qr, wq_b, wk, gamma, beta, wg, ww, H, D = _proj_case(3)
+    T, hidden = x.shape
+    xs = np.zeros_like(x)
+    xs[np.arange(T), np.arange(T) % hidden] = 1.0
+    qs = np.zeros_like(qr)
+    qs[np.arange(T), (3 * np.arange(T)) % qr.shape[1]] = 1.0
+    q, k, gate, w = o.indexer_projections(xs, qs, wq_b, wk, gamma, beta, wg, ww, H, D)
+    for t in range(T):
+        i, j = t % hidden, (3 * t) % qr.shape[1]
+        assert np.array_equal(gate[t], wg[:, i])
+        assert np.array_equal(w[t], ww[:, i])
+        col = wk[:, i].astype(np.float64)
+        ln = (col - col.mean()) / np.sqrt(col.var() + 1e-6) * gamma + beta
+        assert np.allclose(k[t], ln, rtol=2 ** -7, atol=1e-6)
+        assert np.array_equal(q[t].reshape(-1), wq_b[:, j])
+        assert np.array_equal(q[t, 1], wq_b[D:2 * D, j])
+
+
+def pin_k_path_golden(o):
+    """k = BF16(LayerNorm(BF16(x wk^T))): an FP64 evaluation of the same
+    steps (the linear output rounded to BF16 before the norm) agrees on
+    almost every element and within one BF16 ulp everywhere."""
+    x, qr, wq_b, wk, gamma, beta, wg, ww, H, D = _proj_case(4, T=64)
+    _, k, _, _ = o.indexer_projections(x, qr, wq_b, wk, gamma, beta, wg, ww, H, D)
+    lin = (torch.from_numpy(x).double() @ torch.from_numpy(wk).double().T).to(torch.bfloat16).double()
+    ln = torch.nn.functional.layer_norm(lin, (D,), torch.from_numpy(gamma).double(),
+                                        torch.from_numpy(beta).double(), 1e-6)
+    ref = ln.to(torch.bfloat16).double().numpy()
+    assert_within_bf16_ulps(k, ref, 1)
+    assert np.mean(k == ref) > 0.98
+
+
+def pin_head_weights_fp32(o):
+    """The head weights stay in FP32: FP64 product within the FP32
+    dot-product bound, and not rounded to BF16."""
+    x, qr, wq_b, wk, gamma, beta, wg, ww, H, D = _proj_case(5)
+    _, _, _, w = o.indexer_projections(x, qr, wq_b, wk, gamma, beta, wg, ww, H, D)
+    ref = x.astype(np.float64) @ ww.astype(np.float64).T
+    bound = 2 * x.shape[1] * 2.0 ** -24 * (np.abs(x).astype(np.float64) @ np.abs(ww).T)
+    assert np.all(np.abs(w - ref) <= bound)
+    assert np.mean(o.bf16_round(w) != w) > 0.9
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

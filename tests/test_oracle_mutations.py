@@ -55,6 +55,17 @@ MUTATIONS = {
     "fp8_q_not_quantised": ("_, _, q_t = fp8_quantize_rows(q_t)", "pass"),
     "bf16_truncates": ("r = (u + np.uint64(0x7FFF) + keep_lsb)", "r = (u + np.uint64(0))"),
     "bf16_ties_away": ("r = (u + np.uint64(0x7FFF) + keep_lsb)", "r = (u + np.uint64(0x8000))"),
+    "ln_no_eps": ("np.sqrt(var + F32(eps))", "np.sqrt(var)"),
+    "ln_var_unbiased": ("var = ((dev * dev).sum(axis=1, dtype=F32) / F32(v.shape[1]))",
+                        "var = ((dev * dev).sum(axis=1, dtype=F32) / F32(v.shape[1] - 1))"),
+    "ln_bias_not_added": ("+ np.asarray(beta, F32)[None, :]", "+ 0 * np.asarray(beta, F32)[None, :]"),
+    "k_lin_not_rounded": ("k = bf16_round(layer_norm(linear_bf16(x, wk), k_norm_weight",
+                          "k = bf16_round(layer_norm((np.asarray(x, F32) @ np.asarray(wk, F32).T), k_norm_weight"),
+    "head_weights_bf16": ("w = (np.asarray(x, dtype=F32) @ np.asarray(ww, dtype=F32).T).astype(F32)",
+                          "w = bf16_round((np.asarray(x, dtype=F32) @ np.asarray(ww, dtype=F32).T).astype(F32))"),
+    "q_heads_transposed": ("q = linear_bf16(qr, wq_b).reshape(T, num_heads, head_dim)",
+                           "q = linear_bf16(qr, wq_b).reshape(T, head_dim, num_heads).transpose(0, 2, 1)"),
+    "gate_from_wk": ("gate = linear_bf16(x, wg)", "gate = linear_bf16(x, wk)"),
 }
 
 
