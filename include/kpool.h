@@ -290,6 +290,42 @@ kpool_status kpool_decode_topk(const kpool_params* p, const void* q, const float
                                void* workspace, size_t workspace_bytes,
                                int32_t* out_token_idx, int32_t* out_pool_idx, void* stream);
 
+/* ---- The indexer projections -------------------------------------------
+ * ([MLM] section 4, the DSA indexer's forward and its precision split;
+ * section 3, the per-token compression gate.) The four inputs of the
+ * indexer for T tokens, from the layer input x and the query latent qr:
+ *   q    = BF16(qr wq_b^T)                  [T, H*D], read as [T, H, D]
+ *   k    = BF16(LayerNorm(BF16(x wk^T)))    [T, D]   (k_norm, FP32 inside)
+ *   gate = BF16(x wg^T)                     [T, D]   (compression gate logits)
+ *   w    = x ww^T in FP32                   [T, H]   (head weights)
+ * with FP32 accumulation and round-to-nearest-even. LayerNorm over the D
+ * values of a row: (v - mean) / sqrt(var + eps) * k_norm_weight +
+ * k_norm_bias, var the mean squared deviation. No rotary embedding (the
+ * NoPE indexer) and no activation rotation. The gate is read as a linear
+ * map of x (the pages name the parameter, not its shape).
+ *   x   BF16 [T, hidden];  qr BF16 [T, q_lora_rank]
+ *   wq_b BF16 [H*D, q_lora_rank];  wk, wg BF16 [D, hidden] (row = output)
+ *   k_norm_weight, k_norm_bias FP32 [D];  ww FP32 [H, hidden]
+ *   workspace  kpool_proj_workspace_bytes(pp) bytes, 256-byte aligned
+ *   q_out, k_out, gate_out  BF16 outputs;  w_out FP32 [T, H]
+ * Needs head_dim == 128, num_heads in {4, 8, 16, 32}, hidden and
+ * q_lora_rank multiples of 64. */
+typedef struct {
+  int32_t num_tokens;       /* T >= 0                                        */
+  int32_t hidden;           /* width of x                                    */
+  int32_t q_lora_rank;      /* width of qr                                   */
+  int32_t num_heads;        /* H                                             */
+  int32_t head_dim;         /* D (128)                                       */
+  float   eps;              /* LayerNorm epsilon; 0 = 1e-6                   */
+} kpool_proj_params;
+size_t kpool_proj_workspace_bytes(const kpool_proj_params* pp);
+kpool_status kpool_indexer_projections(const kpool_proj_params* pp, const void* x, const void* qr,
+                                       const void* wq_b, const void* wk,
+                                       const float* k_norm_weight, const float* k_norm_bias,
+                                       const void* wg, const float* ww, void* workspace,
+                                       size_t workspace_bytes, void* q_out, void* k_out,
+                                       void* gate_out, float* w_out, void* stream);
+
 /* ---- For callers that cannot allocate ----------------------------------
  * For code that must not call hipMalloc (work captured in a HIP graph, tight
  * serving loops, hosts that forbid allocation): kpool_decode_topk with its

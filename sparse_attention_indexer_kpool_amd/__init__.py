@@ -27,6 +27,32 @@ class KPoolError(RuntimeError):
         self.detail = detail
 
 
+class _ProjParams(ctypes.Structure):
+    _fields_ = [
+        ("num_tokens", ctypes.c_int32),
+        ("hidden", ctypes.c_int32),
+        ("q_lora_rank", ctypes.c_int32),
+        ("num_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("eps", ctypes.c_float),
+    ]
+
+
+@dataclass
+class ProjParams:
+    """Mirror of kpool_proj_params (include/kpool.h)."""
+    num_tokens: int
+    hidden: int
+    q_lora_rank: int
+    num_heads: int
+    head_dim: int = 128
+    eps: float = 0.0
+
+    def c(self) -> _ProjParams:
+        return _ProjParams(int(self.num_tokens), int(self.hidden), int(self.q_lora_rank),
+                           int(self.num_heads), int(self.head_dim), float(self.eps))
+
+
 class _Params(ctypes.Structure):
     _fields_ = [
         ("num_docs", ctypes.c_int32),
@@ -124,6 +150,12 @@ def lib() -> ctypes.CDLL:
         L.kpool_decode_noalloc_max_bytes.argtypes = []
         L.kpool_decode_topk_noalloc.restype = ctypes.c_int
         L.kpool_decode_topk_noalloc.argtypes = [P, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp]
+        PP = ctypes.POINTER(_ProjParams)
+        L.kpool_proj_workspace_bytes.restype = sz
+        L.kpool_proj_workspace_bytes.argtypes = [PP]
+        L.kpool_indexer_projections.restype = ctypes.c_int
+        L.kpool_indexer_projections.argtypes = [PP, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp,
+                                                vp, vp, vp, vp]
         L.kpool_status_string.restype = ctypes.c_char_p
         L.kpool_status_string.argtypes = [ctypes.c_int]
         L.kpool_last_error.restype = ctypes.c_char_p
@@ -140,6 +172,7 @@ EXPORTS = ["kpool_abi_version", "kpool_workspace_bytes", "kpool_logits_ld",
            "kpool_expand",
            "kpool_fp8_quantize", "kpool_compress_pools", "kpool_decode_workspace_bytes",
            "kpool_decode_topk", "kpool_decode_noalloc_max_bytes", "kpool_decode_topk_noalloc",
+           "kpool_proj_workspace_bytes", "kpool_indexer_projections",
            "kpool_status_string", "kpool_last_error"]
 
 
@@ -283,6 +316,19 @@ def kpool_decode_topk_noalloc(p: Params, q, w, pooled, pool_start, seq_lens, out
                                            _ptr(pool_start), _ptr(seq_lens), _ptr(token_base),
                                            _ptr(out_token_idx), _ptr(out_pool_idx),
                                            _stream(stream)))
+
+
+def kpool_proj_workspace_bytes(pp: ProjParams) -> int:
+    return int(lib().kpool_proj_workspace_bytes(ctypes.byref(pp.c())))
+
+
+def kpool_indexer_projections(pp: ProjParams, x, qr, wq_b, wk, k_norm_weight, k_norm_bias, wg,
+                              ww, workspace, q_out, k_out, gate_out, w_out, stream=None) -> None:
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().kpool_indexer_projections(
+        ctypes.byref(pp.c()), _ptr(x), _ptr(qr), _ptr(wq_b), _ptr(wk), _ptr(k_norm_weight),
+        _ptr(k_norm_bias), _ptr(wg), _ptr(ww), _ptr(workspace), ws_bytes, _ptr(q_out),
+        _ptr(k_out), _ptr(gate_out), _ptr(w_out), _stream(stream)))
 
 
 def kpool_status_string(status: int) -> str:

@@ -594,6 +594,68 @@ kpool_status kpool_decode_topk(const kpool_params* p, const void* q, const float
 
 size_t kpool_decode_noalloc_max_bytes(void) { return kScratchBytes; }
 
+size_t kpool_proj_workspace_bytes(const kpool_proj_params* pp) {
+  if (!pp || pp->hidden <= 0) return 0;
+  return round_up((size_t)128 * pp->hidden * 2, 256);
+}
+
+kpool_status kpool_indexer_projections(const kpool_proj_params* pp, const void* x, const void* qr,
+                                       const void* wq_b, const void* wk,
+                                       const float* k_norm_weight, const float* k_norm_bias,
+                                       const void* wg, const float* ww, void* workspace,
+                                       size_t workspace_bytes, void* q_out, void* k_out,
+                                       void* gate_out, float* w_out, void* stream) {
+  Range range("kpool_indexer_projections");
+  if (!pp) return fail(KPOOL_E_INVALID, "params is null");
+  const int T = pp->num_tokens, hidden = pp->hidden, qlr = pp->q_lora_rank, H = pp->num_heads;
+  if (T < 0) return fail(KPOOL_E_INVALID, "num_tokens must be >= 0 (got %d)", T);
+  if (pp->head_dim != 128)
+    return fail(KPOOL_E_UNSUPPORTED, "the projections need head_dim == 128 (got %d)", pp->head_dim);
+  if (H != 4 && H != 8 && H != 16 && H != 32)
+    return fail(KPOOL_E_UNSUPPORTED, "the projections take num_heads 4, 8, 16 or 32 (got %d)", H);
+  if (hidden <= 0 || hidden % 64 != 0 || qlr <= 0 || qlr % 64 != 0)
+    return fail(KPOOL_E_UNSUPPORTED, "hidden (%d) and q_lora_rank (%d) must be positive "
+                "multiples of 64", hidden, qlr);
+  if (!(pp->eps >= 0.f) || pp->eps > 1.f)
+    return fail(KPOOL_E_INVALID, "eps must be in [0, 1] (0 = 1e-6)");
+  if (T == 0) return ok();
+  CHECK(check_ptr(x, 16, "x"));
+  CHECK(check_ptr(qr, 16, "qr"));
+  CHECK(check_ptr(wq_b, 16, "wq_b"));
+  CHECK(check_ptr(wk, 16, "wk"));
+  CHECK(check_ptr(k_norm_weight, 4, "k_norm_weight"));
+  CHECK(check_ptr(k_norm_bias, 4, "k_norm_bias"));
+  CHECK(check_ptr(wg, 16, "wg"));
+  CHECK(check_ptr(ww, 4, "ww"));
+  CHECK(check_ptr(q_out, 16, "q_out"));
+  CHECK(check_ptr(k_out, 16, "k_out"));
+  CHECK(check_ptr(gate_out, 16, "gate_out"));
+  CHECK(check_ptr(w_out, 4, "w_out"));
+  const size_t need = kpool_proj_workspace_bytes(pp);
+  CHECK(check_ptr(workspace, 256, "workspace"));
+  if (workspace_bytes < need)
+    return fail(KPOOL_E_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+  kpool::ProjArgs a{};
+  a.x = reinterpret_cast<const uint16_t*>(x);
+  a.qr = reinterpret_cast<const uint16_t*>(qr);
+  a.wq_b = reinterpret_cast<const uint16_t*>(wq_b);
+  a.wk = reinterpret_cast<const uint16_t*>(wk);
+  a.ln_w = k_norm_weight;
+  a.ln_b = k_norm_bias;
+  a.wg = reinterpret_cast<const uint16_t*>(wg);
+  a.ww = ww;
+  a.w3 = reinterpret_cast<uint16_t*>(workspace);
+  a.T = T; a.hidden = hidden; a.q_lora = qlr; a.H = H;
+  a.eps = pp->eps > 0.f ? pp->eps : 1e-6f;
+  a.q = reinterpret_cast<uint16_t*>(q_out);
+  a.k = reinterpret_cast<uint16_t*>(k_out);
+  a.gate = reinterpret_cast<uint16_t*>(gate_out);
+  a.w = w_out;
+  (void)hipGetLastError();
+  kpool::launch_indexer_projections(a, reinterpret_cast<hipStream_t>(stream));
+  return after_launch();
+}
+
 kpool_status kpool_decode_topk_noalloc(const kpool_params* p, const void* q, const float* w,
                                        const void* pooled, int32_t pooled_rows,
                                        const float* pooled_scale, const int32_t* pool_start,

@@ -101,6 +101,28 @@ void launch_compress_pools(const uint16_t* k, const uint16_t* gate, const float*
                            int D, int kpool, const int32_t* dst_rows, int dst_cap,
                            uint16_t* pooled, float* row_scale, hipStream_t st);
 
+// The indexer projections (head_dim 128): q = qr wq_b^T, k = LayerNorm(x
+// wk^T), gate = x wg^T (BF16), w = x ww^T (FP32); w3 is device scratch of
+// 128 x hidden BF16 for the split of ww.
+struct ProjArgs {
+  const uint16_t* x;        // BF16 [T, hidden]
+  const uint16_t* qr;       // BF16 [T, q_lora]
+  const uint16_t* wq_b;     // BF16 [H*128, q_lora]
+  const uint16_t* wk;       // BF16 [128, hidden]
+  const float* ln_w;        // FP32 [128]
+  const float* ln_b;        // FP32 [128]
+  const uint16_t* wg;       // BF16 [128, hidden]
+  const float* ww;          // FP32 [H, hidden]
+  uint16_t* w3;             // scratch BF16 [128, hidden]
+  int T, hidden, q_lora, H;
+  float eps;
+  uint16_t* q;              // BF16 [T, H*128]
+  uint16_t* k;              // BF16 [T, 128]
+  uint16_t* gate;           // BF16 [T, 128]
+  float* w;                 // FP32 [T, H]
+};
+void launch_indexer_projections(const ProjArgs& p, hipStream_t st);
+
 // Largest max_pools the selection kernel handles (its LDS bitmap has one bit
 // per pool of a row).
 constexpr int kMaxSelectPools = 65536;

@@ -192,3 +192,39 @@ def strided_rows(T: int, n: int) -> list:
     if rows[-1] != T - 1:
         rows.append(T - 1)
     return rows
+
+
+@dataclass
+class ProjInputs:
+    """CPU tensors of the indexer projections for T tokens."""
+    x: torch.Tensor           # bf16 [T, hidden]
+    qr: torch.Tensor          # bf16 [T, q_lora]
+    wq_b: torch.Tensor        # bf16 [H*D, q_lora]
+    wk: torch.Tensor          # bf16 [D, hidden]
+    k_norm_weight: torch.Tensor  # f32 [D]
+    k_norm_bias: torch.Tensor    # f32 [D]
+    wg: torch.Tensor          # bf16 [D, hidden]
+    ww: torch.Tensor          # f32 [H, hidden]
+    H: int
+    D: int
+
+
+def make_proj_inputs(T: int, hidden: int, q_lora: int, H: int, D: int = 128,
+                     seed: int = 0) -> ProjInputs:
+    """Seeded projection inputs: activations ~ N(0, 1), weight rows ~
+    N(0, 1 / fan_in) (so the outputs are O(1)), k_norm weight 1 + 0.1 N(0, 1),
+    bias 0.1 N(0, 1). Draw order: x, qr, wq_b, wk, wg, k_norm weight, bias,
+    ww; BF16 tensors cast with round to nearest even."""
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn(T, hidden, generator=g)
+    qr = torch.randn(T, q_lora, generator=g)
+    wq_b = torch.randn(H * D, q_lora, generator=g) / math.sqrt(q_lora)
+    wk = torch.randn(D, hidden, generator=g) / math.sqrt(hidden)
+    wg = torch.randn(D, hidden, generator=g) / math.sqrt(hidden)
+    lw = 1.0 + 0.1 * torch.randn(D, generator=g)
+    lb = 0.1 * torch.randn(D, generator=g)
+    ww = torch.randn(H, hidden, generator=g) / math.sqrt(hidden)
+    bf = lambda t: t.to(torch.bfloat16).contiguous()
+    return ProjInputs(x=bf(x), qr=bf(qr), wq_b=bf(wq_b), wk=bf(wk),
+                      k_norm_weight=lw.float().contiguous(), k_norm_bias=lb.float().contiguous(),
+                      wg=bf(wg), ww=ww.float().contiguous(), H=H, D=D)
