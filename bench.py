@@ -274,6 +274,38 @@ def decode_bench(reps: int, B: int = 64, L: int = 65536, fp8: bool = False):
             "note": "keys read once, scores written and read once, token rows written"}
 
 
+def projections_bench(reps: int, T: int = 65536, hidden: int = 4096, q_lora: int = 1536,
+                      H: int = 32):
+    """kpool_indexer_projections at T tokens (stand-in sizes: the pages give
+    neither the hidden size nor the query latent width). Returns the JSON
+    object of its line."""
+    import sparse_attention_indexer_kpool_amd as kp
+    pi = wlm.make_proj_inputs(T, hidden, q_lora, H, seed=11)
+    dev = "cuda:0"
+    d = lambda t: t.to(dev).contiguous()
+    pp = kp.ProjParams(num_tokens=T, hidden=hidden, q_lora_rank=q_lora, num_heads=H, head_dim=128)
+    ws = torch.empty(kp.kpool_proj_workspace_bytes(pp), dtype=torch.uint8, device=dev)
+    q = torch.empty(T, H * 128, dtype=torch.bfloat16, device=dev)
+    k = torch.empty(T, 128, dtype=torch.bfloat16, device=dev)
+    g = torch.empty_like(k)
+    w = torch.empty(T, H, dtype=torch.float32, device=dev)
+    args = [d(pi.x), d(pi.qr), d(pi.wq_b), d(pi.wk), d(pi.k_norm_weight), d(pi.k_norm_bias),
+            d(pi.wg), d(pi.ww)]
+    run = lambda: kp.kpool_indexer_projections(pp, *args, ws, q, k, g, w)
+    ms = time_region(run, reps, warm=2)
+    # algorithmic MFMA work: q, k and the gate, and the head weights as three
+    # BF16 products (FP32 weights split exactly into three BF16 parts)
+    flops = 2.0 * T * (q_lora * H * 128 + hidden * (128 + 128 + 3 * H))
+    del pi, args, q, k, g, w, ws
+    torch.cuda.empty_cache()
+    return {"entry": "kpool_indexer_projections",
+            "workload": f"proj_T{T}_hidden{hidden}_qlora{q_lora}_H{H}_D128", "ms": round(ms, 4),
+            "roofline": {"bound": "mfma", "achieved": round(flops / (ms * 1e-3) / 1e12, 2),
+                         "peak": round(PEAK_BF16_TFLOPS, 1), "unit": "TFLOP/s",
+                         "frac": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
+            "note": "hidden and q_lora_rank are stand-in sizes"}
+
+
 def measure_workload(wl, steps: int, warmup: int):
     """One workload: the whole step timed over `steps` steps after `warmup`
     untimed ones, then each phase alone with the same launches. Returns
@@ -427,6 +459,8 @@ def main():
         out["decode"] = decode_bench(reps)
         out["decode_fp8"] = decode_bench(reps, fp8=True)
     if not args.no_others and wl.name == "long_T65536_H32_D128":
+        log("indexer projections")
+        out["projections"] = projections_bench(max(3, min(args.steps, 10)))
         # the FP8 input path and the short workloads, each timed the same way
         for key, other in (("fp8", "fp8_T32768_H32_D128"), ("tiny", "tiny_T256_H4_D64"),
                            ("single_4k", "single_T4096_H32_D128"),

@@ -96,6 +96,7 @@ struct GemmBlock {                 // one 128-column block of the output
 struct GemmArgs {
   const uint16_t* a;               // BF16 [M, K]
   int M, K;
+  int nblk;                        // column blocks (N / 128)
   GemmBlock blk[32];               // blockIdx.y -> block (N / 128 of them)
   const float* ln_w;               // LayerNorm weight, bias [128] (EPI_LAYERNORM)
   const float* ln_b;
@@ -112,8 +113,17 @@ __global__ __launch_bounds__(kGemmThreads) void proj_gemm_kernel(GemmArgs g) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wm = wid >> 1, wn = wid & 1;
   const int n = lane & 31, hg = lane >> 5;
-  const GemmBlock blk = g.blk[blockIdx.y];
-  const int row0 = (int)blockIdx.x * kBM;
+  // block -> (row block, column block): groups of kGroupM row blocks take
+  // every column block before the next group starts, and workgroups are
+  // dealt to the 8 XCDs in turn, so an XCD's L2 holds its group's rows of A
+  // and a quarter of the column blocks of B while they are used
+  constexpr int kGroupM = 8;
+  const int per_group = kGroupM * g.nblk;
+  const int grp = (int)blockIdx.x / per_group, within = (int)blockIdx.x % per_group;
+  const int mb = grp * kGroupM + within / g.nblk, nb = within % g.nblk;
+  const int row0 = mb * kBM;
+  if (row0 >= g.M) return;                 // padding of the last group (uniform)
+  const GemmBlock blk = g.blk[nb];
   const int KT = g.K / kBK;
 
   // fragment offsets (the same swizzle for A and B): row n of a 32-row
@@ -278,6 +288,12 @@ __global__ void split3_kernel(const float* __restrict__ w, int H, int K, uint16_
   }
 }
 
+// workgroups for M rows and nblk column blocks, whole groups of 8 row blocks
+static int gemm_grid(int M, int nblk) {
+  const int mblk = (M + kBM - 1) / kBM;
+  return (mblk + 7) / 8 * 8 * nblk;
+}
+
 void launch_indexer_projections(const ProjArgs& p, hipStream_t st) {
   // x-side: k (LayerNorm), gate, the FP32 head weights
   {
@@ -293,8 +309,8 @@ void launch_indexer_projections(const ProjArgs& p, hipStream_t st) {
     g.blk[0] = GemmBlock{p.wk, 128, EPI_LAYERNORM, p.k, 128, 0};
     g.blk[1] = GemmBlock{p.wg, 128, EPI_STORE_BF16, p.gate, 128, 0};
     g.blk[2] = GemmBlock{p.w3, 128, EPI_SUM3_F32, p.w, p.H, 0};
-    const dim3 grid((p.T + kBM - 1) / kBM, 3);
-    proj_gemm_kernel<<<grid, kGemmThreads, 0, st>>>(g);
+    g.nblk = 3;
+    proj_gemm_kernel<<<gemm_grid(p.T, g.nblk), kGemmThreads, 0, st>>>(g);
   }
   // q: the query latent times wq_b, H*D columns in blocks of 128
   {
@@ -309,8 +325,8 @@ void launch_indexer_projections(const ProjArgs& p, hipStream_t st) {
         const int c0 = n0 + b * kBN;
         g.blk[b] = GemmBlock{p.wq_b + (size_t)c0 * p.q_lora, 128, EPI_STORE_BF16, p.q, N, c0};
       }
-      const dim3 grid((p.T + kBM - 1) / kBM, nb);
-      proj_gemm_kernel<<<grid, kGemmThreads, 0, st>>>(g);
+      g.nblk = nb;
+      proj_gemm_kernel<<<gemm_grid(p.T, nb), kGemmThreads, 0, st>>>(g);
     }
   }
 }
