@@ -22,4 +22,5 @@ from .kpool_oracle import (  # noqa: F401
     pow2_row_exponent,
     row_scores,
     select_pools,
+    sparse_mla_forward,
 )

@@ -2,9 +2,10 @@
 
 Only tests/, `__graft_entry__.smoke()` and the CPU-baseline leg of bench.py may
 use this module. It shares no code with the HIP library: no kernels, headers,
-helpers, tables or constants. Everything is NumPy in FP32 (the pages fix FP32
-accumulation for the pooling), evaluated in the order the pages describe, with
-no blocking or fusion. BF16 and E4M3 rounding are written out from their
+helpers, tables or constants. The indexer is NumPy in FP32 (the pages fix FP32
+accumulation for the pooling); the sparse attention that consumes its indices
+is NumPy in FP64. Both are evaluated in the order the pages describe, with no
+blocking or fusion. BF16 and E4M3 rounding are written out from their
 definitions.
 
 Sources (three web pages; cited by title and section):
@@ -36,6 +37,11 @@ notes of the repository):
     to BF16; row exponent e = min{e : amax <= 448 * 2^e} (0 for an all-zero
     row); codes = OCP E4M3 (e4m3fn, max 448, subnormals kept) of y * 2^-e,
     round to nearest even. The keys are quantised after pooling.
+  * Sparse attention (the consumer): one latent row per token shared by all
+    heads serves as key (all d_qk components) and value (the first d_v); the
+    score is sm_scale * <q, row> with sm_scale an input; an entry outside
+    [0, N) is unused, every other entry is one softmax term; lse is the
+    natural logarithm; a query with no used entry gets o = 0, lse = -inf.
 """
 from __future__ import annotations
 
@@ -422,3 +428,46 @@ def indexer_projections(x, qr, wq_b, wk, k_norm_weight, k_norm_bias, wg, ww,
     gate = linear_bf16(x, wg)
     w = (np.asarray(x, dtype=F32) @ np.asarray(ww, dtype=F32).T).astype(F32)
     return q, k, gate, w
+
+
+# ---------------------------------------------------------------------------
+# The consumer of the indices: sparse attention of the NoPE absorbed MLA.
+# [XT] Summary: a new sparse MLA backend runs FlashMLA's forward over the
+# indexer's int32 token indices; its heads must come in multiples of 64, and
+# its (head_dim, value_dim) pair is no longer fixed at 576. [MLM] section 3:
+# with NoPE the absorbed query has no positional slice. [XT] LSE fix commit:
+# the saved softmax LSE is the natural logarithm.
+# Readings: in the absorbed form every head attends to one shared latent row
+# per token; with no positional slice that row is both the key (all d_qk
+# components) and the value (its first d_v components). The score is
+# sm_scale * <q, row>; sm_scale is an input, since the pages give no value.
+# A listed entry outside [0, N) -- the indexer's -1 padding -- is unused;
+# every other entry is one term of the softmax (a row listed twice counts
+# twice). A query with no used entry gets o = 0 and lse = -inf.
+# Evaluated in FP64 from the BF16 inputs.
+# ---------------------------------------------------------------------------
+
+def sparse_mla_forward(q, kv, indices, sm_scale: float, d_v: int | None = None):
+    """q [T, H, d_qk], kv [N, d_qk], indices [T, W] integers.
+    Returns o [T, H, d_v] and lse [T, H] (natural log), both FP64."""
+    q = np.asarray(q, dtype=np.float64)
+    kv = np.asarray(kv, dtype=np.float64)
+    indices = np.asarray(indices)
+    T, H, d_qk = q.shape
+    N = kv.shape[0]
+    if d_v is None:
+        d_v = d_qk
+    o = np.zeros((T, H, d_v))
+    lse = np.full((T, H), -np.inf)
+    for t in range(T):
+        sel = [int(j) for j in indices[t] if 0 <= int(j) < N]
+        if not sel:
+            continue
+        rows = kv[sel]                              # [n, d_qk]
+        s = sm_scale * (q[t] @ rows.T)              # [H, n]
+        m = s.max(axis=1)
+        e = np.exp(s - m[:, None])
+        l = e.sum(axis=1)
+        o[t] = (e @ rows[:, :d_v]) / l[:, None]
+        lse[t] = m + np.log(l)
+    return o, lse

@@ -12,7 +12,8 @@ The pages (cited by title and section):
   SkyRL PR #2179, k-pool commit (below the budget every pool is selectable)
     and "Limitations / follow-ups" (score, expand, append the tail).
   xtuner PR #2108 F5 commit message (ReLU homogeneity lets head_dim^-1/2 move
-    from the ReLU argument into the head weight).
+    from the ReLU argument into the head weight), Summary (the sparse MLA
+    forward over the indices) and the LSE fix commit (natural-log LSE).
 """
 from __future__ import annotations
 
@@ -738,6 +739,129 @@ def pin_head_weights_fp32(o):
     bound = 2 * x.shape[1] * 2.0 ** -24 * (np.abs(x).astype(np.float64) @ np.abs(ww).T)
     assert np.all(np.abs(w - ref) <= bound)
     assert np.mean(o.bf16_round(w) != w) > 0.9
+
+
+# ---------------------------------------------------------------------------
+# Sparse attention of the NoPE absorbed MLA over the selected token rows
+# (xtuner PR #2108, Summary: the FlashMLA forward consumes the int32 indices;
+# the LSE fix commit: the saved LSE is the natural logarithm).
+# ---------------------------------------------------------------------------
+
+def _mla_case(seed, T=7, H=4, N=23, d=16, W=9):
+    r = np.random.default_rng(seed)
+    q = r.standard_normal((T, H, d))
+    kv = r.standard_normal((N, d))
+    idx = r.integers(0, N, size=(T, W))
+    idx[r.random((T, W)) < 0.25] = -1
+    return q, kv, idx
+
+
+def _sdpa_rows(q_t, rows, sm_scale, d_v):
+    """torch's scaled_dot_product_attention (FP64, CPU) of one query's heads
+    over the given key/value rows; a library routine, not the oracle."""
+    qt = torch.from_numpy(np.ascontiguousarray(q_t))[None, :, None, :]          # [1, H, 1, d]
+    k = torch.from_numpy(np.ascontiguousarray(rows))[None, None].expand(1, q_t.shape[0], -1, -1)
+    v = torch.from_numpy(np.ascontiguousarray(rows[:, :d_v]))[None, None].expand(1, q_t.shape[0], -1, -1)
+    out = torch.nn.functional.scaled_dot_product_attention(qt, k, v, scale=sm_scale)
+    return out[0, :, 0, :].numpy()
+
+
+def pin_mla_matches_sdpa(o):
+    """Each query equals torch's attention over the rows its valid entries
+    list (repeats included), for d_v = d_qk and for d_v < d_qk (the value is
+    the leading part of the latent row)."""
+    for d_v in (16, 10):
+        q, kv, idx = _mla_case(1)
+        idx[2, :3] = idx[2, 3]                 # a row listed several times
+        got, _ = o.sparse_mla_forward(q, kv, idx, 0.37, d_v=d_v)
+        for t in range(q.shape[0]):
+            sel = [int(j) for j in idx[t] if 0 <= j < kv.shape[0]]
+            ref = _sdpa_rows(q[t], kv[sel], 0.37, d_v) if sel else np.zeros((q.shape[1], d_v))
+            assert np.allclose(got[t], ref, rtol=1e-12, atol=1e-12)
+
+
+def pin_mla_causal_dense(o):
+    """Listing tokens 0..t (then -1 padding) for query t is causal attention
+    over the whole sequence: torch's is_causal path, FP64."""
+    T, H, d = 11, 3, 8
+    r = np.random.default_rng(2)
+    q = r.standard_normal((T, H, d))
+    kv = r.standard_normal((T, d))
+    idx = np.full((T, T), -1)
+    for t in range(T):
+        idx[t, :t + 1] = np.arange(t + 1)
+    got, _ = o.sparse_mla_forward(q, kv, idx, 0.5)
+    qt = torch.from_numpy(q).permute(1, 0, 2)[None]                      # [1, H, T, d]
+    k = torch.from_numpy(kv)[None, None].expand(1, H, T, d)
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, k, k, is_causal=True, scale=0.5)
+    assert np.allclose(got, ref[0].permute(1, 0, 2).numpy(), rtol=1e-12, atol=1e-12)
+
+
+def pin_mla_closed_forms(o):
+    """One valid entry: o is that row, lse its score. q = 0: o is the mean of
+    the listed rows (a repeat counts twice) and lse = ln n. No valid entry
+    (-1 and out-of-range ids): o = 0, lse = -inf."""
+    r = np.random.default_rng(3)
+    N, H, d = 6, 2, 5
+    kv = r.standard_normal((N, d))
+    q = r.standard_normal((4, H, d))
+    q[1] = 0.0
+    q[3] = 0.0
+    idx = np.array([[-1, 4, -1, 17],        # one valid entry (17 >= N is unused)
+                    [0, 2, 2, 5],            # q = 0: weights 1, 2, 1 over rows 0, 2, 5
+                    [-1, -1, -1, N],         # nothing valid
+                    [3, 3, 3, 3]])           # q = 0, one row four times
+    out, lse = o.sparse_mla_forward(q, kv, idx, 0.8)
+    assert np.allclose(out[0], np.broadcast_to(kv[4], (H, d)), rtol=1e-14, atol=1e-14)
+    assert np.allclose(lse[0], 0.8 * (q[0] @ kv[4]), rtol=1e-14, atol=1e-14)
+    assert np.allclose(out[1], np.broadcast_to((kv[0] + 2 * kv[2] + kv[5]) / 4, (H, d)), atol=1e-14)
+    assert np.allclose(lse[1], math.log(4.0), atol=1e-14)
+    assert np.all(out[2] == 0.0) and np.all(np.isneginf(lse[2]))
+    assert np.allclose(out[3], np.broadcast_to(kv[3], (H, d)), atol=1e-14)
+    assert np.allclose(lse[3], math.log(4.0), atol=1e-14)
+
+
+def pin_mla_lse_natural_log(o):
+    """Two listed rows with scores a and b: lse = ln(e^a + e^b) (natural log,
+    not log2), and o = sum_j exp(s_j - lse) v_j."""
+    kv = np.array([[1.0, 0.0, 2.0], [0.0, 1.0, -1.0]])
+    q = np.array([[[0.7, -0.3, 0.2]]])
+    a, b = 0.9 * (0.7 + 0.4), 0.9 * (-0.3 - 0.2)
+    out, lse = o.sparse_mla_forward(q, kv, np.array([[1, 0]]), 0.9)
+    assert abs(lse[0, 0] - math.log(math.exp(a) + math.exp(b))) < 1e-14
+    ref = math.exp(a - lse[0, 0]) * kv[0] + math.exp(b - lse[0, 0]) * kv[1]
+    assert np.allclose(out[0, 0], ref, atol=1e-14)
+
+
+def pin_mla_order_invariance(o):
+    """Shuffling a query's entries, or moving its -1 padding, changes
+    nothing beyond rounding (the softmax is a sum over the listed rows)."""
+    q, kv, idx = _mla_case(4, W=12)
+    ref_o, ref_l = o.sparse_mla_forward(q, kv, idx, 0.25)
+    r = np.random.default_rng(5)
+    shuf = np.stack([r.permutation(row) for row in idx])
+    got_o, got_l = o.sparse_mla_forward(q, kv, shuf, 0.25)
+    assert np.allclose(got_o, ref_o, rtol=1e-12, atol=1e-12)
+    assert np.allclose(got_l, ref_l, rtol=1e-12, atol=1e-12)
+
+
+def pin_mla_brute_loops(o):
+    """Scalar loops with math.exp on a tiny case (no arrays, no library
+    attention)."""
+    q, kv, idx = _mla_case(6, T=3, H=2, N=5, d=3, W=4)
+    out, lse = o.sparse_mla_forward(q, kv, idx, 1.3)
+    for t in range(3):
+        sel = [int(j) for j in idx[t] if 0 <= j < 5]
+        for h in range(2):
+            if not sel:
+                assert lse[t, h] == -math.inf and all(out[t, h] == 0.0)
+                continue
+            s = [1.3 * sum(q[t, h, c] * kv[j, c] for c in range(3)) for j in sel]
+            z = sum(math.exp(x) for x in s)
+            assert abs(lse[t, h] - math.log(z)) < 1e-12
+            for c in range(3):
+                v = sum(math.exp(x) * kv[j, c] for x, j in zip(s, sel)) / z
+                assert abs(out[t, h, c] - v) < 1e-12
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -66,6 +66,19 @@ MUTATIONS = {
     "q_heads_transposed": ("q = linear_bf16(qr, wq_b).reshape(T, num_heads, head_dim)",
                            "q = linear_bf16(qr, wq_b).reshape(T, head_dim, num_heads).transpose(0, 2, 1)"),
     "gate_from_wk": ("gate = linear_bf16(x, wg)", "gate = linear_bf16(x, wk)"),
+    "mla_scale_dropped": ("s = sm_scale * (q[t] @ rows.T)", "s = (q[t] @ rows.T)"),
+    "mla_lse_log2": ("lse[t] = m + np.log(l)", "lse[t] = (m + np.log(l)) * np.log2(np.e)"),
+    "mla_minus_one_wraps": ("if 0 <= int(j) < N]", "if int(j) < N]"),
+    "mla_out_of_range_kept": ("if 0 <= int(j) < N]", "if 0 <= int(j)] if False else "
+                              "[min(int(j), N - 1) for j in indices[t] if 0 <= int(j)]"),
+    "mla_repeats_merged": ("sel = [int(j) for j in indices[t] if 0 <= int(j) < N]",
+                           "sel = sorted(set(int(j) for j in indices[t] if 0 <= int(j) < N))"),
+    "mla_normalised_over_heads": ("o[t] = (e @ rows[:, :d_v]) / l[:, None]",
+                                  "o[t] = (e @ rows[:, :d_v]) / l.sum()"),
+    "mla_values_from_tail": ("o[t] = (e @ rows[:, :d_v])", "o[t] = (e @ rows[:, d_qk - d_v:])"),
+    "mla_no_max_in_lse": ("lse[t] = m + np.log(l)", "lse[t] = np.log(l)"),
+    "mla_empty_lse_zero": ("lse = np.full((T, H), -np.inf)", "lse = np.zeros((T, H))"),
+    "mla_head_order": ("s = sm_scale * (q[t] @ rows.T)", "s = sm_scale * (q[t][::-1] @ rows.T)"),
 }
 
 

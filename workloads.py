@@ -228,3 +228,40 @@ def make_proj_inputs(T: int, hidden: int, q_lora: int, H: int, D: int = 128,
     return ProjInputs(x=bf(x), qr=bf(qr), wq_b=bf(wq_b), wk=bf(wk),
                       k_norm_weight=lw.float().contiguous(), k_norm_bias=lb.float().contiguous(),
                       wg=bf(wg), ww=ww.float().contiguous(), H=H, D=D)
+
+
+@dataclass
+class MlaInputs:
+    """CPU tensors of one sparse-attention call over listed token rows."""
+    q: torch.Tensor           # bf16 [T, H, d]
+    kv: torch.Tensor          # bf16 [N, d] (one latent row per token)
+    indices: torch.Tensor     # int32 [T, width]; -1 and ids >= N are unused entries
+
+
+def make_mla_inputs(T: int, H: int, N: int, width: int, d: int = 512, seed: int = 0,
+                    causal: bool = True, unused_frac: float = 0.1, out_of_range_frac: float = 0.0,
+                    pad_rows_frac: float = 0.25, q_scale: float = 1.0) -> MlaInputs:
+    """Seeded inputs: q ~ q_scale * N(0, 1), kv ~ N(0, 1), both cast to BF16
+    (round to nearest even). Row t lists `width` ids drawn uniformly with
+    replacement from [0, min(N, t + 1)) (causal) or [0, N), so repeats occur;
+    then a fraction `unused_frac` of the entries become -1, a fraction
+    `out_of_range_frac` become ids in [N, 2N), and a fraction `pad_rows_frac`
+    of the rows keep only a random-length prefix (the rest -1, the way an
+    indexer pads its rows). Draw order: q, kv, ids, unused mask, out-of-range
+    mask and ids, padded-row mask, prefix lengths."""
+    g = torch.Generator().manual_seed(seed)
+    q = q_scale * torch.randn(T, H, d, generator=g)
+    kv = torch.randn(N, d, generator=g)
+    hi = torch.clamp(torch.arange(T) + 1, max=N) if causal else torch.full((T,), N)
+    ids = (torch.rand(T, width, generator=g) * hi[:, None]).floor().to(torch.int64)
+    unused = torch.rand(T, width, generator=g) < unused_frac
+    oor = torch.rand(T, width, generator=g) < out_of_range_frac
+    oor_ids = N + (torch.rand(T, width, generator=g) * N).floor().to(torch.int64)
+    ids = torch.where(oor, oor_ids, ids)
+    ids[unused] = -1
+    padded = torch.rand(T, generator=g) < pad_rows_frac
+    keep = (torch.rand(T, generator=g) * (width + 1)).floor().to(torch.int64)
+    col = torch.arange(width)[None, :]
+    ids[padded[:, None] & (col >= keep[:, None])] = -1
+    return MlaInputs(q=q.to(torch.bfloat16).contiguous(), kv=kv.to(torch.bfloat16).contiguous(),
+                     indices=ids.to(torch.int32).contiguous())
