@@ -326,6 +326,43 @@ kpool_status kpool_indexer_projections(const kpool_proj_params* pp, const void* 
                                        size_t workspace_bytes, void* q_out, void* k_out,
                                        void* gate_out, float* w_out, void* stream);
 
+/* ---- Sparse attention over the selected rows (the indices' consumer) ----
+ * ([XT] "Summary": the sparse MLA backend runs FlashMLA's forward over the
+ * indexer's int32 indices, with heads in multiples of 64; [XT] LSE fix
+ * commit: the saved LSE is the natural logarithm; [MLM] section 3: NoPE, the
+ * absorbed query has no positional slice.) For query token t and head h:
+ *   s_j      = sm_scale * <q[t, h, :], kv[j, :]>   for each listed row j
+ *   out[t,h] = sum_j softmax(s)_j * kv[j, :]        BF16 (round to nearest even)
+ *   lse[t,h] = ln sum_j exp(s_j)                    FP32
+ * kv holds one latent row per token, shared by every head, which is both
+ * the key and the value (dim_qk = dim_v = 512). An entry of indices outside
+ * [0, kv_rows) -- such as the indexer's -1 padding -- is unused; any other
+ * entry is one softmax term (a row listed twice counts twice). A query with
+ * no used entry gets out = 0 and lse = -inf. Scores and sums in FP32 from
+ * BF16 products; the softmax weights are rounded to BF16 for the weighted
+ * sum of the rows.
+ *   q        BF16 [num_tokens, num_heads, 512], 16-byte aligned
+ *   kv       BF16 [kv_rows, 512], 16-byte aligned
+ *   indices  int32 [num_tokens, width] (e.g. kpool_indexer_topk's
+ *            out_token_idx with width = index_topk + kpool), 4-byte aligned
+ *   out      BF16 [num_tokens, num_heads, 512], 16-byte aligned
+ *   lse      FP32 [num_tokens, num_heads], 4-byte aligned
+ * Device pointers, owned by the caller; nothing is allocated. Needs
+ * num_heads a positive multiple of 64 and dim_qk = dim_v = 512, else
+ * KPOOL_E_UNSUPPORTED; negative sizes or a non-finite sm_scale give
+ * KPOOL_E_INVALID. Nothing is enqueued on an error. */
+typedef struct {
+  int32_t num_tokens;       /* T >= 0                                        */
+  int32_t num_heads;        /* H, a positive multiple of 64                  */
+  int32_t kv_rows;          /* N >= 0 rows in kv                             */
+  int32_t width;            /* W >= 0 entries per query in indices           */
+  int32_t dim_qk;           /* 512                                           */
+  int32_t dim_v;            /* 512                                           */
+  float   sm_scale;         /* score scale (finite)                          */
+} kpool_mla_params;
+kpool_status kpool_sparse_mla_fwd(const kpool_mla_params* mp, const void* q, const void* kv,
+                                  const int32_t* indices, void* out, float* lse, void* stream);
+
 /* ---- For callers that cannot allocate ----------------------------------
  * For code that must not call hipMalloc (work captured in a HIP graph, tight
  * serving loops, hosts that forbid allocation): kpool_decode_topk with its

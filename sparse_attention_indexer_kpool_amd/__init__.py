@@ -53,6 +53,34 @@ class ProjParams:
                            int(self.num_heads), int(self.head_dim), float(self.eps))
 
 
+class _MlaParams(ctypes.Structure):
+    _fields_ = [
+        ("num_tokens", ctypes.c_int32),
+        ("num_heads", ctypes.c_int32),
+        ("kv_rows", ctypes.c_int32),
+        ("width", ctypes.c_int32),
+        ("dim_qk", ctypes.c_int32),
+        ("dim_v", ctypes.c_int32),
+        ("sm_scale", ctypes.c_float),
+    ]
+
+
+@dataclass
+class MlaParams:
+    """Mirror of kpool_mla_params (include/kpool.h)."""
+    num_tokens: int
+    num_heads: int
+    kv_rows: int
+    width: int
+    sm_scale: float
+    dim_qk: int = 512
+    dim_v: int = 512
+
+    def c(self) -> _MlaParams:
+        return _MlaParams(int(self.num_tokens), int(self.num_heads), int(self.kv_rows),
+                          int(self.width), int(self.dim_qk), int(self.dim_v), float(self.sm_scale))
+
+
 class _Params(ctypes.Structure):
     _fields_ = [
         ("num_docs", ctypes.c_int32),
@@ -156,6 +184,9 @@ def lib() -> ctypes.CDLL:
         L.kpool_indexer_projections.restype = ctypes.c_int
         L.kpool_indexer_projections.argtypes = [PP, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp,
                                                 vp, vp, vp, vp]
+        MP = ctypes.POINTER(_MlaParams)
+        L.kpool_sparse_mla_fwd.restype = ctypes.c_int
+        L.kpool_sparse_mla_fwd.argtypes = [MP, vp, vp, vp, vp, vp, vp]
         L.kpool_status_string.restype = ctypes.c_char_p
         L.kpool_status_string.argtypes = [ctypes.c_int]
         L.kpool_last_error.restype = ctypes.c_char_p
@@ -172,7 +203,7 @@ EXPORTS = ["kpool_abi_version", "kpool_workspace_bytes", "kpool_logits_ld",
            "kpool_expand",
            "kpool_fp8_quantize", "kpool_compress_pools", "kpool_decode_workspace_bytes",
            "kpool_decode_topk", "kpool_decode_noalloc_max_bytes", "kpool_decode_topk_noalloc",
-           "kpool_proj_workspace_bytes", "kpool_indexer_projections",
+           "kpool_proj_workspace_bytes", "kpool_indexer_projections", "kpool_sparse_mla_fwd",
            "kpool_status_string", "kpool_last_error"]
 
 
@@ -329,6 +360,11 @@ def kpool_indexer_projections(pp: ProjParams, x, qr, wq_b, wk, k_norm_weight, k_
         ctypes.byref(pp.c()), _ptr(x), _ptr(qr), _ptr(wq_b), _ptr(wk), _ptr(k_norm_weight),
         _ptr(k_norm_bias), _ptr(wg), _ptr(ww), _ptr(workspace), ws_bytes, _ptr(q_out),
         _ptr(k_out), _ptr(gate_out), _ptr(w_out), _stream(stream)))
+
+
+def kpool_sparse_mla_fwd(mp: MlaParams, q, kv, indices, out, lse, stream=None) -> None:
+    _check(lib().kpool_sparse_mla_fwd(ctypes.byref(mp.c()), _ptr(q), _ptr(kv), _ptr(indices),
+                                      _ptr(out), _ptr(lse), _stream(stream)))
 
 
 def kpool_status_string(status: int) -> str:

@@ -16,7 +16,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libkpool.so")
 
 SOURCES = ["api.cpp", "compress.hip", "decode.hip", "expand.hip", "fp8_quant.hip", "logits.hip",
-           "proj.hip", "select.hip"]
+           "mla.hip", "proj.hip", "select.hip"]
 
 ARCH = "gfx950"
 FLAGS = [

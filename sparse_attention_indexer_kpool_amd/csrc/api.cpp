@@ -7,6 +7,7 @@
 #include <algorithm>
 #include <cstdarg>
 #include <cstdio>
+#include <cmath>
 #include <cstring>
 #include <mutex>
 #include <string>
@@ -653,6 +654,42 @@ kpool_status kpool_indexer_projections(const kpool_proj_params* pp, const void* 
   a.w = w_out;
   (void)hipGetLastError();
   kpool::launch_indexer_projections(a, reinterpret_cast<hipStream_t>(stream));
+  return after_launch();
+}
+
+kpool_status kpool_sparse_mla_fwd(const kpool_mla_params* mp, const void* q, const void* kv,
+                                  const int32_t* indices, void* out, float* lse, void* stream) {
+  Range range("kpool_sparse_mla_fwd");
+  if (!mp) return fail(KPOOL_E_INVALID, "params is null");
+  const int T = mp->num_tokens, H = mp->num_heads, N = mp->kv_rows, W = mp->width;
+  if (T < 0 || N < 0 || W < 0)
+    return fail(KPOOL_E_INVALID, "num_tokens (%d), kv_rows (%d) and width (%d) must be >= 0", T,
+                N, W);
+  if (H <= 0 || H % 64 != 0)
+    return fail(KPOOL_E_UNSUPPORTED, "num_heads must be a positive multiple of 64 (got %d)", H);
+  if (mp->dim_qk != 512 || mp->dim_v != 512)
+    return fail(KPOOL_E_UNSUPPORTED, "dim_qk and dim_v must be 512 (got %d, %d)", mp->dim_qk,
+                mp->dim_v);
+  if (!std::isfinite(mp->sm_scale)) return fail(KPOOL_E_INVALID, "sm_scale must be finite");
+  if ((int64_t)T * (H / 64) > (1ll << 31) - 8)
+    return fail(KPOOL_E_UNSUPPORTED, "num_tokens * num_heads / 64 is too large for one launch");
+  if (T == 0) return ok();
+  CHECK(check_ptr(q, 16, "q"));
+  CHECK(check_ptr(out, 16, "out"));
+  CHECK(check_ptr(lse, 4, "lse"));
+  if (N > 0) CHECK(check_ptr(kv, 16, "kv"));
+  if (W > 0) CHECK(check_ptr(indices, 4, "indices"));
+  kpool::MlaArgs a{};
+  a.q = reinterpret_cast<const uint16_t*>(q);
+  a.kv = reinterpret_cast<const uint16_t*>(kv);
+  a.idx = indices;
+  a.out = reinterpret_cast<uint16_t*>(out);
+  a.lse = lse;
+  a.T = T; a.H = H; a.N = N; a.W = W;
+  a.scale2 = (float)((double)mp->sm_scale * 1.4426950408889634);
+  (void)hipGetLastError();
+  hipError_t e = kpool::launch_sparse_mla(a, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(KPOOL_E_LAUNCH, "HIP launch error: %s", hipGetErrorString(e));
   return after_launch();
 }
 

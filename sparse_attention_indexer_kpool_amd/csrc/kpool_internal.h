@@ -123,6 +123,19 @@ struct ProjArgs {
 };
 void launch_indexer_projections(const ProjArgs& p, hipStream_t st);
 
+// Sparse attention of the NoPE absorbed MLA (latent width 512, key = value).
+struct MlaArgs {
+  const uint16_t* q;        // BF16 [T, H, 512]
+  const uint16_t* kv;       // BF16 [N, 512]
+  const int32_t* idx;       // int32 [T, W]
+  uint16_t* out;            // BF16 [T, H, 512]
+  float* lse;               // FP32 [T, H]
+  int T, H, N, W;
+  float scale2;             // sm_scale * log2(e)
+};
+int mla_lds_bytes();
+hipError_t launch_sparse_mla(const MlaArgs& m, hipStream_t st);
+
 // Largest max_pools the selection kernel handles (its LDS bitmap has one bit
 // per pool of a row).
 constexpr int kMaxSelectPools = 65536;

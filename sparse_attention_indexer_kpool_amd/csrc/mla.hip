@@ -1,0 +1,329 @@
+// Sparse attention of the NoPE absorbed MLA over the indexer's token rows:
+// for query token t and head h,
+//   s_j    = sm_scale * <q[t, h, :], kv[j, :]>          j over the listed rows
+//   o[t,h] = sum_j softmax(s)_j kv[j, :d_v]              (BF16 out)
+//   lse    = ln sum_j exp(s_j)                           (FP32 out)
+// xtuner PR #2108, "Summary" (the sparse MLA backend runs FlashMLA's forward
+// over the int32 indices, heads in multiples of 64, the head/value widths no
+// longer fixed at 576) and the LSE fix commit (natural-log LSE); Megatron-LM
+// PR #7054, section "3. KPool DSA indexer + NoPE" (NoPE: the absorbed query
+// has no positional slice, so the latent row is both key and value).
+// Entries outside [0, kv_rows) -- the indexer's -1 padding -- are unused; a
+// row listed twice counts twice; a query with no used entry gets o = 0 and
+// lse = -inf.
+//
+// One workgroup per (token, group of 64 heads), four waves. Wave w owns heads
+// 32*(w & 1) .. +31 of the group and latent dims 256*(w >> 1) .. +255:
+//   * The listed rows come in blocks of 32. Each block is copied straight
+//     from HBM/L2 into LDS (global_load_lds_dwordx4, one 1 KB row per wave
+//     instruction, double buffered) as a row-major [32][512] BF16 tile whose
+//     16-byte chunks are XOR-swizzled per row.
+//   * Scores: S^T (32 rows x 32 heads) = K . Q^T over the wave's 256 dims
+//     (v_mfma_f32_32x32x16_bf16, K from LDS, Q^T held in registers); the
+//     partner wave (other dim half, same heads) adds its half through LDS.
+//   * Online softmax in base 2 per head (a head is one MFMA column, so its
+//     running max, sum and rescale live in one lane pair).
+//   * O^T (256 dims x 32 heads) += V^T . P^T: V^T comes from the same
+//     row-major tile through the LDS transpose read (ds_read_b64_tr_b16);
+//     P^T is the score accumulator itself, rounded to BF16, because the
+//     transpose read is addressed so that its key order matches the order
+//     of the score rows in the accumulator.
+// Each gathered byte feeds 64 heads x 4 FLOPs: with the dims split two ways
+// and the heads two ways, every LDS byte of the tile is read by two waves.
+
+#include "kpool_device.h"
+#include "kpool_internal.h"
+
+namespace kpool {
+
+namespace {
+
+constexpr int kD = 512;                 // latent width (key = value)
+constexpr int kHG = 64;                 // heads per workgroup
+constexpr int kBlk = 32;                // listed rows per block
+constexpr int kRowBytes = kD * 2;       // 1 KB
+constexpr int kTile = kBlk * kRowBytes; // 32 KB
+constexpr int kXchg = 4 * 16 * 64 * 4;  // partial scores of the four waves
+constexpr int kMlaLds = 2 * kTile + kXchg;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// chunk c (16 bytes) of tile row r sits at chunk position c ^ f(r). f maps
+// the 16 rows of an aligned group onto 0..15 (so 16 rows read at one chunk
+// hit 16 distinct chunk positions) and gives the 4 rows of an aligned
+// quadruple distinct values of f >> 1 (so a transpose read, 4 rows x 2
+// adjacent chunks, spreads over 8 distinct chunk positions).
+__device__ __forceinline__ int swz(int r) {
+  return ((r & 3) << 1) | ((r >> 2) & 1) | (r & 8);
+}
+
+__device__ __forceinline__ void dma_row(const void* src, uint8_t* lds_row) {
+  const uint32_t dst = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds_row);
+  uint32_t m0_saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "global_load_lds_dwordx4 %2, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(m0_saved)
+      : "s"(dst), "v"(src)
+      : "memory");
+}
+
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0f70); }
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ i16x4 lds_tr4(const uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (i16x4 __attribute__((address_space(3)))*)(
+          (__attribute__((address_space(3))) uint8_t*)p));
+}
+
+struct MlaKernelArgs {
+  const uint16_t* q;       // [T, H, 512]
+  const uint16_t* kv;      // [N, 512]
+  const int32_t* idx;      // [T, W]
+  uint16_t* out;           // [T, H, 512]
+  float* lse;              // [T, H]
+  int T, H, N, W, groups;  // groups = H / 64
+  int64_t total;           // T * groups
+  int64_t per_xcd;         // ceil(total / 8)
+  float scale2;            // sm_scale * log2(e)
+};
+
+// Copy block `blk` (listed entries 32*blk .. +31) of this query into `tile`:
+// wave w copies rows 8w .. 8w+7, one 1 KB row per instruction. `ids` holds
+// entry 32*blk + (lane & 31) of the list (-1 past the end); an unused entry
+// copies row 0 (its score is masked).
+__device__ __forceinline__ void load_block(const uint16_t* __restrict__ kv, int ids, int N,
+                                           uint8_t* tile, int wid, int lane) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int r = wid * 8 + j;
+    int tok = __builtin_amdgcn_readlane(ids, r);
+    tok = (tok >= 0 && tok < N) ? tok : 0;
+    const int c = lane ^ swz(r);                   // global chunk for LDS position `lane`
+    dma_row(kv + (size_t)tok * kD + c * 8, tile + r * kRowBytes);
+  }
+}
+
+__global__ __launch_bounds__(256, 1) void mla_fwd_kernel(MlaKernelArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  uint8_t* tiles = smem;                          // 2 x 32 KB
+  float* xchg = (float*)(smem + 2 * kTile);        // [4 waves][16 regs][64 lanes]
+
+  // blocks are dealt to the 8 XCDs in turn: give each XCD a contiguous run of
+  // (token, head group) items, so the rows that neighbouring tokens share
+  // stay in that XCD's L2
+  const int64_t id = blockIdx.x;
+  const int64_t item = (id & 7) * a.per_xcd + (id >> 3);
+  if (item >= a.total) return;
+  const int t = (int)(item / a.groups);
+  const int hg = (int)(item % a.groups);
+
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int hp = wid & 1, fh = wid >> 1;
+  const int32_t* __restrict__ idx_row = a.idx + (size_t)t * a.W;
+
+  // ---- used length of the list: one past its last entry in [0, N)
+  int last = -1;
+  for (int e = tid; e < a.W; e += 256) {
+    const int v = idx_row[e];
+    if (v >= 0 && v < a.N) last = e;
+  }
+  last = wave_max(last);
+  int* red = (int*)xchg;
+  if (lane == 0) red[wid] = last;
+  __syncthreads();
+  last = max(max(red[0], red[1]), max(red[2], red[3]));
+  __syncthreads();
+  const int nblk = (last + kBlk) / kBlk;           // 0 when nothing is used
+
+  auto ids_of = [&](int blk) {
+    const int e = blk * kBlk + (lane & 31);
+    return (blk < nblk && e < a.W) ? idx_row[e] : -1;
+  };
+
+  int ids_cur = ids_of(0);
+  if (nblk > 0) load_block(a.kv, ids_cur, a.N, tiles, wid, lane);
+  int ids_next = ids_of(1);
+
+  // ---- Q^T fragments: head 64hg + 32hp + (lane & 31), dims 256fh + 16ks + 8(lane >> 5) + 0..7
+  bf16x8 qf[16];
+  {
+    const uint16_t* qrow = a.q + ((size_t)t * a.H + hg * kHG + hp * 32 + (lane & 31)) * kD +
+                           fh * 256 + 8 * (lane >> 5);
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks)
+      qf[ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qrow + 16 * ks));
+  }
+
+  f32x16 acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+  const int h = lane >> 5;
+
+  for (int blk = 0; blk < nblk; ++blk) {
+    const uint8_t* tile = tiles + (blk & 1) * kTile;
+    // which of the 32 rows of this block are used
+    const bool used = ids_cur >= 0 && ids_cur < a.N;
+    const uint32_t used_mask = (uint32_t)__ballot(used);
+    wait_vmem_all();
+    __syncthreads();                                   // tile `blk` is in LDS for every wave
+    if (blk + 1 < nblk) load_block(a.kv, ids_next, a.N, tiles + ((blk + 1) & 1) * kTile, wid, lane);
+    ids_cur = ids_next;
+    ids_next = ids_of(blk + 2);
+
+    // ---- partial scores over this wave's 256 dims: S^T[row][head]
+    f32x16 s = f32x16{};
+    {
+      const int r = lane & 31;
+      const uint8_t* trow = tile + r * kRowBytes;
+      const int u = swz(r) ^ h;                        // chunk 2ks + h of the row sits at 2ks ^ u
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        bf16x8 kf[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int ks = half * 8 + j;
+          kf[j] = __builtin_bit_cast(
+              bf16x8, *(const u32x4*)(trow + ((fh * 32 + ((2 * ks) ^ u)) << 4)));
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[j], qf[half * 8 + j], s, 0, 0, 0);
+      }
+    }
+    // ---- add the partner's half (same heads, other dims)
+    float* mine = xchg + wid * 1024;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mine[r * 64 + lane] = s[r];
+    __syncthreads();
+    const float* other = xchg + (wid ^ 2) * 1024;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = s[r] + other[r * 64 + lane];
+
+    // ---- online softmax in base 2; register r holds row 8(r/4) + 4h + r%4.
+    // The reference point m_run only moves when a score passes it by more
+    // than 8 (weights stay <= 2^8), so the accumulator is rarely rescaled.
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = 8 * (r >> 2) + 4 * h + (r & 3);
+      const float v = ((used_mask >> row) & 1u) ? s[r] * a.scale2 : -INFINITY;
+      s[r] = v;
+      mx = fmaxf(mx, v);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const bool move = mx > (m_run == -INFINITY ? -INFINITY : m_run + 8.f);
+    if (__any(move)) {
+      const float m_new = move ? mx : m_run;
+      const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+      if (__any(move && m_run != -INFINITY)) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] *= alpha;
+      }
+      m_run = m_new;
+    }
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;
+    float psum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      s[r] = __builtin_amdgcn_exp2f(s[r] - m_use);
+      psum += s[r];
+    }
+    psum += __shfl_xor(psum, 32);
+    l_run += psum;
+    bf16x8 pb[2];
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      u32x4 w;
+      w.x = pack_bf16x2(s[8 * st + 0], s[8 * st + 1]);
+      w.y = pack_bf16x2(s[8 * st + 2], s[8 * st + 3]);
+      w.z = pack_bf16x2(s[8 * st + 4], s[8 * st + 5]);
+      w.w = pack_bf16x2(s[8 * st + 6], s[8 * st + 7]);
+      pb[st] = __builtin_bit_cast(bf16x8, w);
+    }
+
+    // ---- O^T += V^T . P^T over the 32 rows, 8 tiles of 32 dims
+    {
+      const int b = lane >> 4, i = lane & 15;
+      const int sub = (i & 1) * 8;                     // byte offset inside the 16-byte chunk
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt) {
+        const int c = (fh * 256 + mt * 32 + 16 * (b & 1) + 4 * (i & 3)) >> 3;
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          const int r0 = 16 * st + 4 * h + (i >> 2);
+          const int r1 = r0 + 8;
+          const i16x4 lo = lds_tr4(tile + r0 * kRowBytes + ((c ^ swz(r0)) << 4) + sub);
+          const i16x4 hi = lds_tr4(tile + r1 * kRowBytes + ((c ^ swz(r1)) << 4) + sub);
+          const bf16x8 vf = __builtin_bit_cast(
+              bf16x8, (short __attribute__((ext_vector_type(8)))){lo[0], lo[1], lo[2], lo[3],
+                                                                 hi[0], hi[1], hi[2], hi[3]});
+          acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[st], acc[mt], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // ---- o = O / l (BF16), lse = ln 2 * (m + log2 l)
+  const int head = hg * kHG + hp * 32 + (lane & 31);
+  const bool any = l_run > 0.f;
+  const float inv = any ? 1.f / l_run : 0.f;
+  uint16_t* orow = a.out + ((size_t)t * a.H + head) * kD + fh * 256 + 4 * h;
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      uint2 w;
+      w.x = pack_bf16x2(acc[mt][4 * g + 0] * inv, acc[mt][4 * g + 1] * inv);
+      w.y = pack_bf16x2(acc[mt][4 * g + 2] * inv, acc[mt][4 * g + 3] * inv);
+      *(uint2*)(orow + mt * 32 + 8 * g) = w;
+    }
+  }
+  if (fh == 0 && h == 0)
+    a.lse[(size_t)t * a.H + head] =
+        any ? (m_run + __builtin_amdgcn_logf(l_run)) * 0.69314718055994531f : -INFINITY;
+}
+
+}  // namespace
+
+int mla_lds_bytes() { return kMlaLds; }
+
+hipError_t launch_sparse_mla(const MlaArgs& m, hipStream_t stream) {
+  MlaKernelArgs a;
+  a.q = m.q;
+  a.kv = m.kv;
+  a.idx = m.idx;
+  a.out = m.out;
+  a.lse = m.lse;
+  a.T = m.T;
+  a.H = m.H;
+  a.N = m.N;
+  a.W = m.W;
+  a.groups = m.H / kHG;
+  a.total = (int64_t)m.T * a.groups;
+  a.per_xcd = (a.total + 7) / 8;
+  a.scale2 = m.scale2;
+  if (a.total == 0) return hipSuccess;
+  hipError_t e = hipFuncSetAttribute((const void*)mla_fwd_kernel,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, kMlaLds);
+  if (e != hipSuccess) return e;
+  const int64_t grid = 8 * a.per_xcd;
+  hipLaunchKernelGGL(mla_fwd_kernel, dim3((unsigned)grid), dim3(256), kMlaLds, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace kpool

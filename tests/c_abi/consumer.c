@@ -57,6 +57,33 @@ int main(void) {
                            (const int32_t*)fake, fake, ws - 1, (int32_t*)fake, NULL, NULL) ==
         KPOOL_E_WORKSPACE);
   CHECK(kpool_fp8_quantize(fake, -1, (uint8_t*)fake, (float*)fake, NULL) == KPOOL_E_INVALID);
+  {
+    kpool_mla_params mp;
+    memset(&mp, 0, sizeof mp);
+    mp.num_tokens = 4;
+    mp.num_heads = 64;
+    mp.kv_rows = 16;
+    mp.width = 8;
+    mp.dim_qk = 512;
+    mp.dim_v = 512;
+    mp.sm_scale = 0.0625f;
+    mp.num_heads = 96;
+    CHECK(kpool_sparse_mla_fwd(&mp, fake, fake, (const int32_t*)fake, fake, (float*)fake, NULL) ==
+          KPOOL_E_UNSUPPORTED);
+    mp.num_heads = 64;
+    mp.dim_v = 448;
+    CHECK(kpool_sparse_mla_fwd(&mp, fake, fake, (const int32_t*)fake, fake, (float*)fake, NULL) ==
+          KPOOL_E_UNSUPPORTED);
+    mp.dim_v = 512;
+    mp.width = -1;
+    CHECK(kpool_sparse_mla_fwd(&mp, fake, fake, (const int32_t*)fake, fake, (float*)fake, NULL) ==
+          KPOOL_E_INVALID);
+    mp.width = 8;
+    CHECK(kpool_sparse_mla_fwd(&mp, fake + 2, fake, (const int32_t*)fake, fake, (float*)fake,
+                               NULL) == KPOOL_E_INVALID);
+    mp.num_tokens = 0;
+    CHECK(kpool_sparse_mla_fwd(&mp, NULL, NULL, NULL, NULL, NULL, NULL) == KPOOL_OK);
+  }
   printf("all checks passed\n");
   return 0;
 }

@@ -250,3 +250,40 @@ def test_header_constants_match_binding():
     for name in ("KPOOL_LOGITS_FILL_MASKED", "KPOOL_LOGITS_SKIP_ALL_SELECTED",
                  "KPOOL_LOGITS_INPUTS_QUANTIZED"):
         assert getattr(kp, name) == int(defs[name]), name
+
+
+def _mla(T=4, H=64, N=16, W=8, scale=0.0625, dqk=512, dv=512):
+    return kp.MlaParams(num_tokens=T, num_heads=H, kv_rows=N, width=W, sm_scale=scale,
+                        dim_qk=dqk, dim_v=dv)
+
+
+@pytest.mark.parametrize("mp,status,msg", [
+    (_mla(H=32), kp.KPOOL_E_UNSUPPORTED, "multiple of 64"),
+    (_mla(H=0), kp.KPOOL_E_UNSUPPORTED, "multiple of 64"),
+    (_mla(dqk=576), kp.KPOOL_E_UNSUPPORTED, "512"),
+    (_mla(T=-1), kp.KPOOL_E_INVALID, ">= 0"),
+    (_mla(N=-3), kp.KPOOL_E_INVALID, ">= 0"),
+    (_mla(scale=float("inf")), kp.KPOOL_E_INVALID, "finite"),
+])
+def test_sparse_mla_rejects_bad_params(mp, status, msg):
+    """Shape and scale checks of kpool_sparse_mla_fwd come before any device
+    work (the pointers here are fake host addresses never dereferenced)."""
+    fake = 4096
+    st = kp.lib().kpool_sparse_mla_fwd(ctypes.byref(mp.c()), fake, fake, fake, fake, fake, None)
+    assert st == status
+    assert msg in kp.kpool_last_error()
+
+
+def test_sparse_mla_pointer_checks():
+    """Null or misaligned pointers are refused; T = 0 needs none; kv and
+    indices may be null when kv_rows or width is 0."""
+    L = kp.lib()
+    mp = _mla()
+    ok = 4096
+    for args, name in [((None, ok, ok, ok, ok), "q"), ((ok + 8, ok, ok, ok, ok), "q"),
+                       ((ok, None, ok, ok, ok), "kv"), ((ok, ok, ok + 2, ok, ok), "indices"),
+                       ((ok, ok, ok, ok + 4, ok), "out"), ((ok, ok, ok, ok, ok + 1), "lse")]:
+        st = L.kpool_sparse_mla_fwd(ctypes.byref(mp.c()), *args, None)
+        assert st == kp.KPOOL_E_INVALID and name in kp.kpool_last_error(), (args, name)
+    assert L.kpool_sparse_mla_fwd(ctypes.byref(_mla(T=0).c()), None, None, None, None, None,
+                                  None) == kp.KPOOL_OK

@@ -265,3 +265,19 @@ def make_mla_inputs(T: int, H: int, N: int, width: int, d: int = 512, seed: int 
     ids[padded[:, None] & (col >= keep[:, None])] = -1
     return MlaInputs(q=q.to(torch.bfloat16).contiguous(), kv=kv.to(torch.bfloat16).contiguous(),
                      indices=ids.to(torch.int32).contiguous())
+
+
+def make_mla_inputs_device(T: int, H: int, N: int, width: int, device, d: int = 512,
+                           seed: int = 0) -> MlaInputs:
+    """Large sparse-attention inputs drawn directly on `device` with a seeded
+    device generator (torch's Philox): q, kv ~ N(0, 1) cast to BF16; row t
+    lists `width` ids drawn uniformly with replacement from [0, min(N, t+1)),
+    the last `width // 8` entries of every fourth row set to -1. Draw order:
+    q, kv, ids."""
+    g = torch.Generator(device=device).manual_seed(seed)
+    q = torch.randn(T, H, d, generator=g, device=device).to(torch.bfloat16)
+    kv = torch.randn(N, d, generator=g, device=device).to(torch.bfloat16)
+    hi = torch.clamp(torch.arange(T, device=device) + 1, max=N)
+    ids = (torch.rand(T, width, generator=g, device=device) * hi[:, None]).floor().to(torch.int32)
+    ids[::4, width - width // 8:] = -1
+    return MlaInputs(q=q.contiguous(), kv=kv.contiguous(), indices=ids.contiguous())
