@@ -348,17 +348,17 @@ kpool_status kpool_indexer_projections(const kpool_proj_params* pp, const void* 
  *   out      BF16 [num_tokens, num_heads, 512], 16-byte aligned
  *   lse      FP32 [num_tokens, num_heads], 4-byte aligned
  * Device pointers, owned by the caller; nothing is allocated. Needs
- * num_heads a positive multiple of 64 and dim_qk = dim_v = 512, else
- * KPOOL_E_UNSUPPORTED; negative sizes or a non-finite sm_scale give
- * KPOOL_E_INVALID. Nothing is enqueued on an error. */
+ * num_heads a positive multiple of 64, dim_qk = dim_v = 512 and width <=
+ * 4096, else KPOOL_E_UNSUPPORTED; negative sizes or an sm_scale that is not finite
+ * and positive give KPOOL_E_INVALID. Nothing is enqueued on an error. */
 typedef struct {
   int32_t num_tokens;       /* T >= 0                                        */
   int32_t num_heads;        /* H, a positive multiple of 64                  */
   int32_t kv_rows;          /* N >= 0 rows in kv                             */
-  int32_t width;            /* W >= 0 entries per query in indices           */
+  int32_t width;            /* 0 <= W <= 4096 entries per query in indices  */
   int32_t dim_qk;           /* 512                                           */
   int32_t dim_v;            /* 512                                           */
-  float   sm_scale;         /* score scale (finite)                          */
+  float   sm_scale;         /* score scale, finite and > 0                   */
 } kpool_mla_params;
 kpool_status kpool_sparse_mla_fwd(const kpool_mla_params* mp, const void* q, const void* kv,
                                   const int32_t* indices, void* out, float* lse, void* stream);

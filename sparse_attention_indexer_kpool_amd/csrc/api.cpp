@@ -667,10 +667,13 @@ kpool_status kpool_sparse_mla_fwd(const kpool_mla_params* mp, const void* q, con
                 N, W);
   if (H <= 0 || H % 64 != 0)
     return fail(KPOOL_E_UNSUPPORTED, "num_heads must be a positive multiple of 64 (got %d)", H);
+  if (W > 4096)
+    return fail(KPOOL_E_UNSUPPORTED, "width must be <= 4096 entries per query (got %d)", W);
   if (mp->dim_qk != 512 || mp->dim_v != 512)
     return fail(KPOOL_E_UNSUPPORTED, "dim_qk and dim_v must be 512 (got %d, %d)", mp->dim_qk,
                 mp->dim_v);
-  if (!std::isfinite(mp->sm_scale)) return fail(KPOOL_E_INVALID, "sm_scale must be finite");
+  if (!std::isfinite(mp->sm_scale) || !(mp->sm_scale > 0.f))
+    return fail(KPOOL_E_INVALID, "sm_scale must be finite and > 0");
   if ((int64_t)T * (H / 64) > (1ll << 31) - 8)
     return fail(KPOOL_E_UNSUPPORTED, "num_tokens * num_heads / 64 is too large for one launch");
   if (T == 0) return ok();

@@ -43,8 +43,10 @@ constexpr int kHG = 64;                 // heads per workgroup
 constexpr int kBlk = 32;                // listed rows per block
 constexpr int kRowBytes = kD * 2;       // 1 KB
 constexpr int kTile = kBlk * kRowBytes; // 32 KB
+constexpr int kStages = 4;              // tile buffers: three blocks in flight
 constexpr int kXchg = 4 * 16 * 64 * 4;  // partial scores of the four waves
-constexpr int kMlaLds = 2 * kTile + kXchg;
+constexpr int kMaxWidth = 4096;         // list entries staged in LDS
+constexpr int kMlaLds = kStages * kTile + kXchg + kMaxWidth * 4;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -60,21 +62,27 @@ __device__ __forceinline__ int swz(int r) {
   return ((r & 3) << 1) | ((r >> 2) & 1) | (r & 8);
 }
 
-__device__ __forceinline__ void dma_row(const void* src, uint8_t* lds_row) {
-  const uint32_t dst = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds_row);
+// One 1 KB row: lane l copies 16 bytes from row_base + voff(l) to LDS
+// address dst + 16 l (row_base and dst are wave-uniform, voff a 32-bit byte
+// offset).
+__device__ __forceinline__ void dma_row(const void* row_base, uint32_t voff, uint32_t dst) {
   uint32_t m0_saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
       "s_mov_b32 m0, %1\n\t"
-      "global_load_lds_dwordx4 %2, off\n\t"
+      "global_load_lds_dwordx4 %2, %3\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(m0_saved)
-      : "s"(dst), "v"(src)
+      : "s"(dst), "v"(voff), "s"(row_base)
       : "memory");
 }
 
-__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0f70); }
+// s_waitcnt vmcnt(N) with expcnt and lgkmcnt left unconstrained
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0f70 | (N & 15) | ((N >> 4) << 14));
+}
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
@@ -105,21 +113,22 @@ struct MlaKernelArgs {
 // entry 32*blk + (lane & 31) of the list (-1 past the end); an unused entry
 // copies row 0 (its score is masked).
 __device__ __forceinline__ void load_block(const uint16_t* __restrict__ kv, int ids, int N,
-                                           uint8_t* tile, int wid, int lane) {
+                                           uint32_t tile_lds, int wid, int lane) {
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const int r = wid * 8 + j;
+    const int r = wid * 8 + j;                       // wave-uniform
     int tok = __builtin_amdgcn_readlane(ids, r);
     tok = (tok >= 0 && tok < N) ? tok : 0;
-    const int c = lane ^ swz(r);                   // global chunk for LDS position `lane`
-    dma_row(kv + (size_t)tok * kD + c * 8, tile + r * kRowBytes);
+    const uint32_t c = (uint32_t)(lane ^ swz(r));  // global chunk for LDS position `lane`
+    dma_row(kv + (size_t)tok * kD, c << 4, tile_lds + r * kRowBytes);
   }
 }
 
 __global__ __launch_bounds__(256, 1) void mla_fwd_kernel(MlaKernelArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  uint8_t* tiles = smem;                          // 2 x 32 KB
-  float* xchg = (float*)(smem + 2 * kTile);        // [4 waves][16 regs][64 lanes]
+  uint8_t* tiles = smem;                                   // kStages x 32 KB
+  float* xchg = (float*)(smem + kStages * kTile);          // [4 waves][16 regs][64 lanes]
+  int* ids_lds = (int*)(smem + kStages * kTile + kXchg);   // the query's list
 
   // blocks are dealt to the 8 XCDs in turn: give each XCD a contiguous run of
   // (token, head group) items, so the rows that neighbouring tokens share
@@ -130,14 +139,17 @@ __global__ __launch_bounds__(256, 1) void mla_fwd_kernel(MlaKernelArgs a) {
   const int t = (int)(item / a.groups);
   const int hg = (int)(item % a.groups);
 
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t tiles_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
   const int hp = wid & 1, fh = wid >> 1;
   const int32_t* __restrict__ idx_row = a.idx + (size_t)t * a.W;
 
-  // ---- used length of the list: one past its last entry in [0, N)
+  // ---- stage the list in LDS; used length = one past its last entry in [0, N)
   int last = -1;
   for (int e = tid; e < a.W; e += 256) {
     const int v = idx_row[e];
+    ids_lds[e] = v;
     if (v >= 0 && v < a.N) last = e;
   }
   last = wave_max(last);
@@ -148,14 +160,15 @@ __global__ __launch_bounds__(256, 1) void mla_fwd_kernel(MlaKernelArgs a) {
   __syncthreads();
   const int nblk = (last + kBlk) / kBlk;           // 0 when nothing is used
 
+  // entry 32*blk + (lane & 31) of the list, -1 past its end
   auto ids_of = [&](int blk) {
     const int e = blk * kBlk + (lane & 31);
-    return (blk < nblk && e < a.W) ? idx_row[e] : -1;
+    return e < a.W ? ids_lds[e] : -1;
   };
 
-  int ids_cur = ids_of(0);
-  if (nblk > 0) load_block(a.kv, ids_cur, a.N, tiles, wid, lane);
-  int ids_next = ids_of(1);
+#pragma unroll
+  for (int p = 0; p < kStages; ++p)
+    if (p < nblk) load_block(a.kv, ids_of(p), a.N, tiles_lds + p * kTile, wid, lane);
 
   // ---- Q^T fragments: head 64hg + 32hp + (lane & 31), dims 256fh + 16ks + 8(lane >> 5) + 0..7
   bf16x8 qf[16];
@@ -166,6 +179,9 @@ __global__ __launch_bounds__(256, 1) void mla_fwd_kernel(MlaKernelArgs a) {
     for (int ks = 0; ks < 16; ++ks)
       qf[ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qrow + 16 * ks));
   }
+  // the first blocks and Q have landed: no wait for Q remains inside the loop,
+  // where it would also hold back the copies of later blocks
+  wait_vmcnt<0>();
 
   f32x16 acc[8];
 #pragma unroll
@@ -173,109 +189,191 @@ __global__ __launch_bounds__(256, 1) void mla_fwd_kernel(MlaKernelArgs a) {
   float m_run = -INFINITY, l_run = 0.f;
   const int h = lane >> 5;
 
-  for (int blk = 0; blk < nblk; ++blk) {
-    const uint8_t* tile = tiles + (blk & 1) * kTile;
-    // which of the 32 rows of this block are used
-    const bool used = ids_cur >= 0 && ids_cur < a.N;
-    const uint32_t used_mask = (uint32_t)__ballot(used);
-    wait_vmem_all();
-    __syncthreads();                                   // tile `blk` is in LDS for every wave
-    if (blk + 1 < nblk) load_block(a.kv, ids_next, a.N, tiles + ((blk + 1) & 1) * kTile, wid, lane);
-    ids_cur = ids_next;
-    ids_next = ids_of(blk + 2);
+  // per-lane LDS byte offsets inside a tile
+  //   K (A operand of S^T = K.Q^T): row lane & 31, dims 256fh + 16ks + 8h .. +7
+  const int krow = (lane & 31) * kRowBytes;
+  const int ku = swz(lane & 31) ^ h;                     // chunk 2ks + h sits at 2ks ^ ku
+  //   V^T (A operand of O^T = V^T.P^T) by transpose reads: rows r0 and r0 + 8
+  //   (r0 = 16 st + 4h + (i >> 2)), dims 256fh + 32mt + 16(b & 1) + 4(i & 3) ..
+  const int tb = lane >> 4, ti = lane & 15;
+  const int tsub = (ti & 1) * 8;
 
-    // ---- partial scores over this wave's 256 dims: S^T[row][head]
-    f32x16 s = f32x16{};
-    {
-      const int r = lane & 31;
-      const uint8_t* trow = tile + r * kRowBytes;
-      const int u = swz(r) ^ h;                        // chunk 2ks + h of the row sits at 2ks ^ u
+  auto kfrags = [&](uint32_t tile_off, bf16x8 (&kf)[16]) {
+    const uint8_t* trow = tiles + tile_off + krow;
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        bf16x8 kf[8];
+    for (int ks = 0; ks < 16; ++ks)
+      kf[ks] = __builtin_bit_cast(bf16x8,
+                                  *(const u32x4*)(trow + ((fh * 32 + ((2 * ks) ^ ku)) << 4)));
+  };
+  auto vfrags = [&](uint32_t tile_off, bf16x8 (&vf)[8][2]) {
+    const uint8_t* tile = tiles + tile_off;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int ks = half * 8 + j;
-          kf[j] = __builtin_bit_cast(
-              bf16x8, *(const u32x4*)(trow + ((fh * 32 + ((2 * ks) ^ u)) << 4)));
-        }
+    for (int mt = 0; mt < 8; ++mt) {
+      const int c = (fh * 256 + mt * 32 + 16 * (tb & 1) + 4 * (ti & 3)) >> 3;
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[j], qf[half * 8 + j], s, 0, 0, 0);
+      for (int st = 0; st < 2; ++st) {
+        const int r0 = 16 * st + 4 * h + (ti >> 2);
+        const int r1 = r0 + 8;
+        const i16x4 lo = lds_tr4(tile + r0 * kRowBytes + ((c ^ swz(r0)) << 4) + tsub);
+        const i16x4 hi = lds_tr4(tile + r1 * kRowBytes + ((c ^ swz(r1)) << 4) + tsub);
+        vf[mt][st] = __builtin_bit_cast(
+            bf16x8, (short __attribute__((ext_vector_type(8)))){lo[0], lo[1], lo[2], lo[3],
+                                                               hi[0], hi[1], hi[2], hi[3]});
       }
     }
-    // ---- add the partner's half (same heads, other dims)
-    float* mine = xchg + wid * 1024;
+  };
+  // S = this wave's partial + the partner's (same heads, other dim half);
+  // both waves add the same two numbers, so both hold identical scores
+  float* mine = xchg + wid * 1024;
+  const float* other = xchg + (wid ^ 2) * 1024;
+  auto put_partial = [&](const f32x16& sp) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mine[r * 64 + lane] = s[r];
+    for (int r = 0; r < 16; ++r) mine[r * 64 + lane] = sp[r];
+  };
+  auto add_partner = [&](f32x16& sp) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sp[r] = sp[r] + other[r * 64 + lane];
+  };
+
+  // Unused rows of block b become -inf; returns the block's largest score
+  // in base-2 units (scale2 > 0 keeps the order), -inf if none is used.
+  auto prep = [&](f32x16& sc, int b) {
+    const int idc = ids_of(b);
+    const uint32_t used_mask = (uint32_t)__ballot(idc >= 0 && idc < a.N);
+    if (used_mask != 0xffffffffu) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = 8 * (r >> 2) + 4 * h + (r & 3);
+        sc[r] = ((used_mask >> row) & 1u) ? sc[r] : -INFINITY;
+      }
+    }
+    float mxs = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
+                      fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
+    mxs = fmaxf(mxs, fmaxf(fmaxf(fmaxf(sc[8], sc[9]), fmaxf(sc[10], sc[11])),
+                           fmaxf(fmaxf(sc[12], sc[13]), fmaxf(sc[14], sc[15]))));
+    mxs = fmaxf(mxs, __shfl_xor(mxs, 32));
+    return mxs * a.scale2;
+  };
+
+  // Software pipeline over blocks: iteration blk holds the full scores of
+  // block blk (s_cur, with its max mx_cur); it runs the weights of blk
+  // interleaved with the score products of block blk + 1, then
+  // O^T += V^T P^T of blk, then exchanges the partial scores of blk + 1.
+  // Register r of a score accumulator holds row 8(r/4) + 4h + r%4 (the
+  // 32 x 32 MFMA output layout). The base-2 reference point m_run moves only
+  // when a score passes it by more than 8 (weights stay <= 2^8); when it
+  // moves with a non-zero accumulator the inner loop stops, the accumulator
+  // is rescaled outside it, and the loop resumes at the same block.
+  f32x16 s_cur = f32x16{};
+  float mx_cur = -INFINITY;
+  if (nblk > 0) {
+    __syncthreads();                                   // the first blocks are in LDS
+    bf16x8 kf[16];
+    kfrags(0, kf);
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks)
+      s_cur = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], s_cur, 0, 0, 0);
+    put_partial(s_cur);
     __syncthreads();
-    const float* other = xchg + (wid ^ 2) * 1024;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s[r] = s[r] + other[r * 64 + lane];
+    add_partner(s_cur);
+    mx_cur = prep(s_cur, 0);
+  }
 
-    // ---- online softmax in base 2; register r holds row 8(r/4) + 4h + r%4.
-    // The reference point m_run only moves when a score passes it by more
-    // than 8 (weights stay <= 2^8), so the accumulator is rarely rescaled.
-    float mx = -INFINITY;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = 8 * (r >> 2) + 4 * h + (r & 3);
-      const float v = ((used_mask >> row) & 1u) ? s[r] * a.scale2 : -INFINITY;
-      s[r] = v;
-      mx = fmaxf(mx, v);
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const bool move = mx > (m_run == -INFINITY ? -INFINITY : m_run + 8.f);
-    if (__any(move)) {
-      const float m_new = move ? mx : m_run;
-      const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run *= alpha;
-      if (__any(move && m_run != -INFINITY)) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] *= alpha;
+  int blk = 0;
+  for (;;) {
+    for (; blk < nblk; ++blk) {
+      const bool move = mx_cur > (m_run == -INFINITY ? -INFINITY : m_run + 8.f);
+      if (__any(move && m_run != -INFINITY)) break;   // rare: rescale below
+      m_run = move ? mx_cur : m_run;                   // first used block: nothing to rescale
+      const bool nxt = blk + 1 < nblk;                 // uniform
+      if (nxt) {
+        // block blk + 1 has landed once at most the copies of blocks blk + 2
+        // and blk + 3 (8 per block and wave, issued later, completing in
+        // order) are outstanding
+        if (blk + 3 < nblk) wait_vmcnt<16>();
+        else if (blk + 2 < nblk) wait_vmcnt<8>();
+        else wait_vmcnt<0>();
+        __syncthreads();
       }
-      m_run = m_new;
-    }
-    const float m_use = m_run == -INFINITY ? 0.f : m_run;
-    float psum = 0.f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      s[r] = __builtin_amdgcn_exp2f(s[r] - m_use);
-      psum += s[r];
-    }
-    psum += __shfl_xor(psum, 32);
-    l_run += psum;
-    bf16x8 pb[2];
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      u32x4 w;
-      w.x = pack_bf16x2(s[8 * st + 0], s[8 * st + 1]);
-      w.y = pack_bf16x2(s[8 * st + 2], s[8 * st + 3]);
-      w.z = pack_bf16x2(s[8 * st + 4], s[8 * st + 5]);
-      w.w = pack_bf16x2(s[8 * st + 6], s[8 * st + 7]);
-      pb[st] = __builtin_bit_cast(bf16x8, w);
-    }
+      const uint32_t tcur = (uint32_t)(blk % kStages) * kTile;
+      const uint32_t tnxt = (uint32_t)((blk + 1) % kStages) * kTile;
 
-    // ---- O^T += V^T . P^T over the 32 rows, 8 tiles of 32 dims
-    {
-      const int b = lane >> 4, i = lane & 15;
-      const int sub = (i & 1) * 8;                     // byte offset inside the 16-byte chunk
+      // ---- region A: K fragments of the next block (stale data after the
+      // last block, whose products are discarded) and V^T fragments of this
+      // one; the first half of the next block's products
+      bf16x8 kf[16], vf[8][2];
+      f32x16 s_nxt = f32x16{};
+      __builtin_amdgcn_sched_barrier(0);
+      kfrags(tnxt, kf);
+      vfrags(tcur, vf);
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+        s_nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], s_nxt, 0, 0, 0);
+      // ---- region B: the weights of this block beside the second half of
+      // the next block's products, then O^T += V^T P^T
+      const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
+#pragma unroll
+      for (int ks = 8; ks < 16; ++ks)
+        s_nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], s_nxt, 0, 0, 0);
+      float psum = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s_cur[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[r], a.scale2, neg_m));
+        psum += s_cur[r];
+      }
+      bf16x8 pb[2];
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        u32x4 w;
+        w.x = pack_bf16x2(s_cur[8 * st + 0], s_cur[8 * st + 1]);
+        w.y = pack_bf16x2(s_cur[8 * st + 2], s_cur[8 * st + 3]);
+        w.z = pack_bf16x2(s_cur[8 * st + 4], s_cur[8 * st + 5]);
+        w.w = pack_bf16x2(s_cur[8 * st + 6], s_cur[8 * st + 7]);
+        pb[st] = __builtin_bit_cast(bf16x8, w);
+      }
+      psum += __shfl_xor(psum, 32);
+      l_run += psum;
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt) {
-        const int c = (fh * 256 + mt * 32 + 16 * (b & 1) + 4 * (i & 3)) >> 3;
 #pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          const int r0 = 16 * st + 4 * h + (i >> 2);
-          const int r1 = r0 + 8;
-          const i16x4 lo = lds_tr4(tile + r0 * kRowBytes + ((c ^ swz(r0)) << 4) + sub);
-          const i16x4 hi = lds_tr4(tile + r1 * kRowBytes + ((c ^ swz(r1)) << 4) + sub);
-          const bf16x8 vf = __builtin_bit_cast(
-              bf16x8, (short __attribute__((ext_vector_type(8)))){lo[0], lo[1], lo[2], lo[3],
-                                                                 hi[0], hi[1], hi[2], hi[3]});
-          acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[st], acc[mt], 0, 0, 0);
-        }
+        for (int st = 0; st < 2; ++st)
+          acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[mt][st], pb[st], acc[mt], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);     // K reads
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // one product
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);    // four V^T reads
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // one next-block product
+        __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);    // weights, sums, packing
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);     // O^T += V^T P^T
+      __builtin_amdgcn_sched_barrier(0);
+
+      // ---- exchange the next block's partial scores; then the buffer of
+      // this block is free for block blk + 4
+      if (nxt) {
+        put_partial(s_nxt);
+        __syncthreads();
+        if (blk + kStages < nblk)
+          load_block(a.kv, ids_of(blk + kStages), a.N, tiles_lds + tcur, wid, lane);
+        add_partner(s_nxt);
+        s_cur = s_nxt;
+        mx_cur = prep(s_cur, blk + 1);
       }
     }
+    if (blk >= nblk) break;
+    // the reference point of some heads moves by more than 8 at block blk
+    const bool move = mx_cur > m_run + 8.f;
+    const float m_new = move ? mx_cur : m_run;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    l_run *= alpha;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] *= alpha;
+    m_run = m_new;
   }
 
   // ---- o = O / l (BF16), lse = ln 2 * (m + log2 l)

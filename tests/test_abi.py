@@ -261,9 +261,12 @@ def _mla(T=4, H=64, N=16, W=8, scale=0.0625, dqk=512, dv=512):
     (_mla(H=32), kp.KPOOL_E_UNSUPPORTED, "multiple of 64"),
     (_mla(H=0), kp.KPOOL_E_UNSUPPORTED, "multiple of 64"),
     (_mla(dqk=576), kp.KPOOL_E_UNSUPPORTED, "512"),
+    (_mla(W=4097), kp.KPOOL_E_UNSUPPORTED, "4096"),
     (_mla(T=-1), kp.KPOOL_E_INVALID, ">= 0"),
     (_mla(N=-3), kp.KPOOL_E_INVALID, ">= 0"),
     (_mla(scale=float("inf")), kp.KPOOL_E_INVALID, "finite"),
+    (_mla(scale=0.0), kp.KPOOL_E_INVALID, "> 0"),
+    (_mla(scale=-0.5), kp.KPOOL_E_INVALID, "> 0"),
 ])
 def test_sparse_mla_rejects_bad_params(mp, status, msg):
     """Shape and scale checks of kpool_sparse_mla_fwd come before any device
