@@ -113,13 +113,18 @@ struct MlaKernelArgs {
 // entry 32*blk + (lane & 31) of the list (-1 past the end); an unused entry
 // copies row 0 (its score is masked).
 __device__ __forceinline__ void load_block(const uint16_t* __restrict__ kv, int ids, int N,
-                                           uint32_t tile_lds, int wid, int lane) {
+                                           uint32_t tile_lds, int wid) {
+  // the lane id, produced here (opaque to the compiler): the eight source
+  // offsets below are recomputed (one XOR each) instead of being kept live
+  // across the loop
+  int ln;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+  const int ids_ok = (ids >= 0 && ids < N) ? ids : 0;   // one clamp for all 32 rows
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int r = wid * 8 + j;                       // wave-uniform
-    int tok = __builtin_amdgcn_readlane(ids, r);
-    tok = (tok >= 0 && tok < N) ? tok : 0;
-    const uint32_t c = (uint32_t)(lane ^ swz(r));  // global chunk for LDS position `lane`
+    const int tok = __builtin_amdgcn_readlane(ids_ok, r);
+    const uint32_t c = (uint32_t)(ln ^ swz(r));    // global chunk for LDS position `lane`
     dma_row(kv + (size_t)tok * kD, c << 4, tile_lds + r * kRowBytes);
   }
 }
@@ -167,8 +172,8 @@ __global__ __launch_bounds__(256, 1) void mla_fwd_kernel(MlaKernelArgs a) {
   };
 
 #pragma unroll
-  for (int p = 0; p < kStages; ++p)
-    if (p < nblk) load_block(a.kv, ids_of(p), a.N, tiles_lds + p * kTile, wid, lane);
+  for (int p = 0; p < kStages - 1; ++p)
+    if (p < nblk) load_block(a.kv, ids_of(p), a.N, tiles_lds + p * kTile, wid);
 
   // ---- Q^T fragments: head 64hg + 32hp + (lane & 31), dims 256fh + 16ks + 8(lane >> 5) + 0..7
   bf16x8 qf[16];
@@ -182,6 +187,10 @@ __global__ __launch_bounds__(256, 1) void mla_fwd_kernel(MlaKernelArgs a) {
   // the first blocks and Q have landed: no wait for Q remains inside the loop,
   // where it would also hold back the copies of later blocks
   wait_vmcnt<0>();
+  // Q^T stays in accumulation registers (an MFMA reads its B operand from
+  // there directly), leaving the vector registers to the LDS fragments
+#pragma unroll
+  for (int ks = 0; ks < 16; ++ks) asm volatile("" : "+a"(qf[ks]));
 
   f32x16 acc[8];
 #pragma unroll
@@ -204,23 +213,6 @@ __global__ __launch_bounds__(256, 1) void mla_fwd_kernel(MlaKernelArgs a) {
     for (int ks = 0; ks < 16; ++ks)
       kf[ks] = __builtin_bit_cast(bf16x8,
                                   *(const u32x4*)(trow + ((fh * 32 + ((2 * ks) ^ ku)) << 4)));
-  };
-  auto vfrags = [&](uint32_t tile_off, bf16x8 (&vf)[8][2]) {
-    const uint8_t* tile = tiles + tile_off;
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt) {
-      const int c = (fh * 256 + mt * 32 + 16 * (tb & 1) + 4 * (ti & 3)) >> 3;
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        const int r0 = 16 * st + 4 * h + (ti >> 2);
-        const int r1 = r0 + 8;
-        const i16x4 lo = lds_tr4(tile + r0 * kRowBytes + ((c ^ swz(r0)) << 4) + tsub);
-        const i16x4 hi = lds_tr4(tile + r1 * kRowBytes + ((c ^ swz(r1)) << 4) + tsub);
-        vf[mt][st] = __builtin_bit_cast(
-            bf16x8, (short __attribute__((ext_vector_type(8)))){lo[0], lo[1], lo[2], lo[3],
-                                                               hi[0], hi[1], hi[2], hi[3]});
-      }
-    }
   };
   // S = this wave's partial + the partner's (same heads, other dim half);
   // both waves add the same two numbers, so both hold identical scores
@@ -281,45 +273,75 @@ __global__ __launch_bounds__(256, 1) void mla_fwd_kernel(MlaKernelArgs a) {
 
   int blk = 0;
   for (;;) {
+    // nothing the compiler loaded is pending when the inner loop starts, so
+    // it places no wait inside the loop (a wait there would also hold back
+    // the copies of later blocks)
+    wait_vmcnt<0>();
     for (; blk < nblk; ++blk) {
       const bool move = mx_cur > (m_run == -INFINITY ? -INFINITY : m_run + 8.f);
       if (__any(move && m_run != -INFINITY)) break;   // rare: rescale below
       m_run = move ? mx_cur : m_run;                   // first used block: nothing to rescale
       const bool nxt = blk + 1 < nblk;                 // uniform
       if (nxt) {
-        // block blk + 1 has landed once at most the copies of blocks blk + 2
-        // and blk + 3 (8 per block and wave, issued later, completing in
-        // order) are outstanding
-        if (blk + 3 < nblk) wait_vmcnt<16>();
-        else if (blk + 2 < nblk) wait_vmcnt<8>();
+        // block blk + 1 has landed once at most the copies of block blk + 2
+        // (8 per wave, issued later, completing in order) are outstanding
+        if (blk + 2 < nblk) wait_vmcnt<8>();
         else wait_vmcnt<0>();
-        __syncthreads();
+        __syncthreads();   // block blk + 1 is in LDS; block blk - 1 is no longer read
+        if (blk + kStages - 1 < nblk)
+          load_block(a.kv, ids_of(blk + kStages - 1), a.N,
+                     tiles_lds + (uint32_t)((blk + kStages - 1) % kStages) * kTile, wid);
       }
       const uint32_t tcur = (uint32_t)(blk % kStages) * kTile;
       const uint32_t tnxt = (uint32_t)((blk + 1) % kStages) * kTile;
 
-      // ---- region A: K fragments of the next block (stale data after the
-      // last block, whose products are discarded) and V^T fragments of this
-      // one; the first half of the next block's products
-      bf16x8 kf[16], vf[8][2];
-      f32x16 s_nxt = f32x16{};
-      __builtin_amdgcn_sched_barrier(0);
-      kfrags(tnxt, kf);
-      vfrags(tcur, vf);
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks)
-        s_nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], s_nxt, 0, 0, 0);
-      // ---- region B: the weights of this block beside the second half of
-      // the next block's products, then O^T += V^T P^T
+      // ---- the weights of this block beside the score products of the next
+      // one (K fragments of the next block: stale data after the last block,
+      // whose products are discarded), with the V^T reads of this block
+      // spread over the same steps. Each step is fenced so that the issue
+      // order is exactly: one product, the weight of one score, two reads.
       const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
-#pragma unroll
-      for (int ks = 8; ks < 16; ++ks)
-        s_nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], s_nxt, 0, 0, 0);
+      const uint8_t* vt = tiles + tcur;
+      const int vc = fh * 32 + 2 * (tb & 1) + ((ti & 3) >> 1);   // chunk of dim tile 0
+      auto vread = [&](int j) -> i16x4 {                         // j = 4 mt + 2 st + half
+        const int mt = j >> 2, st = (j >> 1) & 1, hf = j & 1;
+        const int rr = 16 * st + 4 * h + (ti >> 2) + 8 * hf;
+        return lds_tr4(vt + rr * kRowBytes + (((vc + 4 * mt) ^ swz(rr)) << 4) + tsub);
+      };
+      const uint8_t* krd = tiles + tnxt + krow;
+      auto kread = [&](int ks) -> bf16x8 {
+        return __builtin_bit_cast(bf16x8,
+                                  *(const u32x4*)(krd + ((fh * 32 + ((2 * ks) ^ ku)) << 4)));
+      };
+      auto vfrag = [&](const i16x4& lo, const i16x4& hi) -> bf16x8 {
+        return __builtin_bit_cast(
+            bf16x8, (short __attribute__((ext_vector_type(8)))){lo[0], lo[1], lo[2], lo[3],
+                                                               hi[0], hi[1], hi[2], hi[3]});
+      };
+      bf16x8 kf[16];
+      i16x4 vr[32];
+      f32x16 s_nxt = f32x16{};
       float psum = 0.f;
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s_cur[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[r], a.scale2, neg_m));
-        psum += s_cur[r];
+      for (int ks = 0; ks < 8; ++ks) kf[ks] = kread(ks);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) vr[j] = vread(j);
+      __builtin_amdgcn_sched_barrier(0);
+      // steps k = 0..15: product k, weight of score k, then the K fragment
+      // eight steps ahead (k < 8) or two V^T reads of dim tiles 0..3 (k >= 8)
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        s_nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[k], qf[k], s_nxt, 0, 0, 0);
+        s_cur[k] = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[k], a.scale2, neg_m));
+        psum += s_cur[k];
+        if (k < 8) {
+          kf[k + 8] = kread(k + 8);
+        } else if (k < 14) {
+          vr[4 + 2 * (k - 8)] = vread(4 + 2 * (k - 8));
+          vr[5 + 2 * (k - 8)] = vread(5 + 2 * (k - 8));
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
       bf16x8 pb[2];
 #pragma unroll
@@ -333,33 +355,29 @@ __global__ __launch_bounds__(256, 1) void mla_fwd_kernel(MlaKernelArgs a) {
       }
       psum += __shfl_xor(psum, 32);
       l_run += psum;
+      __builtin_amdgcn_sched_barrier(0);
+      // ---- O^T += V^T P^T: dim tiles 0..3 while tiles 4..7 are read
 #pragma unroll
-      for (int mt = 0; mt < 8; ++mt) {
-#pragma unroll
-        for (int st = 0; st < 2; ++st)
-          acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[mt][st], pb[st], acc[mt], 0, 0, 0);
+      for (int q = 0; q < 8; ++q) {
+        const int mt = q >> 1, st = q & 1;
+        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            vfrag(vr[4 * mt + 2 * st], vr[4 * mt + 2 * st + 1]), pb[st], acc[mt], 0, 0, 0);
+        vr[16 + 2 * q] = vread(16 + 2 * q);
+        vr[17 + 2 * q] = vread(17 + 2 * q);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);     // K reads
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // one product
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);    // four V^T reads
+      for (int q = 8; q < 16; ++q) {
+        const int mt = q >> 1, st = q & 1;
+        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            vfrag(vr[4 * mt + 2 * st], vr[4 * mt + 2 * st + 1]), pb[st], acc[mt], 0, 0, 0);
       }
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // one next-block product
-        __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);    // weights, sums, packing
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);     // O^T += V^T P^T
       __builtin_amdgcn_sched_barrier(0);
 
-      // ---- exchange the next block's partial scores; then the buffer of
-      // this block is free for block blk + 4
+      // ---- exchange the next block's partial scores
       if (nxt) {
         put_partial(s_nxt);
         __syncthreads();
-        if (blk + kStages < nblk)
-          load_block(a.kv, ids_of(blk + kStages), a.N, tiles_lds + tcur, wid, lane);
         add_partner(s_nxt);
         s_cur = s_nxt;
         mx_cur = prep(s_cur, blk + 1);
