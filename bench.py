@@ -15,6 +15,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME|IDX]
 from __future__ import annotations
 
 import argparse
+import math
 import hashlib
 import json
 import os
@@ -306,6 +307,38 @@ def projections_bench(reps: int, T: int = 65536, hidden: int = 4096, q_lora: int
             "note": "hidden and q_lora_rank are stand-in sizes"}
 
 
+def sparse_mla_bench(reps: int, T: int = 65536, H: int = 64, W: int = 2052):
+    """kpool_sparse_mla_fwd over T query tokens, H heads and W listed rows
+    each (index_topk 2048 + kpool 4, the indexer's row width), latent width
+    512, rows drawn uniformly from each token's causal prefix. Returns the
+    JSON object of its line."""
+    import sparse_attention_indexer_kpool_amd as kp
+    dev = "cuda:0"
+    m = wlm.make_mla_inputs_device(T, H, T, W, dev, seed=5)
+    out = torch.empty(T, H, 512, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(T, H, dtype=torch.float32, device=dev)
+    mp = kp.MlaParams(num_tokens=T, num_heads=H, kv_rows=T, width=W, sm_scale=1 / math.sqrt(192))
+    used = int(((m.indices >= 0) & (m.indices < T)).sum().item())
+    run = lambda: kp.kpool_sparse_mla_fwd(mp, m.q, m.kv, m.indices, out, lse)
+    ms = time_region(run, reps, warm=2)
+    # algorithmic work: per used entry and head, 512 multiply-adds for the
+    # score and 512 for the weighted row
+    flops = used * H * 512 * 4.0
+    gathered = used * 1024.0 + 2 * T * H * 512 * 2 + T * W * 4
+    del m, out, lse
+    torch.cuda.empty_cache()
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"entry": "kpool_sparse_mla_fwd",
+            "workload": f"sparse_mla_T{T}_H{H}_W{W}_D512", "ms": round(ms, 4),
+            "tokens_per_s": round(T / (ms * 1e-3), 1),
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2),
+                         "peak": round(PEAK_BF16_TFLOPS, 1), "unit": "TFLOP/s",
+                         "frac": round(tf / PEAK_BF16_TFLOPS, 4)},
+            "bytes_touched": gathered,
+            "note": "rows gathered per query: 1 KB each, mostly from L2/MALL; "
+                    "rows drawn uniformly from the causal prefix"}
+
+
 def measure_workload(wl, steps: int, warmup: int):
     """One workload: the whole step timed over `steps` steps after `warmup`
     untimed ones, then each phase alone with the same launches. Returns
@@ -461,6 +494,8 @@ def main():
     if not args.no_others and wl.name == "long_T65536_H32_D128":
         log("indexer projections")
         out["projections"] = projections_bench(max(3, min(args.steps, 10)))
+        log("sparse MLA forward over the selected rows")
+        out["sparse_mla"] = sparse_mla_bench(max(3, min(args.steps, 5)))
         # the FP8 input path and the short workloads, each timed the same way
         for key, other in (("fp8", "fp8_T32768_H32_D128"), ("tiny", "tiny_T256_H4_D64"),
                            ("single_4k", "single_T4096_H32_D128"),
