@@ -326,6 +326,26 @@ kpool_status kpool_indexer_projections(const kpool_proj_params* pp, const void* 
                                        size_t workspace_bytes, void* q_out, void* k_out,
                                        void* gate_out, float* w_out, void* stream);
 
+/* ---- Debug check of the document offsets -------------------------------
+ * ([MLM] section 3: pools restart at every document of the packed batch, so
+ * cu_seqlens decides every pool's tokens.) The entry points that take
+ * cu_seqlens assume, without checking its device-resident contents, that
+ * cu_seqlens[0] = 0, that it never decreases, that no document is longer
+ * than max_seqlen and that cu_seqlens[num_docs] = total_tokens. This call
+ * checks exactly that on the device and writes, to the device int32
+ * *flags_out, the OR of KPOOL_CU_* bits for the violations found (0 = the
+ * offsets are valid). It reads cu_seqlens[0 .. num_docs] and writes
+ * *flags_out only (no prior clearing needed); one small launch on `stream`.
+ * KPOOL_E_INVALID for num_docs < 0, total_tokens < 0, max_seqlen < 0, or a
+ * null or misaligned (4-byte) pointer. */
+#define KPOOL_CU_FIRST_NOT_ZERO 1
+#define KPOOL_CU_DECREASING 2
+#define KPOOL_CU_TOO_LONG 4
+#define KPOOL_CU_LAST_NOT_TOTAL 8
+kpool_status kpool_check_cu_seqlens(const int32_t* cu_seqlens, int32_t num_docs,
+                                    int32_t total_tokens, int32_t max_seqlen, int32_t* flags_out,
+                                    void* stream);
+
 /* ---- Sparse attention over the selected rows (the indices' consumer) ----
  * ([XT] "Summary": the sparse MLA backend runs FlashMLA's forward over the
  * indexer's int32 indices, with heads in multiples of 64; [XT] LSE fix

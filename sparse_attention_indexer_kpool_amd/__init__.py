@@ -184,6 +184,8 @@ def lib() -> ctypes.CDLL:
         L.kpool_indexer_projections.restype = ctypes.c_int
         L.kpool_indexer_projections.argtypes = [PP, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp,
                                                 vp, vp, vp, vp]
+        L.kpool_check_cu_seqlens.restype = ctypes.c_int
+        L.kpool_check_cu_seqlens.argtypes = [vp, i32, i32, i32, vp, vp]
         MP = ctypes.POINTER(_MlaParams)
         L.kpool_sparse_mla_fwd.restype = ctypes.c_int
         L.kpool_sparse_mla_fwd.argtypes = [MP, vp, vp, vp, vp, vp, vp]
@@ -204,7 +206,7 @@ EXPORTS = ["kpool_abi_version", "kpool_workspace_bytes", "kpool_logits_ld",
            "kpool_fp8_quantize", "kpool_compress_pools", "kpool_decode_workspace_bytes",
            "kpool_decode_topk", "kpool_decode_noalloc_max_bytes", "kpool_decode_topk_noalloc",
            "kpool_proj_workspace_bytes", "kpool_indexer_projections", "kpool_sparse_mla_fwd",
-           "kpool_status_string", "kpool_last_error"]
+           "kpool_check_cu_seqlens", "kpool_status_string", "kpool_last_error"]
 
 
 def _check(status: int) -> None:
@@ -279,6 +281,10 @@ def kpool_indexer_topk_fused(p: Params, q, w, pooled, cu_seqlens, cu_pools, work
 KPOOL_LOGITS_FILL_MASKED = 1
 KPOOL_LOGITS_SKIP_ALL_SELECTED = 2
 KPOOL_LOGITS_INPUTS_QUANTIZED = 4
+KPOOL_CU_FIRST_NOT_ZERO = 1
+KPOOL_CU_DECREASING = 2
+KPOOL_CU_TOO_LONG = 4
+KPOOL_CU_LAST_NOT_TOTAL = 8
 
 
 def kpool_logits(p: Params, q, w, pooled, cu_seqlens, cu_pools, q_begin, q_end, workspace,
@@ -360,6 +366,12 @@ def kpool_indexer_projections(pp: ProjParams, x, qr, wq_b, wk, k_norm_weight, k_
         ctypes.byref(pp.c()), _ptr(x), _ptr(qr), _ptr(wq_b), _ptr(wk), _ptr(k_norm_weight),
         _ptr(k_norm_bias), _ptr(wg), _ptr(ww), _ptr(workspace), ws_bytes, _ptr(q_out),
         _ptr(k_out), _ptr(gate_out), _ptr(w_out), _stream(stream)))
+
+
+def kpool_check_cu_seqlens(cu_seqlens, num_docs: int, total_tokens: int, max_seqlen: int,
+                           flags_out, stream=None) -> None:
+    _check(lib().kpool_check_cu_seqlens(_ptr(cu_seqlens), int(num_docs), int(total_tokens),
+                                        int(max_seqlen), _ptr(flags_out), _stream(stream)))
 
 
 def kpool_sparse_mla_fwd(mp: MlaParams, q, kv, indices, out, lse, stream=None) -> None:

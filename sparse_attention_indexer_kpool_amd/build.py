@@ -15,7 +15,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libkpool.so")
 
-SOURCES = ["api.cpp", "compress.hip", "decode.hip", "expand.hip", "fp8_quant.hip", "logits.hip",
+SOURCES = ["api.cpp", "check.hip", "compress.hip", "decode.hip", "expand.hip", "fp8_quant.hip", "logits.hip",
            "mla.hip", "proj.hip", "select.hip"]
 
 ARCH = "gfx950"

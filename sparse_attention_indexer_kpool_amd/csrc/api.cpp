@@ -657,6 +657,27 @@ kpool_status kpool_indexer_projections(const kpool_proj_params* pp, const void* 
   return after_launch();
 }
 
+kpool_status kpool_check_cu_seqlens(const int32_t* cu_seqlens, int32_t num_docs,
+                                    int32_t total_tokens, int32_t max_seqlen, int32_t* flags_out,
+                                    void* stream) {
+  Range range("kpool_check_cu_seqlens");
+  static_assert(kpool::kCuFirstNotZero == KPOOL_CU_FIRST_NOT_ZERO &&
+                    kpool::kCuDecreasing == KPOOL_CU_DECREASING &&
+                    kpool::kCuTooLong == KPOOL_CU_TOO_LONG &&
+                    kpool::kCuLastNotTotal == KPOOL_CU_LAST_NOT_TOTAL,
+                "violation bits");
+  if (num_docs < 0 || total_tokens < 0 || max_seqlen < 0)
+    return fail(KPOOL_E_INVALID, "num_docs (%d), total_tokens (%d) and max_seqlen (%d) must be >= 0",
+                num_docs, total_tokens, max_seqlen);
+  CHECK(check_ptr(cu_seqlens, 4, "cu_seqlens"));
+  CHECK(check_ptr(flags_out, 4, "flags_out"));
+  (void)hipGetLastError();
+  hipError_t e = kpool::launch_check_cu_seqlens(cu_seqlens, num_docs, total_tokens, max_seqlen,
+                                                flags_out, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(KPOOL_E_LAUNCH, "HIP launch error: %s", hipGetErrorString(e));
+  return ok();
+}
+
 kpool_status kpool_sparse_mla_fwd(const kpool_mla_params* mp, const void* q, const void* kv,
                                   const int32_t* indices, void* out, float* lse, void* stream) {
   Range range("kpool_sparse_mla_fwd");

@@ -136,6 +136,12 @@ struct MlaArgs {
 int mla_lds_bytes();
 hipError_t launch_sparse_mla(const MlaArgs& m, hipStream_t st);
 
+// Violation bits of the cu_seqlens check (the values of the header's
+// KPOOL_CU_* constants).
+constexpr int kCuFirstNotZero = 1, kCuDecreasing = 2, kCuTooLong = 4, kCuLastNotTotal = 8;
+hipError_t launch_check_cu_seqlens(const int32_t* cu, int B, int T, int max_seqlen, int32_t* out,
+                                   hipStream_t stream);
+
 // Largest max_pools the selection kernel handles (its LDS bitmap has one bit
 // per pool of a row).
 constexpr int kMaxSelectPools = 65536;

@@ -84,6 +84,11 @@ int main(void) {
     mp.num_tokens = 0;
     CHECK(kpool_sparse_mla_fwd(&mp, NULL, NULL, NULL, NULL, NULL, NULL) == KPOOL_OK);
   }
+  CHECK(kpool_check_cu_seqlens((const int32_t*)fake, -1, 8, 8, (int32_t*)fake, NULL) ==
+        KPOOL_E_INVALID);
+  CHECK(kpool_check_cu_seqlens(NULL, 1, 8, 8, (int32_t*)fake, NULL) == KPOOL_E_INVALID);
+  CHECK((KPOOL_CU_FIRST_NOT_ZERO | KPOOL_CU_DECREASING | KPOOL_CU_TOO_LONG |
+         KPOOL_CU_LAST_NOT_TOTAL) == 15);
   printf("all checks passed\n");
   return 0;
 }

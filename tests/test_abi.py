@@ -248,7 +248,8 @@ def test_header_constants_match_binding():
         if hasattr(kp, name):
             assert getattr(kp, name) == int(val), name
     for name in ("KPOOL_LOGITS_FILL_MASKED", "KPOOL_LOGITS_SKIP_ALL_SELECTED",
-                 "KPOOL_LOGITS_INPUTS_QUANTIZED"):
+                 "KPOOL_LOGITS_INPUTS_QUANTIZED", "KPOOL_CU_FIRST_NOT_ZERO",
+                 "KPOOL_CU_DECREASING", "KPOOL_CU_TOO_LONG", "KPOOL_CU_LAST_NOT_TOTAL"):
         assert getattr(kp, name) == int(defs[name]), name
 
 
@@ -290,3 +291,16 @@ def test_sparse_mla_pointer_checks():
         assert st == kp.KPOOL_E_INVALID and name in kp.kpool_last_error(), (args, name)
     assert L.kpool_sparse_mla_fwd(ctypes.byref(_mla(T=0).c()), None, None, None, None, None,
                                   None) == kp.KPOOL_OK
+
+
+def test_check_cu_seqlens_argument_checks():
+    """kpool_check_cu_seqlens refuses negative sizes and null or misaligned
+    pointers before any launch (fake host addresses, never dereferenced)."""
+    L = kp.lib()
+    ok = 4096
+    for args, msg in [((ok, -1, 8, 8, ok), ">= 0"), ((ok, 1, -8, 8, ok), ">= 0"),
+                      ((ok, 1, 8, -1, ok), ">= 0"), ((None, 1, 8, 8, ok), "cu_seqlens"),
+                      ((ok + 2, 1, 8, 8, ok), "cu_seqlens"), ((ok, 1, 8, 8, None), "flags_out"),
+                      ((ok, 1, 8, 8, ok + 1), "flags_out")]:
+        assert L.kpool_check_cu_seqlens(*args, None) == kp.KPOOL_E_INVALID, args
+        assert msg in kp.kpool_last_error()
