@@ -53,11 +53,14 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-// chunk c (16 bytes) of tile row r sits at chunk position c ^ f(r). f maps
-// the 16 rows of an aligned group onto 0..15 (so 16 rows read at one chunk
-// hit 16 distinct chunk positions) and gives the 4 rows of an aligned
-// quadruple distinct values of f >> 1 (so a transpose read, 4 rows x 2
-// adjacent chunks, spreads over 8 distinct chunk positions).
+// chunk c (16 bytes) of tile row r sits at chunk position
+// c ^ f(r) ^ 8 ((c >> 1) & 1). f maps the 16 rows of an aligned group onto
+// 0..15, so 16 rows read at one chunk hit 16 distinct positions. f also gives
+// the 4 rows of an aligned quadruple distinct values of f >> 1, so a
+// transpose read (4 rows x 2 adjacent chunks per 16 lanes) covers 8
+// distinct positions of one aligned 8-chunk half of a 256-byte bank window.
+// The extra flip of bit 3 by bit 1 of c sends the 16 lanes next to them,
+// which read chunks c + 2 and c + 3 of the same rows, to the other half.
 __device__ __forceinline__ int swz(int r) {
   return ((r & 3) << 1) | ((r >> 2) & 1) | (r & 8);
 }
@@ -124,7 +127,8 @@ __device__ __forceinline__ void load_block(const uint16_t* __restrict__ kv, int 
   for (int j = 0; j < 8; ++j) {
     const int r = wid * 8 + j;                       // wave-uniform
     const int tok = __builtin_amdgcn_readlane(ids_ok, r);
-    const uint32_t c = (uint32_t)(ln ^ swz(r));    // global chunk for LDS position `lane`
+    const int c0 = ln ^ swz(r);                      // global chunk for LDS position `lane`
+    const uint32_t c = (uint32_t)(c0 ^ (((c0 >> 1) & 1) << 3));
     dma_row(kv + (size_t)tok * kD, c << 4, tile_lds + r * kRowBytes);
   }
 }
@@ -201,7 +205,7 @@ __global__ __launch_bounds__(256, 1) void mla_fwd_kernel(MlaKernelArgs a) {
   // per-lane LDS byte offsets inside a tile
   //   K (A operand of S^T = K.Q^T): row lane & 31, dims 256fh + 16ks + 8h .. +7
   const int krow = (lane & 31) * kRowBytes;
-  const int ku = swz(lane & 31) ^ h;                     // chunk 2ks + h sits at 2ks ^ ku
+  const int ku = swz(lane & 31) ^ h;    // chunk 2ks + h sits at 2ks ^ ku ^ 8 (ks & 1)
   //   V^T (A operand of O^T = V^T.P^T) by transpose reads: rows r0 and r0 + 8
   //   (r0 = 16 st + 4h + (i >> 2)), dims 256fh + 32mt + 16(b & 1) + 4(i & 3) ..
   const int tb = lane >> 4, ti = lane & 15;
@@ -211,8 +215,8 @@ __global__ __launch_bounds__(256, 1) void mla_fwd_kernel(MlaKernelArgs a) {
     const uint8_t* trow = tiles + tile_off + krow;
 #pragma unroll
     for (int ks = 0; ks < 16; ++ks)
-      kf[ks] = __builtin_bit_cast(bf16x8,
-                                  *(const u32x4*)(trow + ((fh * 32 + ((2 * ks) ^ ku)) << 4)));
+      kf[ks] = __builtin_bit_cast(
+          bf16x8, *(const u32x4*)(trow + ((fh * 32 + ((2 * ks) ^ ku ^ ((ks & 1) << 3))) << 4)));
   };
   // S = this wave's partial + the partner's (same heads, other dim half);
   // both waves add the same two numbers, so both hold identical scores
@@ -306,12 +310,13 @@ __global__ __launch_bounds__(256, 1) void mla_fwd_kernel(MlaKernelArgs a) {
       auto vread = [&](int j) -> i16x4 {                         // j = 4 mt + 2 st + half
         const int mt = j >> 2, st = (j >> 1) & 1, hf = j & 1;
         const int rr = 16 * st + 4 * h + (ti >> 2) + 8 * hf;
-        return lds_tr4(vt + rr * kRowBytes + (((vc + 4 * mt) ^ swz(rr)) << 4) + tsub);
+        return lds_tr4(vt + rr * kRowBytes + (((vc + 4 * mt) ^ swz(rr) ^ ((tb & 1) << 3)) << 4) +
+                       tsub);
       };
       const uint8_t* krd = tiles + tnxt + krow;
       auto kread = [&](int ks) -> bf16x8 {
-        return __builtin_bit_cast(bf16x8,
-                                  *(const u32x4*)(krd + ((fh * 32 + ((2 * ks) ^ ku)) << 4)));
+        return __builtin_bit_cast(
+            bf16x8, *(const u32x4*)(krd + ((fh * 32 + ((2 * ks) ^ ku ^ ((ks & 1) << 3))) << 4)));
       };
       auto vfrag = [&](const i16x4& lo, const i16x4& hi) -> bf16x8 {
         return __builtin_bit_cast(
