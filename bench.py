@@ -152,18 +152,32 @@ class Path:
         del graph, ks, gs
         return ms / n_copies
 
-    def phase_logits(self, logits):
-        """The scoring kernel of every chunk, as the indexer launches it. On
-        the FP8 path the workspace already holds the quantised q and keys of
-        the last step, so only the scoring kernel runs."""
+    def indexer_phases(self, reps):
+        """Device ms per step of the indexer's scoring kernels and of its
+        selection + expansion kernels: the step's own launches
+        (kpool_indexer_scoring, then kpool_indexer_selection, launch by
+        launch), each kernel group bracketed by HIP events on the launch
+        stream; one untimed pass first. On the FP8 path the workspace already
+        holds the quantised q and keys of the last step, so only the scoring
+        kernel runs."""
         kp = self.kp
-        flags = kp.KPOOL_LOGITS_SKIP_ALL_SELECTED
-        if self.p.use_fp8:
-            flags |= kp.KPOOL_LOGITS_INPUTS_QUANTIZED
-        for c0 in range(0, self.inp.T, self.qc):
-            c1 = min(self.inp.T, c0 + self.qc)
-            kp.kpool_logits(self.p, self.q, self.w, self.pooled, self.cu, self.cu_pools, c0, c1,
-                            self.ws, logits[:c1 - c0], flags=flags)
+        launches = kp.kpool_indexer_launches(self.p)
+        flags = kp.KPOOL_LOGITS_INPUTS_QUANTIZED if self.p.use_fp8 else 0
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in launches]
+        t_score = t_select = 0.0
+        for r in range(reps + 1):
+            for i, e in enumerate(ev):
+                e[0].record()
+                kp.kpool_indexer_scoring(self.p, i, self.q, self.w, self.pooled, self.cu,
+                                         self.cu_pools, self.ws, flags)
+                e[1].record()
+                kp.kpool_indexer_selection(self.p, i, self.cu, self.cu_pools, self.ws, self.tok)
+                e[2].record()
+            torch.cuda.synchronize()
+            if r:
+                t_score += sum(e[0].elapsed_time(e[1]) for e in ev)
+                t_select += sum(e[1].elapsed_time(e[2]) for e in ev)
+        return t_score / reps, t_select / reps, len(launches)
 
     def phase_fp8_quant(self, bufs):
         """The FP8 input path over every q row (t, h) and every pooled key."""
@@ -172,18 +186,29 @@ class Path:
         self.kp.kpool_fp8_quantize(self.q.view(rows, 128), rows, qc, qs)
         self.kp.kpool_fp8_quantize(self.pooled[:P], P, kc, ks)
 
-    def phase_select(self, logits, ids):
+    def phase_select(self, logits, ids, reps):
+        """Device ms of the kpool_select stage entry (pool ids only) over every
+        chunk: each chunk's scores come first from kpool_logits (untimed),
+        then the selection kernel alone between HIP events."""
         kp = self.kp
-        for c0 in range(0, self.inp.T, self.qc):
-            c1 = min(self.inp.T, c0 + self.qc)
-            kp.kpool_select(self.p, logits[:c1 - c0], c0, c1, self.cu, self.cu_pools, ids[c0:c1])
-
-    def phase_select_expand(self, logits):
-        kp = self.kp
-        for c0 in range(0, self.inp.T, self.qc):
-            c1 = min(self.inp.T, c0 + self.qc)
-            kp.kpool_select_expand(self.p, logits[:c1 - c0], c0, c1, self.cu, self.cu_pools, None,
-                                   self.tok[c0:c1])
+        flags = kp.KPOOL_LOGITS_SKIP_ALL_SELECTED
+        if self.p.use_fp8:
+            flags |= kp.KPOOL_LOGITS_INPUTS_QUANTIZED
+        chunks = [(c0, min(self.inp.T, c0 + self.qc)) for c0 in range(0, self.inp.T, self.qc)]
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in chunks]
+        t = 0.0
+        for r in range(reps + 1):
+            for (c0, c1), e in zip(chunks, ev):
+                kp.kpool_logits(self.p, self.q, self.w, self.pooled, self.cu, self.cu_pools, c0,
+                                c1, self.ws, logits[:c1 - c0], flags=flags)
+                e[0].record()
+                kp.kpool_select(self.p, logits[:c1 - c0], c0, c1, self.cu, self.cu_pools,
+                                ids[c0:c1])
+                e[1].record()
+            torch.cuda.synchronize()
+            if r:
+                t += sum(a.elapsed_time(b) for a, b in ev)
+        return t / reps
 
     def phase_expand(self, ids):
         self.kp.kpool_expand(self.p, ids, self.cu, self.cu_pools, self.tok)
@@ -357,15 +382,13 @@ def measure_workload(wl, steps: int, warmup: int):
     ms = time_region(path.step, steps, warm=0)
     log(f"{wl.name}: {ms:.4f} ms/step")
 
-    # phases, each timed live on the launch stream with the same launches
+    # phases, each timed live on the launch stream with the step's launches
     logits = torch.empty(path.qc, path.ld, dtype=torch.float32, device="cuda:0")
     ids = torch.empty(T, wl.k_sel, dtype=torch.int32, device="cuda:0")
     reps = max(3, min(steps, 10))
-    path.phase_logits(logits)      # also leaves the pooled keys / fp8 buffers in place
     ms_compress = path.time_compress_cold()
-    ms_logits = time_region(lambda: path.phase_logits(logits), reps)
-    ms_select_expand = time_region(lambda: path.phase_select_expand(logits), reps)
-    ms_select = time_region(lambda: path.phase_select(logits, ids), reps)
+    ms_logits, ms_select_expand, n_launches = path.indexer_phases(reps)
+    ms_select = path.phase_select(logits, ids, reps)
     ms_expand = time_region(lambda: path.phase_expand(ids), reps)
     ms_fp8 = None
     P = sum(L // wl.kpool for L in inp.doc_lengths)
@@ -377,7 +400,6 @@ def measure_workload(wl, steps: int, warmup: int):
                 torch.empty(max(P, 1), dtype=torch.float32, device="cuda:0"), P)
         ms_fp8 = time_region(lambda: path.phase_fp8_quant(bufs), reps)
     del logits, ids
-    n_chunks = (T + path.qc - 1) // path.qc
     fused = None
     if wl.k_sel <= path.kp.kpool_fused_max_ksel(path.p):
         path.fused_step()
@@ -408,7 +430,7 @@ def measure_workload(wl, steps: int, warmup: int):
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak, 1),
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": logits_traffic(wl.name),
-                     "kernel": "logits_kernel", "launches_per_step": n_chunks,
+                     "kernel": "logits_kernel", "launches_per_step": n_launches,
                      "algorithmic_flops_per_step": flops},
         "phases_ms": {"compress": round(ms_compress, 4), "logits": round(ms_logits, 4),
                       "select_expand": round(ms_select_expand, 4),

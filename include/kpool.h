@@ -117,9 +117,12 @@ kpool_status kpool_compress(const kpool_params* p, const void* k, const void* ga
  * the min(K_sel, n_c(t)) best pools (ties to the lower pool id) are expanded,
  * in ascending pool order, to their kpool tokens, followed by the tail(t)
  * tokens cu[b] + n_c(t)*kpool .. t, then -1 up to width W. Query rows go
- * kpool_query_chunk_rows at a time through a logits tile in the workspace:
- * the scoring kernel of kpool_logits, then the selection + expansion kernel
- * of kpool_select_expand on each chunk.
+ * kpool_query_chunk_rows at a time (a chunk) through a logits tile in the
+ * workspace ([XT] summary: chunking bounds the tile): the launches that
+ * kpool_indexer_launches lists, each the scoring kernel of kpool_logits over
+ * one chunk, or over a long and a short chunk that fit the tile together at
+ * their own row strides, then the selection + expansion kernel of
+ * kpool_select_expand on each of its chunks.
  * With use_fp8 the q rows (t, h) and the pooled rows first go through the FP8
  * input path of kpool_fp8_quantize and are scored from their E4M3 codes and
  * power-of-two scales.
@@ -136,6 +139,45 @@ kpool_status kpool_indexer_topk(const kpool_params* p, const void* q, const floa
                                 const int32_t* cu_pools, void* workspace,
                                 size_t workspace_bytes, int32_t* out_token_idx,
                                 int32_t* out_pool_idx, void* stream);
+
+/* kpool_indexer_topk one launch at a time, for callers that interleave other
+ * work with the chunks or time the two kernels apart.
+ *
+ * kpool_indexer_launches returns the number of scoring launches the indexer
+ * makes (0 when T == 0 or the parameters are invalid) and, when info is not
+ * NULL, writes the first min(count, max_launches) of them as six int32 each:
+ *   {a0, a1, lda, b0, b1, ldb}
+ * launch i scores query rows a0 .. a1-1 into the workspace's logits tile
+ * with row stride lda floats, then rows b0 .. b1-1 (none when b0 == b1)
+ * right after them with row stride ldb. Every row stride is at least the
+ * largest causal pool count of its rows, rounded up to 64 (a row t has at
+ * most (t + 1) / kpool pools); the two ranges fit the tile together. Every
+ * query row belongs to exactly one range of one launch.
+ *
+ * kpool_indexer_scoring enqueues launch i's scoring kernel (rows with
+ * n_c(t) <= K_sel are left unwritten, as the indexer does). With use_fp8 it
+ * first quantises the launch's q rows and all pooled keys into the
+ * workspace, unless flags holds KPOOL_LOGITS_INPUTS_QUANTIZED (the workspace
+ * already holds them; no other flag is accepted).
+ * kpool_indexer_selection enqueues the selection + expansion of launch i's
+ * rows from the tile; it writes rows a0 .. a1-1 and b0 .. b1-1 of
+ * out_token_idx [T, W] (16-byte aligned) and, if not NULL, of out_pool_idx
+ * [T, K_sel]. Scoring then selection of every launch, in any launch order
+ * but each selection after its own scoring and before the next scoring,
+ * writes what kpool_indexer_topk writes. Arguments as for
+ * kpool_indexer_topk; both return KPOOL_E_INVALID for a launch index outside
+ * [0, count). */
+int32_t kpool_indexer_launches(const kpool_params* p, int32_t* info, int32_t max_launches);
+kpool_status kpool_indexer_scoring(const kpool_params* p, int32_t launch, const void* q,
+                                   const float* w, const void* pooled,
+                                   const int32_t* cu_seqlens, const int32_t* cu_pools,
+                                   void* workspace, size_t workspace_bytes, int32_t flags,
+                                   void* stream);
+kpool_status kpool_indexer_selection(const kpool_params* p, int32_t launch,
+                                     const int32_t* cu_seqlens, const int32_t* cu_pools,
+                                     const void* workspace, size_t workspace_bytes,
+                                     int32_t* out_token_idx, int32_t* out_pool_idx,
+                                     void* stream);
 
 /* Steps 2-4 in one kernel per query chunk, with the same arguments and the
  * same output as kpool_indexer_topk, bit for bit ([MLM] section 3 names a

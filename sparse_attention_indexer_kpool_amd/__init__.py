@@ -152,6 +152,12 @@ def lib() -> ctypes.CDLL:
         L.kpool_compress.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
         L.kpool_indexer_topk.restype = ctypes.c_int
         L.kpool_indexer_topk.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp]
+        L.kpool_indexer_launches.restype = i32
+        L.kpool_indexer_launches.argtypes = [P, vp, i32]
+        L.kpool_indexer_scoring.restype = ctypes.c_int
+        L.kpool_indexer_scoring.argtypes = [P, i32, vp, vp, vp, vp, vp, vp, sz, i32, vp]
+        L.kpool_indexer_selection.restype = ctypes.c_int
+        L.kpool_indexer_selection.argtypes = [P, i32, vp, vp, vp, sz, vp, vp, vp]
         L.kpool_fused_max_ksel.restype = ctypes.c_int32
         L.kpool_fused_max_ksel.argtypes = [P]
         L.kpool_fused_workspace_bytes.restype = sz
@@ -199,7 +205,8 @@ def lib() -> ctypes.CDLL:
 
 EXPORTS = ["kpool_abi_version", "kpool_workspace_bytes", "kpool_logits_ld",
            "kpool_query_chunk_rows", "kpool_compress",
-           "kpool_indexer_topk", "kpool_fused_max_ksel", "kpool_fused_workspace_bytes",
+           "kpool_indexer_topk", "kpool_indexer_launches", "kpool_indexer_scoring",
+           "kpool_indexer_selection", "kpool_fused_max_ksel", "kpool_fused_workspace_bytes",
            "kpool_indexer_topk_fused",
            "kpool_logits", "kpool_select", "kpool_select_expand",
            "kpool_expand",
@@ -259,6 +266,34 @@ def kpool_indexer_topk(p: Params, q, w, pooled, cu_seqlens, cu_pools, workspace,
     _check(lib().kpool_indexer_topk(ctypes.byref(p.c()), _ptr(q), _ptr(w), _ptr(pooled),
                                     _ptr(cu_seqlens), _ptr(cu_pools), _ptr(workspace), ws_bytes,
                                     _ptr(out_token_idx), _ptr(out_pool_idx), _stream(stream)))
+
+
+def kpool_indexer_launches(p: Params) -> list:
+    """The indexer's scoring launches: one (a0, a1, lda, b0, b1, ldb) tuple
+    each (rows a0..a1-1 at row stride lda, then rows b0..b1-1 at ldb)."""
+    n = int(lib().kpool_indexer_launches(ctypes.byref(p.c()), None, 0))
+    if n <= 0:
+        return []
+    info = (ctypes.c_int32 * (6 * n))()
+    lib().kpool_indexer_launches(ctypes.byref(p.c()), info, n)
+    return [tuple(int(x) for x in info[6 * i:6 * i + 6]) for i in range(n)]
+
+
+def kpool_indexer_scoring(p: Params, launch, q, w, pooled, cu_seqlens, cu_pools, workspace,
+                          flags=0, stream=None) -> None:
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().kpool_indexer_scoring(ctypes.byref(p.c()), int(launch), _ptr(q), _ptr(w),
+                                       _ptr(pooled), _ptr(cu_seqlens), _ptr(cu_pools),
+                                       _ptr(workspace), ws_bytes, int(flags), _stream(stream)))
+
+
+def kpool_indexer_selection(p: Params, launch, cu_seqlens, cu_pools, workspace, out_token_idx,
+                            out_pool_idx=None, stream=None) -> None:
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().kpool_indexer_selection(ctypes.byref(p.c()), int(launch), _ptr(cu_seqlens),
+                                         _ptr(cu_pools), _ptr(workspace), ws_bytes,
+                                         _ptr(out_token_idx), _ptr(out_pool_idx),
+                                         _stream(stream)))
 
 
 def kpool_fused_max_ksel(p: Params) -> int:

@@ -11,6 +11,7 @@
 #include <cstring>
 #include <mutex>
 #include <string>
+#include <vector>
 
 #include <rocprofiler-sdk-roctx/roctx.h>
 
@@ -131,6 +132,46 @@ kpool_status derive(const kpool_params* p, Derived* d, bool need_heads) {
   return KPOOL_OK;
 }
 
+// The indexer's scoring launches. Chunk c is query rows [c qc, min(T, (c + 1)
+// qc)); a row t has at most (t + 1) / kpool causal pools, so the chunk's
+// scores fit a row stride of min(max_pools, c1 / kpool) rounded up to 64.
+// Two chunks share a launch when both fit the logits tile (qc x ld floats)
+// at their own strides: the longest chunk left goes with the shortest, its
+// rows first. Each CU then takes a long and a short block and the dispatcher
+// evens them out, so whole blocks suffice (one start-up per block instead of
+// two pieces of a long block), and there are about half as many launches.
+// Every score is computed as in a launch of its own chunk.
+struct ChunkLaunch {
+  int c_long, c_short;             // chunk indices; c_short = -1: none
+  int64_t ld_long, ld_short;       // their tile row strides (floats)
+};
+
+int64_t chunk_ld(const Derived& d, int c) {
+  const int c1 = std::min(d.T, (c + 1) * d.qc);
+  const int bound = std::min(d.max_pools, c1 / d.kpool);
+  return (int64_t)round_up((size_t)std::max(bound, 1), 64);
+}
+
+std::vector<ChunkLaunch> chunk_plan(const Derived& d) {
+  std::vector<ChunkLaunch> plan;
+  if (d.T <= 0) return plan;
+  const int nch = (d.T + d.qc - 1) / d.qc;
+  const int64_t cap = (int64_t)d.qc * d.ld;
+  auto rows = [&](int c) { return (int64_t)(std::min(d.T, (c + 1) * d.qc) - c * d.qc); };
+  int lo = 0, hi = nch - 1;
+  while (lo <= hi) {
+    const int64_t ldh = chunk_ld(d, hi), ldl = chunk_ld(d, lo);
+    if (lo < hi && rows(hi) * ldh + rows(lo) * ldl <= cap) {
+      plan.push_back({hi, lo, ldh, ldl});
+      ++lo;
+    } else {
+      plan.push_back({hi, -1, ldh, 0});
+    }
+    --hi;
+  }
+  return plan;
+}
+
 kpool_status check_ptr(const void* ptr, size_t align, const char* name) {
   if (!ptr) return fail(KPOOL_E_INVALID, "%s is null", name);
   if (!aligned(ptr, align)) return fail(KPOOL_E_INVALID, "%s is not %zu-byte aligned", name, align);
@@ -166,15 +207,71 @@ kpool::LogitsArgs logits_args(const Derived& d, const void* q, const float* w, c
   return a;
 }
 
-void quantize_inputs(const Derived& d, const void* q, const void* pooled, const int32_t* cuP,
-                     int q_begin, int q_end, uint8_t* ws, hipStream_t st) {
+void quantize_q(const Derived& d, const void* q, int q_begin, int q_end, uint8_t* ws,
+                hipStream_t st) {
   const size_t qrow0 = (size_t)q_begin * d.H;
   const int qrows = (q_end - q_begin) * d.H;
+  if (qrows <= 0) return;
   kpool::launch_fp8_quantize(reinterpret_cast<const uint16_t*>(q) + qrow0 * 128, qrows, nullptr,
                              ws + d.off_qc + qrow0 * 128,
                              reinterpret_cast<float*>(ws + d.off_qs) + qrow0, st);
+}
+
+void quantize_inputs(const Derived& d, const void* q, const void* pooled, const int32_t* cuP,
+                     int q_begin, int q_end, uint8_t* ws, hipStream_t st) {
+  quantize_q(d, q, q_begin, q_end, ws, st);
   kpool::launch_fp8_quantize(reinterpret_cast<const uint16_t*>(pooled), d.T / d.kpool,
                              cuP + d.B, ws + d.off_kc, reinterpret_cast<float*>(ws + d.off_ks), st);
+}
+
+// The rows of one scoring launch of the indexer: range a at the start of the
+// tile, range b (possibly empty) right after a's rows.
+struct LaunchRows {
+  int a0, a1, b0, b1;
+  int64_t lda, ldb;
+};
+
+LaunchRows launch_rows(const Derived& d, const ChunkLaunch& L) {
+  LaunchRows R{};
+  R.a0 = L.c_long * d.qc;
+  R.a1 = std::min(d.T, R.a0 + d.qc);
+  R.lda = L.ld_long;
+  if (L.c_short >= 0) {
+    R.b0 = L.c_short * d.qc;
+    R.b1 = std::min(d.T, R.b0 + d.qc);
+    R.ldb = L.ld_short;
+  }
+  return R;
+}
+
+// The scoring kernel of one indexer launch into the workspace tile.
+void enqueue_scoring(const Derived& d, const LaunchRows& R, kpool::LogitsArgs a, uint8_t* ws,
+                     hipStream_t st) {
+  float* const tile = reinterpret_cast<float*>(ws + d.off_logits);
+  a.skip_select_all = 1;
+  a.q_begin = R.a0;
+  a.q_end = R.a1;
+  a.out = tile;
+  a.ld = R.lda;
+  a.q_begin2 = R.b0;
+  a.q_end2 = R.b1;
+  a.out2 = tile + (size_t)(R.a1 - R.a0) * R.lda;
+  a.ld2 = R.ldb;
+  kpool::launch_logits(a, st);
+}
+
+// The selection + expansion kernels of one indexer launch, from the tile.
+void enqueue_selection(const Derived& d, const LaunchRows& R, const uint8_t* ws,
+                       const int32_t* cu, const int32_t* cuP, int32_t* out_tok,
+                       int32_t* out_ids, hipStream_t st) {
+  const float* const tile = reinterpret_cast<const float*>(ws + d.off_logits);
+  auto select = [&](const float* scores, int64_t ld, int c0, int c1) {
+    kpool::launch_select(scores, ld, c0, c1, cu, cuP, d.B, d.T, d.kpool, d.k_sel, d.width,
+                         d.tail, d.max_pools, out_ids ? out_ids + (size_t)c0 * d.k_sel : nullptr,
+                         out_tok + (size_t)c0 * d.width, st);
+  };
+  select(tile, R.lda, R.a0, R.a1);
+  if (R.b1 > R.b0) select(tile + (size_t)(R.a1 - R.a0) * R.lda, R.ldb, R.b0, R.b1);
 }
 
 // Parameters of a decode call: num_docs = B sequences, max_seqlen bounds
@@ -310,23 +407,89 @@ kpool_status kpool_indexer_topk(const kpool_params* p, const void* q, const floa
     Range r("kpool.fp8_quantize");
     quantize_inputs(d, q, pooled, cu_pools, 0, d.T, ws, st);
   }
-  kpool::LogitsArgs a = logits_args(d, q, w, pooled, cu_seqlens, cu_pools, ws);
-  a.out = reinterpret_cast<float*>(ws + d.off_logits);
-  a.skip_select_all = 1;
-  for (int c0 = 0; c0 < d.T; c0 += d.qc) {
-    const int c1 = std::min(d.T, c0 + d.qc);
-    a.q_begin = c0;
-    a.q_end = c1;
+  const kpool::LogitsArgs a = logits_args(d, q, w, pooled, cu_seqlens, cu_pools, ws);
+  for (const ChunkLaunch& L : chunk_plan(d)) {
+    const LaunchRows R = launch_rows(d, L);
     {
       Range r("kpool.logits");
-      kpool::launch_logits(a, st);
+      enqueue_scoring(d, R, a, ws, st);
     }
     Range r("kpool.select_expand");
-    kpool::launch_select(a.out, d.ld, c0, c1, cu_seqlens, cu_pools, d.B, d.T, d.kpool, d.k_sel,
-                         d.width, d.tail, d.max_pools,
-                         out_pool_idx ? out_pool_idx + (size_t)c0 * d.k_sel : nullptr,
-                         out_token_idx + (size_t)c0 * d.width, st);
+    enqueue_selection(d, R, ws, cu_seqlens, cu_pools, out_token_idx, out_pool_idx, st);
   }
+  return after_launch();
+}
+
+int32_t kpool_indexer_launches(const kpool_params* p, int32_t* info, int32_t max_launches) {
+  Derived d;
+  if (derive(p, &d, true) != KPOOL_OK) return 0;
+  const std::vector<ChunkLaunch> plan = chunk_plan(d);
+  if (info) {
+    for (int i = 0; i < (int)plan.size() && i < max_launches; ++i) {
+      const LaunchRows R = launch_rows(d, plan[i]);
+      int32_t* o = info + 6 * (size_t)i;
+      o[0] = R.a0; o[1] = R.a1; o[2] = (int32_t)R.lda;
+      o[3] = R.b0; o[4] = R.b1; o[5] = (int32_t)R.ldb;
+    }
+  }
+  return (int32_t)plan.size();
+}
+
+kpool_status kpool_indexer_scoring(const kpool_params* p, int32_t launch, const void* q,
+                                   const float* w, const void* pooled,
+                                   const int32_t* cu_seqlens, const int32_t* cu_pools,
+                                   void* workspace, size_t workspace_bytes, int32_t flags,
+                                   void* stream) {
+  Derived d;
+  CHECK(derive(p, &d, true));
+  if (flags & ~KPOOL_LOGITS_INPUTS_QUANTIZED)
+    return fail(KPOOL_E_INVALID, "unknown scoring flags 0x%x", flags);
+  const std::vector<ChunkLaunch> plan = chunk_plan(d);
+  if (launch < 0 || launch >= (int)plan.size())
+    return fail(KPOOL_E_INVALID, "launch %d outside [0, %d)", launch, (int)plan.size());
+  CHECK(check_ptr(q, 16, "q"));
+  CHECK(check_ptr(w, 4, "w"));
+  CHECK(check_ptr(cu_seqlens, 4, "cu_seqlens"));
+  CHECK(check_ptr(cu_pools, 4, "cu_pools"));
+  if (d.T / d.kpool > 0) CHECK(check_ptr(pooled, 16, "pooled"));
+  CHECK(check_ptr(workspace, 256, "workspace"));
+  if (workspace_bytes < d.total)
+    return fail(KPOOL_E_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, d.total);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
+  const LaunchRows R = launch_rows(d, plan[launch]);
+  (void)hipGetLastError();
+  if (d.fp8 && !(flags & KPOOL_LOGITS_INPUTS_QUANTIZED)) {
+    quantize_inputs(d, q, pooled, cu_pools, R.a0, R.a1, ws, st);
+    quantize_q(d, q, R.b0, R.b1, ws, st);
+  }
+  Range r("kpool.logits");
+  enqueue_scoring(d, R, logits_args(d, q, w, pooled, cu_seqlens, cu_pools, ws), ws, st);
+  return after_launch();
+}
+
+kpool_status kpool_indexer_selection(const kpool_params* p, int32_t launch,
+                                     const int32_t* cu_seqlens, const int32_t* cu_pools,
+                                     const void* workspace, size_t workspace_bytes,
+                                     int32_t* out_token_idx, int32_t* out_pool_idx,
+                                     void* stream) {
+  Derived d;
+  CHECK(derive(p, &d, true));
+  const std::vector<ChunkLaunch> plan = chunk_plan(d);
+  if (launch < 0 || launch >= (int)plan.size())
+    return fail(KPOOL_E_INVALID, "launch %d outside [0, %d)", launch, (int)plan.size());
+  CHECK(check_ptr(cu_seqlens, 4, "cu_seqlens"));
+  CHECK(check_ptr(cu_pools, 4, "cu_pools"));
+  CHECK(check_ptr(out_token_idx, 16, "out_token_idx"));
+  if (out_pool_idx) CHECK(check_ptr(out_pool_idx, 4, "out_pool_idx"));
+  CHECK(check_ptr(workspace, 256, "workspace"));
+  if (workspace_bytes < d.total)
+    return fail(KPOOL_E_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, d.total);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  Range r("kpool.select_expand");
+  enqueue_selection(d, launch_rows(d, plan[launch]), reinterpret_cast<const uint8_t*>(workspace),
+                    cu_seqlens, cu_pools, out_token_idx, out_pool_idx, st);
   return after_launch();
 }
 

@@ -31,6 +31,13 @@ struct LogitsArgs {
   int q_begin, q_end;       // global query rows of this launch
   float* out;               // FP32 [q_end - q_begin, ld]
   int64_t ld;
+  // a second row range in the same launch, scored into out2 with row stride
+  // ld2 (none when q_end2 <= q_begin2; fill_masked covers the first range
+  // only). Its blocks are dispatched after the first range's, so the range
+  // with the longer rows goes first.
+  int q_begin2, q_end2;
+  float* out2;
+  int64_t ld2;
   int fill_masked;          // 1: write -inf in columns n_c .. ld-1
   int skip_select_all;      // 1: leave rows with n_c <= k_sel unwritten
   int fp8;

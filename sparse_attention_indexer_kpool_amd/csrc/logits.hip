@@ -364,14 +364,33 @@ __global__ __launch_bounds__(64 * kLogitsWaves) void logits_kernel(LogitsArgs a)
   // workgroups go to consecutive XCDs; the pieces of one block are 8 apart, so
   // they land on the same XCD at about the same time and read its q rows
   // through one L2. The largest blocks (latest queries, most causal pools)
-  // are dispatched first.
-  const int nqb = (a.q_end - a.q_begin + QPB - 1) / QPB;
-  const int grp = (int)blockIdx.x / (8 * a.pieces), r8 = (int)blockIdx.x % (8 * a.pieces);
-  const int piece = r8 / 8;
-  const int bi = grp * 8 + r8 % 8;
-  if (bi >= nqb) return;                     // padding of the last group
-  const int qblk = nqb - 1 - bi;
-  const int t0 = a.q_begin + qblk * QPB;
+  // are dispatched first: those of the first row range, then those of the
+  // second (a launch with two ranges puts the range with the longer rows
+  // first).
+  // Only the first range is split into pieces; the second range's blocks
+  // follow the first range's workgroups, one each.
+  const int nqb1 = (a.q_end - a.q_begin + QPB - 1) / QPB;
+  const int nqb2 = a.q_end2 > a.q_begin2 ? (a.q_end2 - a.q_begin2 + QPB - 1) / QPB : 0;
+  const int nwg1 = (nqb1 + 7) / 8 * 8 * a.pieces;
+  int bi, piece = 0, npieces = 1;
+  if ((int)blockIdx.x < nwg1) {
+    const int grp = (int)blockIdx.x / (8 * a.pieces), r8 = (int)blockIdx.x % (8 * a.pieces);
+    piece = r8 / 8;
+    npieces = a.pieces;
+    bi = grp * 8 + r8 % 8;
+    if (bi >= nqb1) return;                  // padding of the last group
+  } else {
+    bi = nqb1 + ((int)blockIdx.x - nwg1);
+    if (bi >= nqb1 + nqb2) return;
+  }
+  // this block's row range: its first row, its end, and where its scores go
+  const bool second = bi >= nqb1;
+  const int q_begin = second ? a.q_begin2 : a.q_begin;
+  const int q_end = second ? a.q_end2 : a.q_end;
+  float* const out_base = second ? a.out2 : a.out;
+  const int64_t ld = second ? a.ld2 : a.ld;
+  const int qblk = second ? nqb2 - 1 - (bi - nqb1) : nqb1 - 1 - bi;
+  const int t0 = q_begin + qblk * QPB;
   const uint8_t* keys = reinterpret_cast<const uint8_t*>(a.keys);
 
   // document, causal range and pool offset of each query: a few dependent
@@ -379,7 +398,7 @@ __global__ __launch_bounds__(64 * kLogitsWaves) void logits_kernel(LogitsArgs a)
   int my_doc = -1, my_nc = 0, my_pool0 = 0, my_start = 0;
   if (tid < QPB) {
     const int t = t0 + tid;
-    if (t < a.q_end) {
+    if (t < q_end) {
       const QueryInfo qi = query_info(a.cu, a.cu_pools, a.B, a.T, a.kpool, a.max_pools, t);
       my_doc = qi.doc;
       my_nc = qi.n_c;
@@ -423,8 +442,8 @@ __global__ __launch_bounds__(64 * kLogitsWaves) void logits_kernel(LogitsArgs a)
     DocWork d{run_nc[r], run_pool0[r], 0, 0};
     if (d.maxnc == 0 || (a.skip_select_all && d.maxnc <= a.k_sel)) return d;
     const int ntiles = (d.maxnc + kPoolTile - 1) / kPoolTile;
-    d.jt_lo = ntiles * piece / a.pieces;
-    d.jt_hi = ntiles * (piece + 1) / a.pieces;
+    d.jt_lo = ntiles * piece / npieces;
+    d.jt_hi = ntiles * (piece + 1) / npieces;
     return d;
   };
   int r_first = n_runs;
@@ -505,7 +524,7 @@ __global__ __launch_bounds__(64 * kLogitsWaves) void logits_kernel(LogitsArgs a)
                              a.k_scale, kscale_lds[0]);
   }
   {
-    const size_t row0 = (size_t)(t0 + wid * QPW) * H, row_last = (size_t)a.q_end * H - 1;
+    const size_t row0 = (size_t)(t0 + wid * QPW) * H, row_last = (size_t)q_end * H - 1;
     load_q_rows<H, D, FP8>(reinterpret_cast<const uint8_t*>(a.q), row0, row_last,
                            tile1 + wid * C::A_BYTES, lane);
     // the wave's 64 head weights (rows past the launch read row_last)
@@ -547,7 +566,7 @@ __global__ __launch_bounds__(64 * kLogitsWaves) void logits_kernel(LogitsArgs a)
       const float4 w4 = *reinterpret_cast<const float4*>(tile1 + W_OFF + (wid * 64 + fr) * 4);
       float4 s4 = make_float4(1.f, 1.f, 1.f, 1.f);
       if constexpr (FP8) s4 = *reinterpret_cast<const float4*>(tile1 + QS_OFF + (wid * 64 + fr) * 4);
-      const bool ok = t0 + wid * QPW + fr / H < a.q_end;   // the four rows share a query
+      const bool ok = t0 + wid * QPW + fr / H < q_end;   // the four rows share a query
       wq[mt][J * 4 + 0] = ok ? w4.x * a.scale * s4.x : 0.f;
       wq[mt][J * 4 + 1] = ok ? w4.y * a.scale * s4.y : 0.f;
       wq[mt][J * 4 + 2] = ok ? w4.z * a.scale * s4.z : 0.f;
@@ -556,7 +575,7 @@ __global__ __launch_bounds__(64 * kLogitsWaves) void logits_kernel(LogitsArgs a)
   }
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
-    const bool ok = t0 + wid * QPW + (mt * 32 + n) / H < a.q_end;
+    const bool ok = t0 + wid * QPW + (mt * 32 + n) / H < q_end;
     const uint8_t* blk = tile1 + wid * C::A_BYTES + mt * 32 * C::ROWB;
 #pragma unroll
     for (int s = 0; s < C::NSTEP; ++s) {
@@ -577,10 +596,10 @@ __global__ __launch_bounds__(64 * kLogitsWaves) void logits_kernel(LogitsArgs a)
 
   // ---- scores leave through a buffer resource over this workgroup's rows;
   // a masked lane stores at offset num_records, which the hardware drops
-  const int wg_rows = min(QPB, a.q_end - t0);
-  const uint32_t nrec = (uint32_t)((size_t)wg_rows * a.ld * 4);
+  const int wg_rows = min(QPB, q_end - t0);
+  const uint32_t nrec = (uint32_t)((size_t)wg_rows * ld * 4);
   const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
-      a.out + (size_t)(t0 - a.q_begin) * a.ld, 0, (int)nrec, 0x00020000);
+      out_base + (size_t)(t0 - q_begin) * ld, 0, (int)nrec, 0x00020000);
 
   for (int r = r_first; r < n_runs; ++r) {
     const DocWork dw = run_work(r);
@@ -595,7 +614,7 @@ __global__ __launch_bounds__(64 * kLogitsWaves) void logits_kernel(LogitsArgs a)
       const int qb = wid * QPW + S::query(k, g);
       const bool mine = q_doc[qb] == b && (H != 64 || g == 0);
       lim[k] = mine ? (uint32_t)q_nc[qb] : 0u;
-      roff[k] = (uint32_t)((size_t)qb * a.ld * 4);
+      roff[k] = (uint32_t)((size_t)qb * ld * 4);
     }
 
     // epilogue of one 32-pool unit whose first column is cbase (negative:
@@ -797,7 +816,7 @@ __global__ __launch_bounds__(64 * kLogitsWaves) void logits_kernel(LogitsArgs a)
     for (int qq = 0; qq < QPW; ++qq) {
       const int qb = wid * QPW + qq;
       const int t = t0 + qb;
-      if (t >= a.q_end) break;
+      if (t >= q_end) break;
       const int n_c = q_nc[qb];
       const int start = q_start[qb];
       const int n_sel = n_c < a.k_sel ? n_c : a.k_sel;
@@ -813,7 +832,7 @@ __global__ __launch_bounds__(64 * kLogitsWaves) void logits_kernel(LogitsArgs a)
           list_select<(SEL ? CAP : 64)>(lval + base, lidx + base, c, a.k_sel, 0, lane, kept);
       }
       const int tail = a.tail_on ? (t - start + 1) % a.kpool : 0;
-      const int row = t - a.q_begin;
+      const int row = t - q_begin;
       int32_t* otok = a.out_tok + (size_t)row * a.width;
       if (a.out_ids) {
         int32_t* oid = a.out_ids + (size_t)row * a.k_sel;
@@ -861,7 +880,8 @@ __global__ void fill_kernel(float* __restrict__ out, size_t count, float v) {
 template <int H, int D, bool FP8, bool SEL>
 static void launch_hdf(LogitsArgs a, hipStream_t st) {
   constexpr int QPB = LogitsCfg<H, D, FP8>::QPB;
-  const int rows = a.q_end - a.q_begin;
+  const int nqb1 = (a.q_end - a.q_begin + QPB - 1) / QPB;
+  const int nqb2 = a.q_end2 > a.q_begin2 ? (a.q_end2 - a.q_begin2 + QPB - 1) / QPB : 0;
   // Each query block is one workgroup of a CU, and its work grows with its
   // queries' causal range, so one workgroup per block leaves CUs idle while
   // the longest rows finish. Long rows are split into two pieces of the pool
@@ -871,11 +891,16 @@ static void launch_hdf(LogitsArgs a, hipStream_t st) {
   // context (16384 pools, BF16) it gains about 1 %, and it loses at 8192
   // pools on the FP8 path, whose sweep is half as long per pool. The fused
   // selection keeps each query's candidates in its workgroup, so it takes
-  // whole blocks.
+  // whole blocks. A launch of two row ranges (short rows after long ones)
+  // has its own mix of block sizes to balance with and takes whole blocks.
   const long sweep = (long)a.max_pools * (FP8 ? 1 : 2);
+#ifdef KPOOL_PAIR_PIECES
   a.pieces = (!SEL && sweep >= 32768) ? 2 : 1;
-  const int groups = ((rows + QPB - 1) / QPB + 7) / 8;
-  logits_kernel<H, D, FP8, SEL><<<groups * 8 * a.pieces, 64 * kLogitsWaves, 0, st>>>(a);
+#else
+  a.pieces = (!SEL && nqb2 == 0 && sweep >= 32768) ? 2 : 1;
+#endif
+  const int nwg = (nqb1 + 7) / 8 * 8 * a.pieces + nqb2;
+  logits_kernel<H, D, FP8, SEL><<<nwg, 64 * kLogitsWaves, 0, st>>>(a);
 }
 
 template <int D, bool FP8, bool SEL>
@@ -891,8 +916,8 @@ static void launch_df(const LogitsArgs& a, hipStream_t st) {
 
 void launch_logits(const LogitsArgs& a, hipStream_t st) {
   const int rows = a.q_end - a.q_begin;
-  if (rows <= 0) return;
-  if (a.fill_masked) {
+  if (rows <= 0 && a.q_end2 <= a.q_begin2) return;
+  if (a.fill_masked && rows > 0) {
     const size_t count = (size_t)rows * a.ld;
     const int blocks = (int)std::min<size_t>((count + 255) / 256, 8192);
     fill_kernel<<<blocks, 256, 0, st>>>(a.out, count, -INFINITY);

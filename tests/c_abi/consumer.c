@@ -56,6 +56,18 @@ int main(void) {
   CHECK(kpool_indexer_topk(&p, fake, (const float*)fake, fake, (const int32_t*)fake,
                            (const int32_t*)fake, fake, ws - 1, (int32_t*)fake, NULL, NULL) ==
         KPOOL_E_WORKSPACE);
+  {
+    /* the indexer's launches: nine at 64K with 4096-row chunks */
+    int32_t info[6 * 9];
+    CHECK(kpool_indexer_launches(&p, NULL, 0) == 9);
+    CHECK(kpool_indexer_launches(&p, info, 9) == 9);
+    CHECK(info[0] == 61440 && info[1] == 65536 && info[2] == 16384 && info[3] == info[4]);
+    CHECK(info[6 + 3] == 0 && info[6 + 4] == 4096 && info[6 + 5] == 1024);
+    CHECK(kpool_indexer_scoring(&p, 9, fake, (const float*)fake, fake, (const int32_t*)fake,
+                                (const int32_t*)fake, fake, ws, 0, NULL) == KPOOL_E_INVALID);
+    CHECK(kpool_indexer_selection(&p, -1, (const int32_t*)fake, (const int32_t*)fake, fake, ws,
+                                  (int32_t*)fake, NULL, NULL) == KPOOL_E_INVALID);
+  }
   CHECK(kpool_fp8_quantize(fake, -1, (uint8_t*)fake, (float*)fake, NULL) == KPOOL_E_INVALID);
   {
     kpool_mla_params mp;

@@ -6,6 +6,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 import sparse_attention_indexer_kpool_amd as kp
@@ -69,6 +70,52 @@ def test_workspace_and_ld():
     # unsupported or invalid parameters size to 0
     assert kp.kpool_workspace_bytes(P(num_heads=12)) == 0
     assert kp.kpool_workspace_bytes(P(max_seqlen=70000)) == 0
+
+
+def _check_plan(p):
+    """Every query row in exactly one range of one launch; each range's row
+    stride a multiple of 64 holding its rows' causal pools; the two ranges of
+    a launch fit the tile together; the first range has the longer rows."""
+    launches = kp.kpool_indexer_launches(p)
+    T, qc, ld = p.total_tokens, kp.kpool_query_chunk_rows(p), kp.kpool_logits_ld(p)
+    seen = np.zeros(T, np.int32)
+    for a0, a1, lda, b0, b1, ldb in launches:
+        assert 0 <= a0 < a1 <= T and a0 % qc == 0 and (a1 - a0 == qc or a1 == T)
+        assert lda % 64 == 0 and lda >= min(p.max_seqlen // p.kpool, a1 // p.kpool)
+        seen[a0:a1] += 1
+        used = (a1 - a0) * lda
+        if b1 > b0:
+            assert 0 <= b0 < b1 <= T and b0 % qc == 0 and b0 < a0
+            assert ldb % 64 == 0 and ldb >= min(p.max_seqlen // p.kpool, b1 // p.kpool)
+            assert ldb <= lda
+            seen[b0:b1] += 1
+            used += (b1 - b0) * ldb
+        else:
+            assert b0 == b1 == 0 and ldb == 0
+        assert used <= qc * ld
+    assert np.all(seen == 1)
+    return launches
+
+
+def test_indexer_launch_plan():
+    # 64K, 4096-row chunks: the last chunk alone, then seven pairs (chunk
+    # 14 - i with chunk i), then chunk 7 alone
+    L = _check_plan(P())
+    assert len(L) == 9
+    assert L[0] == (61440, 65536, 16384, 0, 0, 0)
+    assert L[1] == (57344, 61440, 15360, 0, 4096, 1024)
+    assert L[7] == (32768, 36864, 9216, 24576, 28672, 7168)
+    assert L[8] == (28672, 32768, 8192, 0, 0, 0)
+    assert len(_check_plan(P(use_fp8=1, total_tokens=32768, max_seqlen=32768))) == 5
+    # one chunk: one launch; a ragged last chunk; short documents; kpool 3
+    _check_plan(P(query_chunk=0))
+    assert len(_check_plan(P(total_tokens=4096, max_seqlen=4096, query_chunk=0))) == 1
+    _check_plan(P(total_tokens=20011, max_seqlen=20011, query_chunk=1500))
+    _check_plan(P(num_docs=8, total_tokens=19679, max_seqlen=3789, query_chunk=1000))
+    _check_plan(P(total_tokens=9001, max_seqlen=9001, kpool=3, index_topk=96, query_chunk=333))
+    _check_plan(P(total_tokens=5, max_seqlen=5, kpool=8, index_topk=64, query_chunk=2))
+    assert kp.kpool_indexer_launches(P(total_tokens=0, max_seqlen=0)) == []
+    assert kp.kpool_indexer_launches(P(num_heads=12)) == []
 
 
 def raw(name, *args):
@@ -152,6 +199,31 @@ def test_pointer_checks():
     assert raw("kpool_fp8_quantize", FAKE, 4, None, FAKE, None) == kp.KPOOL_E_INVALID
     # null params
     assert raw("kpool_indexer_topk", None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, FAKE, None, None) == kp.KPOOL_E_INVALID
+
+
+@raw_calls
+def test_staged_indexer_checks():
+    p = P()
+    ws = kp.kpool_workspace_bytes(p)
+    for i in (-1, 9, 1 << 30):
+        assert raw("kpool_indexer_scoring", pref(p), i, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, 0, None) == kp.KPOOL_E_INVALID
+        assert "launch" in kp.kpool_last_error()
+        assert raw("kpool_indexer_selection", pref(p), i, FAKE, FAKE, FAKE, ws, FAKE, None, None) == kp.KPOOL_E_INVALID
+        assert "launch" in kp.kpool_last_error()
+    # flags other than KPOOL_LOGITS_INPUTS_QUANTIZED
+    for f in (kp.KPOOL_LOGITS_FILL_MASKED, kp.KPOOL_LOGITS_SKIP_ALL_SELECTED, 8):
+        assert raw("kpool_indexer_scoring", pref(p), 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, f, None) == kp.KPOOL_E_INVALID
+        assert "flags" in kp.kpool_last_error()
+    # workspace too small, null or misaligned pointers
+    assert raw("kpool_indexer_scoring", pref(p), 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws - 1, 0, None) == kp.KPOOL_E_WORKSPACE
+    assert raw("kpool_indexer_scoring", pref(p), 0, None, FAKE, FAKE, FAKE, FAKE, FAKE, ws, 0, None) == kp.KPOOL_E_INVALID
+    assert raw("kpool_indexer_selection", pref(p), 0, FAKE, FAKE, FAKE, ws - 1, FAKE, None, None) == kp.KPOOL_E_WORKSPACE
+    assert raw("kpool_indexer_selection", pref(p), 0, FAKE, FAKE, FAKE, ws, FAKE + 4, None, None) == kp.KPOOL_E_INVALID
+    assert "out_token_idx" in kp.kpool_last_error()
+    assert raw("kpool_indexer_selection", pref(p), 0, FAKE, FAKE, FAKE + 16, ws, FAKE, None, None) == kp.KPOOL_E_INVALID
+    # T = 0: no launches, so every index is out of range
+    p0 = P(total_tokens=0, max_seqlen=0)
+    assert raw("kpool_indexer_scoring", pref(p0), 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 0, None) == kp.KPOOL_E_INVALID
 
 
 @raw_calls
