@@ -894,11 +894,7 @@ static void launch_hdf(LogitsArgs a, hipStream_t st) {
   // whole blocks. A launch of two row ranges (short rows after long ones)
   // has its own mix of block sizes to balance with and takes whole blocks.
   const long sweep = (long)a.max_pools * (FP8 ? 1 : 2);
-#ifdef KPOOL_PAIR_PIECES
-  a.pieces = (!SEL && sweep >= 32768) ? 2 : 1;
-#else
   a.pieces = (!SEL && nqb2 == 0 && sweep >= 32768) ? 2 : 1;
-#endif
   const int nwg = (nqb1 + 7) / 8 * 8 * a.pieces + nqb2;
   logits_kernel<H, D, FP8, SEL><<<nwg, 64 * kLogitsWaves, 0, st>>>(a);
 }
