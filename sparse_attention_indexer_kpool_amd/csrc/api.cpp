@@ -270,8 +270,12 @@ void enqueue_selection(const Derived& d, const LaunchRows& R, const uint8_t* ws,
                          d.tail, d.max_pools, out_ids ? out_ids + (size_t)c0 * d.k_sel : nullptr,
                          out_tok + (size_t)c0 * d.width, st);
   };
-  select(tile, R.lda, R.a0, R.a1);
-  if (R.b1 > R.b0) select(tile + (size_t)(R.a1 - R.a0) * R.lda, R.ldb, R.b0, R.b1);
+  if (R.b1 > R.b0)
+    kpool::launch_select2(tile, R.lda, R.a0, R.a1, tile + (size_t)(R.a1 - R.a0) * R.lda, R.ldb,
+                          R.b0, R.b1, cu, cuP, d.B, d.T, d.kpool, d.k_sel, d.width, d.tail,
+                          d.max_pools, out_ids, out_tok, st);
+  else
+    select(tile, R.lda, R.a0, R.a1);
 }
 
 // Parameters of a decode call: num_docs = B sequences, max_seqlen bounds

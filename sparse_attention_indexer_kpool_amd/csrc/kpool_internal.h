@@ -67,6 +67,14 @@ void launch_select(const float* logits, int64_t ld, int q_begin, int q_end,
                    int k_sel, int width, int tail_on, int max_pools, int32_t* out_ids,
                    int32_t* out_tok, hipStream_t st);
 
+// The same on two row ranges in one launch (out_ids / out_tok indexed by the
+// global row t).
+void launch_select2(const float* logits, int64_t ld, int q_begin, int q_end,
+                    const float* logits2, int64_t ld2, int q_begin2, int q_end2,
+                    const int32_t* cu, const int32_t* cu_pools, int B, int T, int kpool,
+                    int k_sel, int width, int tail_on, int max_pools, int32_t* out_ids,
+                    int32_t* out_tok, hipStream_t st);
+
 void launch_expand(const int32_t* pool_ids, int q_begin, int q_end, const int32_t* cu,
                    const int32_t* cu_pools, int B, int T, int kpool, int k_sel, int width,
                    int tail, int max_pools, int32_t* out, hipStream_t st);

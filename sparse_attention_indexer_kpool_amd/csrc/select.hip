@@ -11,8 +11,10 @@
 // selector as the production alternative to a full sort; this kernel is an
 // exact selection written for gfx950.
 //
-// One workgroup per query row; HBM-bound: each causal score is read once with
-// coalesced 16-byte loads and stays in registers. Selection order: larger
+// One workgroup per query row (a launch may cover two row ranges, each with
+// its own scores and row stride: the indexer selects both chunks of a
+// two-chunk scoring launch at once); HBM-bound: each causal score is read
+// once with coalesced 16-byte loads and stays in registers. Selection order: larger
 // score first, equal scores to the lower pool index, NaN ranks as -inf.
 //
 //   1. The row is loaded (slots past n_c hold NaN).
@@ -135,6 +137,12 @@ struct SelectArgs {
   int B, T, kpool, k_sel, width, tail_on, max_pools, list_cap;
   int32_t* out_ids;     // [rows, K_sel] global pool ids, or null
   int32_t* out_tok;     // [rows, width] token ids with the tail, or null
+  // a second row range after the first (none when q_end2 <= q_begin2)
+  const float* logits2;
+  int64_t ld2;
+  int q_begin2, q_end2;
+  int32_t* out_ids2;
+  int32_t* out_tok2;
   // decode rows (dec_len not null): row r is the last token of a sequence of
   // dec_len[r] tokens whose pools start at row dec_pool0[r] and whose token
   // ids start at dec_base[r] (0 when dec_base is null)
@@ -164,23 +172,27 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
   __shared__ Sh sh;
   extern __shared__ __attribute__((aligned(16))) uint8_t dyn[];
   uint2* list = reinterpret_cast<uint2*>(dyn);      // list_cap (value bits, index) pairs
-  const float* __restrict__ logits = a.logits;
-  const int64_t ld = a.ld;
+  const int rows1 = a.q_end - a.q_begin;
+  const bool second = (int)blockIdx.x >= rows1;
+  const float* __restrict__ logits = second ? a.logits2 : a.logits;
+  const int64_t ld = second ? a.ld2 : a.ld;
   const int k_sel = a.k_sel, kpool = a.kpool, list_cap = a.list_cap;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wid = tid >> 6;
-  const int r = blockIdx.x;
-  const int t = a.q_begin + r;
-  if (t >= a.q_end) return;
+  const int r = second ? (int)blockIdx.x - rows1 : (int)blockIdx.x;
+  const int t = (second ? a.q_begin2 : a.q_begin) + r;
+  if (t >= (second ? a.q_end2 : a.q_end)) return;
   const QueryInfo qi = a.dec_len ? decode_info(a, r)
                                  : query_info(a.cu, a.cu_pools, a.B, a.T, kpool, a.max_pools, t);
   const int n_c = qi.n_c;
   const int n_sel = n_c < k_sel ? n_c : k_sel;
   const int tail = a.tail_on ? (qi.i + 1) % kpool : 0;
   const int tail_base = qi.start + n_c * kpool;
-  int32_t* oid = a.out_ids ? a.out_ids + (size_t)r * k_sel : nullptr;
-  int32_t* otok = a.out_tok ? a.out_tok + (size_t)r * a.width : nullptr;
+  int32_t* const ids_base = second ? a.out_ids2 : a.out_ids;
+  int32_t* const tok_base = second ? a.out_tok2 : a.out_tok;
+  int32_t* oid = ids_base ? ids_base + (size_t)r * k_sel : nullptr;
+  int32_t* otok = tok_base ? tok_base + (size_t)r * a.width : nullptr;
 
   // token slots from n_sel * kpool on: the tail tokens, then -1
   auto write_tail = [&]() {
@@ -596,9 +608,9 @@ static void launch_sel(SelectArgs a, hipStream_t st) {
   a.list_cap = list_capacity(NT, G);
   const size_t lds = (size_t)a.list_cap * 8;
   if (a.kpool == 4 && (a.width & 3) == 0)
-    select_kernel<NT, G, true><<<a.q_end - a.q_begin, NT, lds, st>>>(a);
+    select_kernel<NT, G, true><<<(a.q_end - a.q_begin) + max(a.q_end2 - a.q_begin2, 0), NT, lds, st>>>(a);
   else
-    select_kernel<NT, G, false><<<a.q_end - a.q_begin, NT, lds, st>>>(a);
+    select_kernel<NT, G, false><<<(a.q_end - a.q_begin) + max(a.q_end2 - a.q_begin2, 0), NT, lds, st>>>(a);
 }
 
 static void launch_select_args(SelectArgs& a, hipStream_t st) {
@@ -641,6 +653,39 @@ void launch_select(const float* logits, int64_t ld, int q_begin, int q_end,
   a.max_pools = max_pools;
   a.out_ids = out_ids;
   a.out_tok = out_tok;
+  launch_select_args(a, st);
+}
+
+void launch_select2(const float* logits, int64_t ld, int q_begin, int q_end,
+                    const float* logits2, int64_t ld2, int q_begin2, int q_end2,
+                    const int32_t* cu, const int32_t* cu_pools, int B, int T, int kpool,
+                    int k_sel, int width, int tail_on, int max_pools, int32_t* out_ids,
+                    int32_t* out_tok, hipStream_t st) {
+  if (q_end <= q_begin) return;
+  SelectArgs a{};
+  a.logits = logits;
+  a.ld = ld;
+  a.q_begin = q_begin;
+  a.q_end = q_end;
+  a.logits2 = logits2;
+  a.ld2 = ld2;
+  a.q_begin2 = q_begin2;
+  a.q_end2 = q_end2;
+  a.cu = cu;
+  a.cu_pools = cu_pools;
+  a.B = B;
+  a.T = T;
+  a.kpool = kpool;
+  a.k_sel = k_sel;
+  a.width = width;
+  a.tail_on = tail_on;
+  const int bound = max(q_end, q_end2) / kpool;
+  if (bound < max_pools) max_pools = bound < 1 ? 1 : bound;
+  a.max_pools = max_pools;
+  a.out_ids = out_ids ? out_ids + (size_t)q_begin * k_sel : nullptr;
+  a.out_tok = out_tok + (size_t)q_begin * width;
+  a.out_ids2 = out_ids ? out_ids + (size_t)q_begin2 * k_sel : nullptr;
+  a.out_tok2 = out_tok + (size_t)q_begin2 * width;
   launch_select_args(a, st);
 }
 
