@@ -11,7 +11,6 @@
 #include <cstring>
 #include <mutex>
 #include <string>
-#include <vector>
 
 #include <rocprofiler-sdk-roctx/roctx.h>
 
@@ -146,30 +145,55 @@ struct ChunkLaunch {
   int64_t ld_long, ld_short;       // their tile row strides (floats)
 };
 
-int64_t chunk_ld(const Derived& d, int c) {
-  const int c1 = std::min(d.T, (c + 1) * d.qc);
-  const int bound = std::min(d.max_pools, c1 / d.kpool);
-  return (int64_t)round_up((size_t)std::max(bound, 1), 64);
+// first row and row count of chunk c (64-bit: T and the chunk may both be
+// close to 2^31)
+int64_t chunk_begin(const Derived& d, int c) { return (int64_t)c * d.qc; }
+int64_t chunk_rows(const Derived& d, int c) {
+  return std::min<int64_t>(d.T, chunk_begin(d, c) + d.qc) - chunk_begin(d, c);
 }
 
-std::vector<ChunkLaunch> chunk_plan(const Derived& d) {
-  std::vector<ChunkLaunch> plan;
-  if (d.T <= 0) return plan;
-  const int nch = (d.T + d.qc - 1) / d.qc;
-  const int64_t cap = (int64_t)d.qc * d.ld;
-  auto rows = [&](int c) { return (int64_t)(std::min(d.T, (c + 1) * d.qc) - c * d.qc); };
-  int lo = 0, hi = nch - 1;
-  while (lo <= hi) {
+int64_t chunk_ld(const Derived& d, int c) {
+  const int64_t c1 = chunk_begin(d, c) + chunk_rows(d, c);
+  const int64_t bound = std::min<int64_t>(d.max_pools, c1 / d.kpool);
+  return (int64_t)round_up((size_t)std::max<int64_t>(bound, 1), 64);
+}
+
+// The plan is walked, never stored (a batch of 2^31 tokens in 1-row chunks
+// has 2^31 launches): each step takes the longest chunk left and, when it
+// fits, the shortest.
+struct PlanWalk {
+  int lo, hi;
+  explicit PlanWalk(const Derived& d) : lo(0), hi(d.T > 0 ? (int)((d.T - 1) / d.qc) : -1) {}
+  bool next(const Derived& d, ChunkLaunch& L) {
+    if (lo > hi) return false;
+    const int64_t cap = (int64_t)d.qc * d.ld;
     const int64_t ldh = chunk_ld(d, hi), ldl = chunk_ld(d, lo);
-    if (lo < hi && rows(hi) * ldh + rows(lo) * ldl <= cap) {
-      plan.push_back({hi, lo, ldh, ldl});
+    if (lo < hi && chunk_rows(d, hi) * ldh + chunk_rows(d, lo) * ldl <= cap) {
+      L = ChunkLaunch{hi, lo, ldh, ldl};
       ++lo;
     } else {
-      plan.push_back({hi, -1, ldh, 0});
+      L = ChunkLaunch{hi, -1, ldh, 0};
     }
     --hi;
+    return true;
   }
-  return plan;
+};
+
+int64_t plan_count(const Derived& d) {
+  PlanWalk w(d);
+  ChunkLaunch L;
+  int64_t n = 0;
+  while (w.next(d, L)) ++n;
+  return n;
+}
+
+// launch i of the plan (0 <= i < plan_count(d))
+ChunkLaunch plan_at(const Derived& d, int64_t i) {
+  PlanWalk w(d);
+  ChunkLaunch L{};
+  for (int64_t k = 0; k <= i && w.next(d, L); ++k) {
+  }
+  return L;
 }
 
 kpool_status check_ptr(const void* ptr, size_t align, const char* name) {
@@ -233,12 +257,12 @@ struct LaunchRows {
 
 LaunchRows launch_rows(const Derived& d, const ChunkLaunch& L) {
   LaunchRows R{};
-  R.a0 = L.c_long * d.qc;
-  R.a1 = std::min(d.T, R.a0 + d.qc);
+  R.a0 = (int)chunk_begin(d, L.c_long);
+  R.a1 = (int)(chunk_begin(d, L.c_long) + chunk_rows(d, L.c_long));
   R.lda = L.ld_long;
   if (L.c_short >= 0) {
-    R.b0 = L.c_short * d.qc;
-    R.b1 = std::min(d.T, R.b0 + d.qc);
+    R.b0 = (int)chunk_begin(d, L.c_short);
+    R.b1 = (int)(chunk_begin(d, L.c_short) + chunk_rows(d, L.c_short));
     R.ldb = L.ld_short;
   }
   return R;
@@ -412,7 +436,9 @@ kpool_status kpool_indexer_topk(const kpool_params* p, const void* q, const floa
     quantize_inputs(d, q, pooled, cu_pools, 0, d.T, ws, st);
   }
   const kpool::LogitsArgs a = logits_args(d, q, w, pooled, cu_seqlens, cu_pools, ws);
-  for (const ChunkLaunch& L : chunk_plan(d)) {
+  PlanWalk walk(d);
+  ChunkLaunch L;
+  while (walk.next(d, L)) {
     const LaunchRows R = launch_rows(d, L);
     {
       Range r("kpool.logits");
@@ -427,16 +453,19 @@ kpool_status kpool_indexer_topk(const kpool_params* p, const void* q, const floa
 int32_t kpool_indexer_launches(const kpool_params* p, int32_t* info, int32_t max_launches) {
   Derived d;
   if (derive(p, &d, true) != KPOOL_OK) return 0;
-  const std::vector<ChunkLaunch> plan = chunk_plan(d);
-  if (info) {
-    for (int i = 0; i < (int)plan.size() && i < max_launches; ++i) {
-      const LaunchRows R = launch_rows(d, plan[i]);
-      int32_t* o = info + 6 * (size_t)i;
+  PlanWalk walk(d);
+  ChunkLaunch L;
+  int64_t n = 0;
+  while (walk.next(d, L)) {
+    if (info && n < max_launches) {
+      const LaunchRows R = launch_rows(d, L);
+      int32_t* o = info + 6 * (size_t)n;
       o[0] = R.a0; o[1] = R.a1; o[2] = (int32_t)R.lda;
       o[3] = R.b0; o[4] = R.b1; o[5] = (int32_t)R.ldb;
     }
+    ++n;
   }
-  return (int32_t)plan.size();
+  return (int32_t)std::min<int64_t>(n, 0x7fffffff);
 }
 
 kpool_status kpool_indexer_scoring(const kpool_params* p, int32_t launch, const void* q,
@@ -448,9 +477,9 @@ kpool_status kpool_indexer_scoring(const kpool_params* p, int32_t launch, const 
   CHECK(derive(p, &d, true));
   if (flags & ~KPOOL_LOGITS_INPUTS_QUANTIZED)
     return fail(KPOOL_E_INVALID, "unknown scoring flags 0x%x", flags);
-  const std::vector<ChunkLaunch> plan = chunk_plan(d);
-  if (launch < 0 || launch >= (int)plan.size())
-    return fail(KPOOL_E_INVALID, "launch %d outside [0, %d)", launch, (int)plan.size());
+  const int64_t nl = plan_count(d);
+  if (launch < 0 || launch >= nl)
+    return fail(KPOOL_E_INVALID, "launch %d outside [0, %lld)", launch, (long long)nl);
   CHECK(check_ptr(q, 16, "q"));
   CHECK(check_ptr(w, 4, "w"));
   CHECK(check_ptr(cu_seqlens, 4, "cu_seqlens"));
@@ -461,7 +490,7 @@ kpool_status kpool_indexer_scoring(const kpool_params* p, int32_t launch, const 
     return fail(KPOOL_E_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, d.total);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
-  const LaunchRows R = launch_rows(d, plan[launch]);
+  const LaunchRows R = launch_rows(d, plan_at(d, launch));
   (void)hipGetLastError();
   if (d.fp8 && !(flags & KPOOL_LOGITS_INPUTS_QUANTIZED)) {
     quantize_inputs(d, q, pooled, cu_pools, R.a0, R.a1, ws, st);
@@ -479,9 +508,9 @@ kpool_status kpool_indexer_selection(const kpool_params* p, int32_t launch,
                                      void* stream) {
   Derived d;
   CHECK(derive(p, &d, true));
-  const std::vector<ChunkLaunch> plan = chunk_plan(d);
-  if (launch < 0 || launch >= (int)plan.size())
-    return fail(KPOOL_E_INVALID, "launch %d outside [0, %d)", launch, (int)plan.size());
+  const int64_t nl = plan_count(d);
+  if (launch < 0 || launch >= nl)
+    return fail(KPOOL_E_INVALID, "launch %d outside [0, %lld)", launch, (long long)nl);
   CHECK(check_ptr(cu_seqlens, 4, "cu_seqlens"));
   CHECK(check_ptr(cu_pools, 4, "cu_pools"));
   CHECK(check_ptr(out_token_idx, 16, "out_token_idx"));
@@ -492,7 +521,7 @@ kpool_status kpool_indexer_selection(const kpool_params* p, int32_t launch,
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   Range r("kpool.select_expand");
-  enqueue_selection(d, launch_rows(d, plan[launch]), reinterpret_cast<const uint8_t*>(workspace),
+  enqueue_selection(d, launch_rows(d, plan_at(d, launch)), reinterpret_cast<const uint8_t*>(workspace),
                     cu_seqlens, cu_pools, out_token_idx, out_pool_idx, st);
   return after_launch();
 }
@@ -535,12 +564,12 @@ kpool_status kpool_indexer_topk_fused(const kpool_params* p, const void* q, cons
   a.skip_select_all = 1;
   a.width = d.width;
   a.tail_on = d.tail;
-  // one launch per query chunk, as the two-kernel path; nothing but the
-  // token rows (and pool ids) is written
-  for (int c0 = 0; c0 < d.T; c0 += d.qc) {
-    const int c1 = std::min(d.T, c0 + d.qc);
-    a.q_begin = c0;
-    a.q_end = c1;
+  // one launch per query chunk (no tile, so no two-chunk launches); nothing
+  // but the token rows (and pool ids) is written
+  for (int64_t c0 = 0; c0 < d.T; c0 += d.qc) {
+    const int64_t c1 = std::min<int64_t>(d.T, c0 + d.qc);
+    a.q_begin = (int)c0;
+    a.q_end = (int)c1;
     a.out_tok = out_token_idx + (size_t)c0 * d.width;
     a.out_ids = out_pool_idx ? out_pool_idx + (size_t)c0 * d.k_sel : nullptr;
     kpool::launch_logits_select(a, st);

@@ -103,6 +103,37 @@ int main() {
   EXPECT(kpool_indexer_topk_fused(&f, F, Ff, F, Fi, Fi, nullptr, 0, Fo, nullptr, nullptr),
          KPOOL_E_UNSUPPORTED);
 
+  // the indexer's launch plan (host arithmetic only) and its staged entry
+  // points' checks; chunk bounds near 2^31 must not overflow
+  {
+    int32_t info[6 * 9];
+    if (kpool_indexer_launches(&p, info, 9) != 9 || info[0] != 61440 || info[2] != 16384 ||
+        info[6 + 4] != 4096) {
+      std::fprintf(stderr, "64K plan\n");
+      ++failures;
+    }
+    kpool_params huge = base();
+    huge.total_tokens = 0x7fffffff;
+    huge.max_seqlen = 4 * 65536;
+    huge.query_chunk = (1 << 30) + 1;          // the second chunk ends past 2^31
+    int32_t hi[12];
+    if (kpool_indexer_launches(&huge, hi, 2) != 2 || hi[1] != 0x7fffffff || hi[6] != 0 ||
+        hi[7] != (1 << 30) + 1) {
+      std::fprintf(stderr, "plan near 2^31\n");
+      ++failures;
+    }
+    EXPECT(kpool_indexer_scoring(&p, 9, F, Ff, F, Fi, Fi, F, ws, 0, nullptr), KPOOL_E_INVALID);
+    EXPECT(kpool_indexer_scoring(&p, -1, F, Ff, F, Fi, Fi, F, ws, 0, nullptr), KPOOL_E_INVALID);
+    EXPECT(kpool_indexer_scoring(&p, 0, F, Ff, F, Fi, Fi, F, ws, 1, nullptr), KPOOL_E_INVALID);
+    EXPECT(kpool_indexer_scoring(&p, 0, F, Ff, F, Fi, Fi, F, ws - 1, 0, nullptr),
+           KPOOL_E_WORKSPACE);
+    EXPECT(kpool_indexer_selection(&p, 9, Fi, Fi, F, ws, Fo, nullptr, nullptr), KPOOL_E_INVALID);
+    EXPECT(kpool_indexer_selection(&p, 0, Fi, Fi, F, ws, reinterpret_cast<int32_t*>(M), nullptr,
+                                   nullptr),
+           KPOOL_E_INVALID);
+    EXPECT(kpool_indexer_scoring(&huge, 2, F, Ff, F, Fi, Fi, F, ws, 0, nullptr), KPOOL_E_INVALID);
+  }
+
   // serving entry points
   kpool_params d = base();
   d.num_docs = 64;
