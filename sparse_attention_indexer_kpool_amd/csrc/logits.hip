@@ -785,9 +785,15 @@ __global__ __launch_bounds__(64 * kLogitsWaves) void logits_kernel(LogitsArgs a)
         if (pending == stepno) shrink_wave();         // every wave at the same step
         pending = s_req[stepno & 1];
       }
+      // FP8: a wave still in the step's first unit outranks one in the
+      // second, so the two waves of a SIMD reach the next barrier closer
+      // together (measured: -4 % per FP8 step; the BF16 path is 2-4 %
+      // slower with either order, so it keeps equal priority)
+      if constexpr (FP8 && !SEL) __builtin_amdgcn_s_setprio(1);
       mma(accA, tb, 0);
       epilogue(accB, prev, ks_prev);
       interleave();
+      if constexpr (FP8 && !SEL) __builtin_amdgcn_s_setprio(0);
       mma(accB, tb, 1);
       epilogue(accA, j0, ks0);
       interleave();
