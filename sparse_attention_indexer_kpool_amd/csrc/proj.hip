@@ -182,8 +182,15 @@ __global__ __launch_bounds__(kGemmThreads) void proj_gemm_kernel(GemmArgs g) {
                                                      Bs + (wn * 64 + j * 32) * 128 + off[s]));
     };
     rd(0, 0);
+    // falling wave priority over the K step's sub-steps: a wave behind the
+    // other wave of its SIMD outranks it, so both reach the next barrier
+    // together (measured: -4 % for the projections)
+    __builtin_amdgcn_s_setprio(3);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
+      if (s == 1) __builtin_amdgcn_s_setprio(2);
+      if (s == 2) __builtin_amdgcn_s_setprio(1);
+      if (s == 3) __builtin_amdgcn_s_setprio(0);
       if (s + 1 < 4) rd(s + 1, (s + 1) & 1);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
@@ -409,8 +416,15 @@ __global__ __launch_bounds__(kWThreads) void proj_gemm_wide_kernel(WideArgs g) {
                                                      Bs + (wn * 64 + j * 32) * 128 + off[s]));
     };
     rd(0, 0);
+    // falling wave priority over the K step's sub-steps: a wave behind the
+    // other wave of its SIMD outranks it, so both reach the next barrier
+    // together (measured: -4 % for the projections)
+    __builtin_amdgcn_s_setprio(3);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
+      if (s == 1) __builtin_amdgcn_s_setprio(2);
+      if (s == 2) __builtin_amdgcn_s_setprio(1);
+      if (s == 3) __builtin_amdgcn_s_setprio(0);
       if (s + 1 < 4) rd(s + 1, (s + 1) & 1);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
