@@ -74,21 +74,32 @@ def _n_c(inp, rows):
     return (rows - cu[b] + 1) // inp.wl.kpool
 
 
-@pytest.mark.parametrize("wl", [c for c in CASES if not c.fp8], ids=lambda w: w.name)
+def _tile_offset(p, T):
+    """Byte offset of the logits tile in the workspace: after the FP8 codes
+    and row scales of q and of the pooled keys (each piece 256-byte aligned)
+    on the FP8 path, at 0 otherwise (the layout include/kpool.h states)."""
+    if not p.use_fp8:
+        return 0
+    up = lambda x: (x + 255) // 256 * 256
+    qrows, krows = T * p.num_heads, T // p.kpool
+    return up(up(up(up(qrows * 128) + qrows * 4) + krows * 128) + krows * 4)
+
+
+@pytest.mark.parametrize("wl", CASES, ids=lambda w: w.name)
 def test_two_chunk_launch_scores_match_single_chunk(wl):
     d = dev(wl)
     p, inp = d.p, d.inp
-    assert not p.use_fp8          # the tile starts the workspace (no FP8 codes before it)
     launches = kp.kpool_indexer_launches(p)
     two = [i for i, x in enumerate(launches) if x[4] > x[3]]
     assert two, "the case must have a launch of two chunks"
     ws = d.workspace()
     for i in two:
         a0, a1, lda, b0, b1, ldb = launches[i]
-        ws.fill_(0x7F)
+        off0 = _tile_offset(p, inp.T)
+        ws[off0:].fill_(0x7F)
         kp.kpool_indexer_scoring(p, i, d.q, d.w, d.pooled, d.cu, d.cu_pools, ws)
         torch.cuda.synchronize()
-        tile = ws.view(torch.float32)
+        tile = ws[off0:].view(torch.float32)
         for (r0, r1, ld, off) in ((a0, a1, lda, 0), (b0, b1, ldb, (a1 - a0) * lda)):
             got = tile[off:off + (r1 - r0) * ld].view(r1 - r0, ld).cpu().numpy()
             ref = d.logits(r0, r1).cpu().numpy()
