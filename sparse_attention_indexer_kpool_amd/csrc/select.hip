@@ -38,6 +38,13 @@
 //      are asked for, its kpool token ids (one 16-byte store for kpool = 4);
 //      the tail tokens and the -1 padding follow.
 //
+// Short rows (at most three float4 groups per thread, 3072 pools with 256
+// threads) skip steps 2 and 3: every value is its own list entry, held in
+// registers, and one histogram of the whole row takes the place of the
+// sample's and the list's, so the row crosses seven workgroup barriers
+// instead of eleven (64K step: selection 0.68 -> 0.64 ms; allowing four
+// groups measured the same, six and eight slower).
+//
 // General path (non-finite or constant rows, an unlucky sample): repeated
 // histogram rounds over order-preserving 32-bit keys (NaN -> -inf, -0 -> +0),
 // bins a right shift of key - min, then over the pool index once all
@@ -126,6 +133,148 @@ __device__ __forceinline__ void find_bin(SelectShared<NT, G>& sh, int k) {
 // returns the non-NaN operand).
 __device__ __forceinline__ int vbin(float x, float lo, float inv) {
   return (int)fminf(fmaxf((x - lo) * inv, 0.f), (float)(kBins - 1));
+}
+
+// The threshold element among the c_in candidates of bin b* (sh.cand_key,
+// sh.cand_idx): the one of rank k_in - 1 by larger key first, equal keys to
+// the lower index. Every wave ranks the few candidates itself (lane l takes
+// candidates l, l + 64, ...), so the result needs no barrier to reach the
+// other waves. Returns (key, index).
+template <int NT, int G>
+__device__ __forceinline__ uint2 threshold_of(const SelectShared<NT, G>& sh, int c_in, int k_in,
+                                             int lane) {
+  uint32_t tk = 0u;
+  int ti = 0;
+  for (int c0 = 0; c0 < c_in; c0 += 64) {
+    const int ci = c0 + lane;
+    bool hit = false;
+    uint32_t mk = 0u;
+    int mi = 0;
+    if (ci < c_in) {
+      mk = sh.cand_key[ci];
+      mi = sh.cand_idx[ci];
+      int rank = 0;
+      for (int q = 0; q < c_in; ++q) {
+        const uint32_t okey = sh.cand_key[q];
+        rank += (okey > mk) || (okey == mk && sh.cand_idx[q] < mi);
+      }
+      hit = rank == k_in - 1;
+    }
+    const uint64_t hm = __ballot(hit);
+    if (hm) {
+      const int src = __ffsll((unsigned long long)hm) - 1;
+      tk = (uint32_t)__builtin_amdgcn_readlane((int)mk, src);
+      ti = __builtin_amdgcn_readlane(mi, src);
+    }
+  }
+  return make_uint2(tk, (uint32_t)ti);
+}
+
+// A short row (at most GL float4 groups per thread) without the sample, the
+// level and the list: its values stay in registers, one value-linear
+// histogram of the whole row over [min, max] finds the bin b* of the
+// K_sel-th value, b*'s few values are ranked exactly, and the chosen set
+// their bitmap bits. Loads the row itself, clears the histogram, bitmap and
+// counters, and ends with a barrier. Returns false when the row needs the
+// general path (fewer than K_sel non-NaN values, infinities, a constant row,
+// a crowded bin).
+template <int NT, int G, int GL>
+__device__ __forceinline__ bool lean_row(SelectShared<NT, G>& sh, const float* __restrict__ row,
+                                         int ld, int n_c, int k_sel, int nwords) {
+  constexpr int NW = NT / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int ng = (n_c + 4 * NT - 1) / (4 * NT);
+  const uint8_t* rowb = reinterpret_cast<const uint8_t*>(row);
+  auto idx_of = [&](int g, int c) { return (g * NT + tid) * 4 + c; };
+  float4 raw[GL];
+#pragma unroll
+  for (int g = 0; g < GL; ++g) {
+    if (g < ng) {
+      const int off = min(g * NT * 16 + tid * 16, (ld - 4) * 4);
+      raw[g] = *reinterpret_cast<const float4*>(rowb + off);
+    } else {
+      raw[g] = make_float4(NAN, NAN, NAN, NAN);
+    }
+  }
+  float u[4 * GL];
+#pragma unroll
+  for (int g = 0; g < GL; ++g) {
+    u[4 * g + 0] = raw[g].x; u[4 * g + 1] = raw[g].y; u[4 * g + 2] = raw[g].z; u[4 * g + 3] = raw[g].w;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) u[4 * g + c] = idx_of(g, c) < n_c ? u[4 * g + c] : NAN;
+  }
+  forget(u);
+  float mn = INFINITY, mx = -INFINITY;
+  int ns = 0;
+#pragma unroll
+  for (int e = 0; e < 4 * GL; ++e) {
+    mn = fminf(mn, u[e]);
+    mx = fmaxf(mx, u[e]);
+    ns += u[e] == u[e];
+  }
+  mn = wave_min(mn);
+  mx = wave_max(mx);
+  ns = wave_sum(ns);
+  if (lane == 0) { sh.red_f[0][wid] = mn; sh.red_f[1][wid] = mx; sh.red_n[wid] = ns; }
+  for (int j = tid; j <= kBins; j += NT) sh.hist[j] = 0u;
+  for (int j = tid; j < nwords; j += NT) sh.bitmap[j] = 0u;
+  if (tid == 0) { sh.cand_cnt = 0; sh.res[0] = sh.res[1] = sh.res[2] = 0; }
+  __syncthreads();
+  mn = sh.red_f[0][0]; mx = sh.red_f[1][0];
+  int S = sh.red_n[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) {
+    mn = fminf(mn, sh.red_f[0][w]);
+    mx = fmaxf(mx, sh.red_f[1][w]);
+    S += sh.red_n[w];
+  }
+  const float range = mx - mn;
+  bool fast = S >= k_sel && (range > 0.f) && (range <= 3.0e38f);
+  if (fast) {
+    const float inv = (float)kBins / range;
+#pragma unroll
+    for (int e = 0; e < 4 * GL; ++e)
+      if (u[e] == u[e]) atomicAdd(&sh.hist[vbin(u[e], mn, inv)], 1u);
+    __syncthreads();
+    find_bin<NT, G, kBins>(sh, k_sel);
+    const int bstar = sh.res[0];
+    const int k_in = k_sel - sh.res[1];
+    const int c_in = sh.res[2];
+    if (c_in > NT) {
+      fast = false;                                    // crowded bin: general path
+    } else {
+      forget(u);
+#pragma unroll
+      for (int g = 0; g < GL; ++g) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const float x = u[4 * g + c];
+          if (x == x && vbin(x, mn, inv) == bstar) {
+            const int slot = atomicAdd(&sh.cand_cnt, 1);
+            sh.cand_key[slot] = f32_order_key(x);
+            sh.cand_idx[slot] = idx_of(g, c);
+          }
+        }
+      }
+      __syncthreads();
+      const uint2 th = threshold_of<NT, G>(sh, c_in, k_in, lane);
+      forget(u);
+#pragma unroll
+      for (int g = 0; g < GL; ++g) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const float x = u[4 * g + c];
+          const int ix = idx_of(g, c);
+          if (x == x) {
+            const uint32_t kx = f32_order_key(x);
+            if (kx > th.x || (kx == th.x && ix <= (int)th.y)) atomicOr(&sh.bitmap[ix >> 5], 1u << (ix & 31));
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();
+  return fast;
 }
 
 struct SelectArgs {
@@ -251,209 +400,193 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
   const int nwords = (n_c + 31) >> 5;
   auto idx_of = [&](int g, int c) { return (g * NT + tid) * 4 + c; };
 
-  // ---- 1. load the row. All loads are issued before any value is used, so a
-  // wave keeps its loads in flight together. Groups below ng - 1 are full and
-  // load through a uniform base; the last group clamps its addresses into the
-  // row and masks slots past n_c to NaN (which never reaches the level below
-  // and ranks as -inf).
-  const uint8_t* rowb = reinterpret_cast<const uint8_t*>(logits + (size_t)r * ld);
+  // Short rows (at most GL groups per thread) take the lean path, the others
+  // the sampled level and the list.
+  constexpr int GL = G < 3 ? G : 3;
   const float* row = logits + (size_t)r * ld;
-  const int lastg = ng - 1;
-  float4 raw[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    if (g < lastg) {
-      raw[g] = *reinterpret_cast<const float4*>(rowb + g * NT * 16 + tid * 16);
-    } else if (g == lastg) {
-      const int off = min(g * NT * 16 + tid * 16, ((int)ld - 4) * 4);
-      raw[g] = *reinterpret_cast<const float4*>(rowb + off);
-    } else {
-      raw[g] = make_float4(NAN, NAN, NAN, NAN);
+  bool fast;
+  if (ng <= GL) {
+    fast = lean_row<NT, G, GL>(sh, row, (int)ld, n_c, k_sel, nwords);
+  } else {
+    // ---- 1. load the row. All loads are issued before any value is used, so a
+    // wave keeps its loads in flight together. Groups below ng - 1 are full and
+    // load through a uniform base; the last group clamps its addresses into the
+    // row and masks slots past n_c to NaN (which never reaches the level below
+    // and ranks as -inf).
+    const uint8_t* rowb = reinterpret_cast<const uint8_t*>(row);
+    const int lastg = ng - 1;
+    float4 raw[G];
+  #pragma unroll
+    for (int g = 0; g < G; ++g) {
+      if (g < lastg) {
+        raw[g] = *reinterpret_cast<const float4*>(rowb + g * NT * 16 + tid * 16);
+      } else if (g == lastg) {
+        const int off = min(g * NT * 16 + tid * 16, ((int)ld - 4) * 4);
+        raw[g] = *reinterpret_cast<const float4*>(rowb + off);
+      } else {
+        raw[g] = make_float4(NAN, NAN, NAN, NAN);
+      }
     }
-  }
-  float v[E];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    v[4 * g + 0] = raw[g].x; v[4 * g + 1] = raw[g].y; v[4 * g + 2] = raw[g].z; v[4 * g + 3] = raw[g].w;
-    if (g == lastg) {
-      const int base = (g * NT + tid) * 4;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) v[4 * g + c] = base + c < n_c ? v[4 * g + c] : NAN;
+    float v[E];
+  #pragma unroll
+    for (int g = 0; g < G; ++g) {
+      v[4 * g + 0] = raw[g].x; v[4 * g + 1] = raw[g].y; v[4 * g + 2] = raw[g].z; v[4 * g + 3] = raw[g].w;
+      if (g == lastg) {
+        const int base = (g * NT + tid) * 4;
+  #pragma unroll
+        for (int c = 0; c < 4; ++c) v[4 * g + c] = base + c < n_c ? v[4 * g + c] : NAN;
+      }
     }
-  }
-  forget(v);
+    forget(v);
 
-  // ---- 2. sample: value (g, (g / 2) mod 4) of every even group g, its
-  // min / max, and a value-linear histogram of it
-  float smn = INFINITY, smx = -INFINITY;
-  int ns = 0;
-#pragma unroll
-  for (int g = 0; g < G; g += 2) {
-    if (g < ng) {
-      const float x = v[4 * g + ((g >> 1) & 3)];
-      smn = fminf(smn, x);
-      smx = fmaxf(smx, x);
-      ns += x == x;
-    }
-  }
-  smn = wave_min(smn);
-  smx = wave_max(smx);
-  ns = wave_sum(ns);
-  if (lane == 0) { sh.red_f[0][wid] = smn; sh.red_f[1][wid] = smx; sh.red_n[wid] = ns; }
-  for (int j = tid; j <= kBins; j += NT) sh.hist[j] = 0u;
-  for (int j = tid; j < nwords; j += NT) sh.bitmap[j] = 0u;
-  if (tid == 0) { sh.cand_cnt = 0; sh.res[0] = sh.res[1] = sh.res[2] = 0; }
-  __syncthreads();
-  smn = sh.red_f[0][0]; smx = sh.red_f[1][0];
-  int S = sh.red_n[0];
-#pragma unroll
-  for (int w = 1; w < NW; ++w) {
-    smn = fminf(smn, sh.red_f[0][w]);
-    smx = fmaxf(smx, sh.red_f[1][w]);
-    S += sh.red_n[w];
-  }
-  const float srange = smx - smn;
-  bool fast = S > 0 && (srange > 0.f) && (srange <= 3.0e38f);   // finite, not constant
-
-  if (fast) {
-    const float inv = (float)kBins / srange;
-#pragma unroll
+    // ---- 2. sample: value (g, (g / 2) mod 4) of every even group g, its
+    // min / max, and a value-linear histogram of it
+    float smn = INFINITY, smx = -INFINITY;
+    int ns = 0;
+  #pragma unroll
     for (int g = 0; g < G; g += 2) {
       if (g < ng) {
         const float x = v[4 * g + ((g >> 1) & 3)];
-        if (x == x) atomicAdd(&sh.hist[vbin(x, smn, inv)], 1u);
+        smn = fminf(smn, x);
+        smx = fmaxf(smx, x);
+        ns += x == x;
       }
     }
-    __syncthreads();
-    // sample rank of the level: a 25 % margin over the expected count of
-    // chosen values in the sample plus four standard deviations
-    const float expect = (float)k_sel * (float)S / (float)n_c;
-    int m = (int)ceilf(1.25f * expect + 4.f * sqrtf(expect) + 4.f);
-    m = m < S ? m : S;
-    find_bin<NT, G, kBins>(sh, m > 0 ? m : 1);
-    const float L = smn + (float)sh.res[0] * (srange / (float)kBins);
-
-    // ---- 3. compact every value >= L into the LDS list. Each wave appends
-    // to its own segment of seg_cap entries: a ballot gives each lane its
-    // prefix, the running count stays scalar, and a (value, index) pair is one
-    // 8-byte LDS write. A wave that overflows its segment keeps writing into
-    // the segment's last slot; its count records the overflow.
-    const int seg_cap = list_cap / NW;                 // at most 64 * LPL
-    uint2* seg = list + wid * seg_cap;
-    int running = 0;
-    forget(v);
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      if (g < ng) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const bool keep = v[4 * g + c] >= L;
-          const uint64_t m = __ballot(keep);
-          // entries past the segment's end all land in its last slot; the
-          // count still records the overflow, which sends the row to the
-          // general path
-          if (keep) {
-            const int pos = min(running + popc_lt(m), seg_cap - 1);
-            seg[pos] = make_uint2(__float_as_uint(v[4 * g + c]), (uint32_t)idx_of(g, c));
-          }
-          running += __popcll(m);
-        }
-      }
-    }
-    if (lane == 0) sh.seg_cnt[wid] = running;
+    smn = wave_min(smn);
+    smx = wave_max(smx);
+    ns = wave_sum(ns);
+    if (lane == 0) { sh.red_f[0][wid] = smn; sh.red_f[1][wid] = smx; sh.red_n[wid] = ns; }
     for (int j = tid; j <= kBins; j += NT) sh.hist[j] = 0u;
+    for (int j = tid; j < nwords; j += NT) sh.bitmap[j] = 0u;
+    if (tid == 0) { sh.cand_cnt = 0; sh.res[0] = sh.res[1] = sh.res[2] = 0; }
     __syncthreads();
-    int total = 0;
-    bool overflow = false;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const int c = sh.seg_cnt[w];
-      overflow |= c > seg_cap;
-      total += c;
+    smn = sh.red_f[0][0]; smx = sh.red_f[1][0];
+    int S = sh.red_n[0];
+  #pragma unroll
+    for (int w = 1; w < NW; ++w) {
+      smn = fminf(smn, sh.red_f[0][w]);
+      smx = fmaxf(smx, sh.red_f[1][w]);
+      S += sh.red_n[w];
     }
-    if (overflow || total < k_sel) {
-      fast = false;                                    // the level missed: general path
-    } else {
-      // ---- 4. exact threshold on the list. Each wave takes its own segment
-      // into registers once (lane l holds entries l, l + 64, ...); min / max,
-      // histogram, candidate gather and marking all work from there.
-      float ev[LPL];
-      int ei[LPL];
-#pragma unroll
-      for (int i = 0; i < LPL; ++i) {
-        const int j = lane + 64 * i;
-        const uint2 e = seg[j < running ? j : 0];
-        ev[i] = j < running ? __uint_as_float(e.x) : NAN;   // list values are never NaN
-        ei[i] = (int)e.y;
+    const float srange = smx - smn;
+    fast = S > 0 && (srange > 0.f) && (srange <= 3.0e38f);   // finite, not constant
+
+    if (fast) {
+      const float inv = (float)kBins / srange;
+  #pragma unroll
+      for (int g = 0; g < G; g += 2) {
+        if (g < ng) {
+          const float x = v[4 * g + ((g >> 1) & 3)];
+          if (x == x) atomicAdd(&sh.hist[vbin(x, smn, inv)], 1u);
+        }
       }
-      // histogram range: every list value is >= L, and all but the few
-      // above the sample's maximum are <= smx (those land in the top bin,
-      // which keeps the bins monotone); no reduction over the list needed
-      const float lmn = L, lmx = smx;
-      const float lrange = lmx - lmn;
-      if (!(lrange > 0.f) || !(lrange <= 3.0e38f)) {
-        fast = false;                                  // ties or infinities: general path
+      __syncthreads();
+      // sample rank of the level: a 25 % margin over the expected count of
+      // chosen values in the sample plus four standard deviations
+      const float expect = (float)k_sel * (float)S / (float)n_c;
+      int m = (int)ceilf(1.25f * expect + 4.f * sqrtf(expect) + 4.f);
+      m = m < S ? m : S;
+      find_bin<NT, G, kBins>(sh, m > 0 ? m : 1);
+      const float L = smn + (float)sh.res[0] * (srange / (float)kBins);
+
+      // ---- 3. compact every value >= L into the LDS list. Each wave appends
+      // to its own segment of seg_cap entries: a ballot gives each lane its
+      // prefix, the running count stays scalar, and a (value, index) pair is one
+      // 8-byte LDS write. A wave that overflows its segment keeps writing into
+      // the segment's last slot; its count records the overflow.
+      const int seg_cap = list_cap / NW;                 // at most 64 * LPL
+      uint2* seg = list + wid * seg_cap;
+      int running = 0;
+      forget(v);
+  #pragma unroll
+      for (int g = 0; g < G; ++g) {
+        if (g < ng) {
+  #pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const bool keep = v[4 * g + c] >= L;
+            const uint64_t m = __ballot(keep);
+            // entries past the segment's end all land in its last slot; the
+            // count still records the overflow, which sends the row to the
+            // general path
+            if (keep) {
+              const int pos = min(running + popc_lt(m), seg_cap - 1);
+              seg[pos] = make_uint2(__float_as_uint(v[4 * g + c]), (uint32_t)idx_of(g, c));
+            }
+            running += __popcll(m);
+          }
+        }
+      }
+      if (lane == 0) sh.seg_cnt[wid] = running;
+      for (int j = tid; j <= kBins; j += NT) sh.hist[j] = 0u;
+      __syncthreads();
+      int total = 0;
+      bool overflow = false;
+  #pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const int c = sh.seg_cnt[w];
+        overflow |= c > seg_cap;
+        total += c;
+      }
+      if (overflow || total < k_sel) {
+        fast = false;                                    // the level missed: general path
       } else {
-        const float linv = (float)kBins / lrange;
-#pragma unroll
-        for (int i = 0; i < LPL; ++i)
-          if (ev[i] == ev[i]) atomicAdd(&sh.hist[vbin(ev[i], lmn, linv)], 1u);
-        __syncthreads();
-        find_bin<NT, G, kBins>(sh, k_sel);
-        const int bstar = sh.res[0];
-        const int k_in = k_sel - sh.res[1];
-        const int c_in = sh.res[2];
-        if (c_in > NT) {
-          fast = false;                                // crowded bin: general path
+        // ---- 4. exact threshold on the list. Each wave takes its own segment
+        // into registers once (lane l holds entries l, l + 64, ...); min / max,
+        // histogram, candidate gather and marking all work from there.
+        float ev[LPL];
+        int ei[LPL];
+  #pragma unroll
+        for (int i = 0; i < LPL; ++i) {
+          const int j = lane + 64 * i;
+          const uint2 e = seg[j < running ? j : 0];
+          ev[i] = j < running ? __uint_as_float(e.x) : NAN;   // list values are never NaN
+          ei[i] = (int)e.y;
+        }
+        // histogram range: every list value is >= L, and all but the few
+        // above the sample's maximum are <= smx (those land in the top bin,
+        // which keeps the bins monotone); no reduction over the list needed
+        const float lmn = L, lmx = smx;
+        const float lrange = lmx - lmn;
+        if (!(lrange > 0.f) || !(lrange <= 3.0e38f)) {
+          fast = false;                                  // ties or infinities: general path
         } else {
-#pragma unroll
-          for (int i = 0; i < LPL; ++i) {
-            if (ev[i] == ev[i] && vbin(ev[i], lmn, linv) == bstar) {
-              const int slot = atomicAdd(&sh.cand_cnt, 1);
-              sh.cand_key[slot] = f32_order_key(ev[i]);
-              sh.cand_idx[slot] = ei[i];
-            }
-          }
+          const float linv = (float)kBins / lrange;
+  #pragma unroll
+          for (int i = 0; i < LPL; ++i)
+            if (ev[i] == ev[i]) atomicAdd(&sh.hist[vbin(ev[i], lmn, linv)], 1u);
           __syncthreads();
-          // every wave ranks the few candidates itself (lane l takes
-          // candidates l, l + 64, ...), so the threshold element needs no
-          // second barrier to reach the other waves
-          uint32_t tk = 0u;
-          int ti = 0;
-          for (int c0 = 0; c0 < c_in; c0 += 64) {
-            const int ci = c0 + lane;
-            bool hit = false;
-            uint32_t mk = 0u;
-            int mi = 0;
-            if (ci < c_in) {
-              mk = sh.cand_key[ci];
-              mi = sh.cand_idx[ci];
-              int rank = 0;
-              for (int q = 0; q < c_in; ++q) {
-                const uint32_t okey = sh.cand_key[q];
-                rank += (okey > mk) || (okey == mk && sh.cand_idx[q] < mi);
+          find_bin<NT, G, kBins>(sh, k_sel);
+          const int bstar = sh.res[0];
+          const int k_in = k_sel - sh.res[1];
+          const int c_in = sh.res[2];
+          if (c_in > NT) {
+            fast = false;                                // crowded bin: general path
+          } else {
+  #pragma unroll
+            for (int i = 0; i < LPL; ++i) {
+              if (ev[i] == ev[i] && vbin(ev[i], lmn, linv) == bstar) {
+                const int slot = atomicAdd(&sh.cand_cnt, 1);
+                sh.cand_key[slot] = f32_order_key(ev[i]);
+                sh.cand_idx[slot] = ei[i];
               }
-              hit = rank == k_in - 1;
             }
-            const uint64_t hm = __ballot(hit);
-            if (hm) {
-              const int src = __ffsll((unsigned long long)hm) - 1;
-              tk = (uint32_t)__builtin_amdgcn_readlane((int)mk, src);
-              ti = __builtin_amdgcn_readlane(mi, src);
-            }
-          }
-          // ---- 5a. chosen list entries set their bitmap bits
-#pragma unroll
-          for (int i = 0; i < LPL; ++i) {
-            if (ev[i] == ev[i]) {
-              const uint32_t kx = f32_order_key(ev[i]);
-              if (kx > tk || (kx == tk && ei[i] <= ti)) atomicOr(&sh.bitmap[ei[i] >> 5], 1u << (ei[i] & 31));
+            __syncthreads();
+            const uint2 th = threshold_of<NT, G>(sh, c_in, k_in, lane);
+            const uint32_t tk = th.x;
+            const int ti = (int)th.y;
+            // ---- 5a. chosen list entries set their bitmap bits
+  #pragma unroll
+            for (int i = 0; i < LPL; ++i) {
+              if (ev[i] == ev[i]) {
+                const uint32_t kx = f32_order_key(ev[i]);
+                if (kx > tk || (kx == tk && ei[i] <= ti)) atomicOr(&sh.bitmap[ei[i] >> 5], 1u << (ei[i] & 31));
+              }
             }
           }
         }
       }
+      __syncthreads();
     }
-    __syncthreads();
   }
 
   if (!fast) {
