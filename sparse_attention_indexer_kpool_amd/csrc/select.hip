@@ -416,7 +416,7 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
     const uint8_t* rowb = reinterpret_cast<const uint8_t*>(row);
     const int lastg = ng - 1;
     float4 raw[G];
-  #pragma unroll
+#pragma unroll
     for (int g = 0; g < G; ++g) {
       if (g < lastg) {
         raw[g] = *reinterpret_cast<const float4*>(rowb + g * NT * 16 + tid * 16);
@@ -428,12 +428,12 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
       }
     }
     float v[E];
-  #pragma unroll
+#pragma unroll
     for (int g = 0; g < G; ++g) {
       v[4 * g + 0] = raw[g].x; v[4 * g + 1] = raw[g].y; v[4 * g + 2] = raw[g].z; v[4 * g + 3] = raw[g].w;
       if (g == lastg) {
         const int base = (g * NT + tid) * 4;
-  #pragma unroll
+#pragma unroll
         for (int c = 0; c < 4; ++c) v[4 * g + c] = base + c < n_c ? v[4 * g + c] : NAN;
       }
     }
@@ -443,7 +443,7 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
     // min / max, and a value-linear histogram of it
     float smn = INFINITY, smx = -INFINITY;
     int ns = 0;
-  #pragma unroll
+#pragma unroll
     for (int g = 0; g < G; g += 2) {
       if (g < ng) {
         const float x = v[4 * g + ((g >> 1) & 3)];
@@ -462,7 +462,7 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
     __syncthreads();
     smn = sh.red_f[0][0]; smx = sh.red_f[1][0];
     int S = sh.red_n[0];
-  #pragma unroll
+#pragma unroll
     for (int w = 1; w < NW; ++w) {
       smn = fminf(smn, sh.red_f[0][w]);
       smx = fmaxf(smx, sh.red_f[1][w]);
@@ -473,7 +473,7 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
 
     if (fast) {
       const float inv = (float)kBins / srange;
-  #pragma unroll
+#pragma unroll
       for (int g = 0; g < G; g += 2) {
         if (g < ng) {
           const float x = v[4 * g + ((g >> 1) & 3)];
@@ -498,10 +498,10 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
       uint2* seg = list + wid * seg_cap;
       int running = 0;
       forget(v);
-  #pragma unroll
+#pragma unroll
       for (int g = 0; g < G; ++g) {
         if (g < ng) {
-  #pragma unroll
+#pragma unroll
           for (int c = 0; c < 4; ++c) {
             const bool keep = v[4 * g + c] >= L;
             const uint64_t m = __ballot(keep);
@@ -521,7 +521,7 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
       __syncthreads();
       int total = 0;
       bool overflow = false;
-  #pragma unroll
+#pragma unroll
       for (int w = 0; w < NW; ++w) {
         const int c = sh.seg_cnt[w];
         overflow |= c > seg_cap;
@@ -535,7 +535,7 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
         // histogram, candidate gather and marking all work from there.
         float ev[LPL];
         int ei[LPL];
-  #pragma unroll
+#pragma unroll
         for (int i = 0; i < LPL; ++i) {
           const int j = lane + 64 * i;
           const uint2 e = seg[j < running ? j : 0];
@@ -551,7 +551,7 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
           fast = false;                                  // ties or infinities: general path
         } else {
           const float linv = (float)kBins / lrange;
-  #pragma unroll
+#pragma unroll
           for (int i = 0; i < LPL; ++i)
             if (ev[i] == ev[i]) atomicAdd(&sh.hist[vbin(ev[i], lmn, linv)], 1u);
           __syncthreads();
@@ -562,7 +562,7 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
           if (c_in > NT) {
             fast = false;                                // crowded bin: general path
           } else {
-  #pragma unroll
+#pragma unroll
             for (int i = 0; i < LPL; ++i) {
               if (ev[i] == ev[i] && vbin(ev[i], lmn, linv) == bstar) {
                 const int slot = atomicAdd(&sh.cand_cnt, 1);
@@ -575,7 +575,7 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
             const uint32_t tk = th.x;
             const int ti = (int)th.y;
             // ---- 5a. chosen list entries set their bitmap bits
-  #pragma unroll
+#pragma unroll
             for (int i = 0; i < LPL; ++i) {
               if (ev[i] == ev[i]) {
                 const uint32_t kx = f32_order_key(ev[i]);
