@@ -450,7 +450,7 @@ def measure_workload(wl, steps: int, warmup: int):
     fused = None
     if wl.k_sel <= path.kp.kpool_fused_max_ksel(path.p):
         path.fused_step()
-        ms_fused_step = time_region(path.fused_step, steps, warm=1)
+        ms_fused_step = time_region(path.fused_step, min(steps, 50), warm=1)
         ms_fused_idx = time_region(path.fused_indexer, reps)
         fused = (ms_fused_step, ms_fused_idx)
         log(f"{wl.name}: fused step {ms_fused_step:.4f} ms")
@@ -512,7 +512,8 @@ def measure_workload(wl, steps: int, warmup: int):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    # the default times 2000 steps of the 64K workload, about 8 s of GPU work
+    ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="long_T65536_H32_D128")
     ap.add_argument("--cpu-rows", type=int, default=12288)
@@ -569,7 +570,7 @@ def main():
         for key, other in (("fp8", "fp8_T32768_H32_D128"), ("tiny", "tiny_T256_H4_D64"),
                            ("single_4k", "single_T4096_H32_D128"),
                            ("packed8", "packed8_H32_D128")):
-            _, _, f2 = measure_workload(wlm.workload(other), args.steps, args.warmup)
+            _, _, f2 = measure_workload(wlm.workload(other), min(args.steps, 200), args.warmup)
             out[key] = f2
     if rank == 0 and not args.no_cpu_baseline:
         log(f"cpu baseline on {args.cpu_rows} rows")
